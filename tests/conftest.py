@@ -1,0 +1,24 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU; runs the HIP path")
+
+
+@pytest.fixture(scope="session")
+def oracle_mod():
+    """The CPU oracle, built if its shared library is missing."""
+    from oracle.build import LIBRARY, build_oracle
+
+    if not os.path.exists(LIBRARY):
+        build_oracle()
+    import oracle
+
+    return oracle

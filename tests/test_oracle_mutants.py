@@ -1,0 +1,79 @@
+"""Plausible mistakes planted in copies of the oracle must each fail a pin.
+
+Each mutant is the oracle's C source with one textual change (a dropped term,
+a wrong order, index or offset, a flushed sign), compiled to a temporary
+library on the CPU.  The pins of tests/oracle_pins.py run against it and at
+least one must fail; the unmodified oracle passes all of them
+(test_oracle.py).  The mutants only ever run on the host.
+"""
+import os
+import subprocess
+
+import pytest
+
+from tests import oracle_pins
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SOURCE = os.path.join(ROOT, "oracle", "tide_oracle.c")
+
+MUTANTS = [
+    ("drop_last_rank",
+     "for (int32_t u = 1; u < g->W; ++u) acc = acc +",
+     "for (int32_t u = 1; u < g->W - 1; ++u) acc = acc +"),
+    ("reverse_rank_order",
+     "float acc = bf16_to_f32(j->grads[(int64_t)0 * g->P + p][i]);\n"
+     "            for (int32_t u = 1; u < g->W; ++u) acc = acc + bf16_to_f32(j->grads[(int64_t)u * g->P + p][i]);",
+     "float acc = bf16_to_f32(j->grads[(int64_t)(g->W - 1) * g->P + p][i]);\n"
+     "            for (int32_t u = g->W - 2; u >= 0; --u) acc = acc + bf16_to_f32(j->grads[(int64_t)u * g->P + p][i]);"),
+    ("accumulator_starts_at_plus_zero",
+     "float acc = bf16_to_f32(j->grads[(int64_t)0 * g->P + p][i]);",
+     "float acc = 0.0f + bf16_to_f32(j->grads[(int64_t)0 * g->P + p][i]);"),
+    ("double_accumulator",
+     "float acc = bf16_to_f32(", "double acc = bf16_to_f32("),
+    ("floor_rows_per_rank",
+     "int64_t R = (D + W - 1) / W;", "int64_t R = D / W;"),
+    ("landing_pitch_uses_row_length",
+     "landing_offset[(int64_t)p * W + r] = (int64_t)W * g.o[p] + (int64_t)r * g.n[p];",
+     "landing_offset[(int64_t)p * W + r] = (int64_t)W * g.o[p] + (int64_t)r * g.K[p];"),
+    ("rank_major_offset_drops_prefix",
+     "rank_major_offset[(int64_t)p * W + r] = (int64_t)r * g.S + g.o[p];",
+     "rank_major_offset[(int64_t)p * W + r] = (int64_t)r * g.S;"),
+    ("copyout_source_drops_prefix",
+     "const uint16_t* src = j->rank_major + (int64_t)r * g->S + g->o[p];",
+     "const uint16_t* src = j->rank_major + (int64_t)r * g->S;"),
+    ("copyout_destination_uses_real_count",
+     "uint16_t* dst = j->params[p] + (int64_t)r * g->R[p] * g->K[p];",
+     "uint16_t* dst = j->params[p] + (int64_t)r * real;"),
+    ("rs_padding_negative_zero",
+     "dst[e] = 0.0f;", "dst[e] = -0.0f;"),
+    ("pack_padding_not_zero",
+     "(e < real) ? src[e] : (uint16_t)0;", "(e < real) ? src[e] : (uint16_t)0x8000;"),
+    ("row_length_drops_last_dim",
+     "for (int32_t j = 1; j < ndims[p]; ++j) {", "for (int32_t j = 1; j < ndims[p] - 1; ++j) {"),
+    ("rs_source_row_offset_uses_real_count",
+     "int64_t first = (int64_t)r * g->R[p] * g->K[p];\n    float* dst",
+     "int64_t first = (int64_t)r * real;\n    float* dst"),
+]
+
+
+def _build(tmp_path, name, old, new):
+    src = open(SOURCE).read()
+    assert src.count(old) == 1, f"mutant {name}: pattern must occur once in the oracle source"
+    path = tmp_path / f"{name}.c"
+    path.write_text(src.replace(old, new))
+    lib = tmp_path / f"lib{name}.so"
+    subprocess.run(["gcc", "-std=c11", "-O2", "-fPIC", "-shared", "-pthread", "-ffp-contract=off",
+                    "-fno-fast-math", str(path), "-o", str(lib)], check=True)
+    return str(lib)
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_fails_a_pin(tmp_path, name, old, new, oracle_mod):
+    orc = oracle_mod.Oracle(_build(tmp_path, name, old, new))
+    failed = []
+    for check in oracle_pins.ALL_CHECKS:
+        try:
+            check(orc)
+        except (AssertionError, oracle_mod.OracleError, ValueError, IndexError):
+            failed.append(check.__name__)
+    assert failed, f"mutant {name} passed every pin"
