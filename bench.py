@@ -1,0 +1,277 @@
+#!/usr/bin/env python3
+"""Benchmark of the layout-aware FSDP2 collective local stages on one MI355X.
+
+One step is one pass of the whole hot path over one batch of synthetic input
+already resident in HBM: the reduce-scatter local stage (W ranks' bf16
+gradients -> W packed fp32 shards) followed by the all-gather copy-out
+(rank-major bf16 buffer -> per-parameter tensors), on one HIP stream.  The
+shard-layout plan is made once, before timing (it is per-registration work).
+
+Reported (one JSON line): effective HBM GB/s of the step, i.e. algorithmic
+bytes read plus written by both kernels divided by the step time, with
+  * per-kernel figures from HIP events recorded on the kernels' own stream;
+  * the roofline of the dominant kernel (the reduce-scatter) against MI355X's
+    8 TB/s HBM peak, and its measured HBM traffic when a counter summary for
+    the current kernel source is committed under profiles/;
+  * a CU-budget sweep (grid-limited budgets, as the workgroup budget of the
+    pages' short-lived sum kernels);
+  * a plain device-to-device copy of the copy-out's byte count, for context;
+  * the CPU oracle timed on the host's cores on the same workload.
+Algorithmic bytes: reduce-scatter 2*W*sum(D*K) read + 4*W*S written (padding
+is written, never read); copy-out 2*sum(D*K) read + 2*sum(D*K) written.
+"""
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+METRIC = "effective HBM GB/s (and % of peak) for RS-local reduce and AG copy-out"
+DEFAULT_WORKLOAD = "llama3.1-8b-layer"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+KERNEL_SOURCE = os.path.join(ROOT, "param_collectives_amd", "csrc", "tide.hip")
+
+
+def parse_args(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--cu-budget", type=int, default=0)
+    ap.add_argument("--wg-per-cu", type=int, default=0)
+    ap.add_argument("--chunk", type=int, default=0)
+    ap.add_argument("--flags", type=int, default=0)
+    ap.add_argument("--no-sweep", action="store_true", help="skip the CU-budget sweep")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
+    ap.add_argument("--only", choices=["rs", "co", "calib"],
+                    help="launch just one kernel --launches times (for counter collection) and exit")
+    ap.add_argument("--launches", type=int, default=5)
+    return ap.parse_args(argv)
+
+
+def source_digest():
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_for(kernel_key):
+    """HBM bytes per launch from the committed counter summary, or None when
+    there is none for this kernel and workload or the kernel source changed."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != source_digest():
+        return None
+    k = t.get("kernels", {}).get(kernel_key)
+    cal = t.get("calibration")
+    if not k or not cal:
+        return None
+    return k["fetch_kib"] * 1024.0 * cal["fetch_factor"] + k["write_kib"] * 1024.0 * cal["write_factor"]
+
+
+def main(argv=None):
+    args = parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); the W simulated ranks all live "
+              "in one GPU's HBM. Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import synth
+    from param_collectives_amd import tide
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    torch.cuda.set_device(0)
+    w = synth.workload(args.workload)
+    opts = dict(cu_budget=args.cu_budget, wg_per_cu=args.wg_per_cu, chunk_elems=args.chunk, flags=args.flags)
+    plan = tide.Plan(w.world, w.shapes, **opts)
+    W, S = w.world, plan.shard_elems
+    sum_dk = sum(w.numel(p) for p in range(w.nparams))
+    rs_bytes = 2 * W * sum_dk + 4 * W * S
+    co_bytes = 4 * sum_dk
+    stream = torch.cuda.Stream()
+
+    with torch.cuda.stream(stream):
+        grads = synth.grads_device(w, "cuda")
+        outs = [torch.empty(S, dtype=torch.float32, device="cuda") for _ in range(W)]
+        rank_major = synth.rank_major_device(w, W * S, "cuda")
+        params = [torch.empty(s, dtype=torch.bfloat16, device="cuda") for s in w.shapes]
+    stream.synchronize()
+
+    def rs():
+        tide.reduce_scatter_local(plan, grads, outs, stream=stream)
+
+    def co():
+        tide.allgather_copyout(plan, rank_major, params, stream=stream)
+
+    if args.only:
+        if args.only == "calib":
+            n = W * S
+            cplan = tide.Plan(1, [(n,)], **opts)
+            dst = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+            for _ in range(args.launches):
+                tide.allgather_copyout(cplan, rank_major, [dst], stream=stream)
+            stream.synchronize()
+            print(json.dumps({"only": "calib", "launches": args.launches, "bytes_read": 2 * n, "bytes_written": 2 * n}))
+        else:
+            fn = rs if args.only == "rs" else co
+            for _ in range(args.launches):
+                fn()
+            stream.synchronize()
+            print(json.dumps({"only": args.only, "workload": w.name, "launches": args.launches,
+                              "bytes": rs_bytes if args.only == "rs" else co_bytes}))
+        return 0
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    # warm-up (also binds the plan and uploads its tables)
+    for _ in range(args.warmup):
+        rs()
+        co()
+    stream.synchronize()
+
+    marks = [(ev(), ev(), ev()) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b, c in marks:
+        a.record(stream)
+        rs()
+        b.record(stream)
+        co()
+        c.record(stream)
+    stream.synchronize()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    rs_ms = [a.elapsed_time(b) for a, b, _ in marks]
+    co_ms = [b.elapsed_time(c) for _, b, c in marks]
+    step_ms_events = marks[0][0].elapsed_time(marks[-1][2]) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+
+    def kstats(ms, nbytes):
+        avg = sum(ms) / len(ms)
+        med = statistics.median(ms)
+        return {"bytes": nbytes, "avg_ms": round(avg, 5), "median_ms": round(med, 5), "min_ms": round(min(ms), 5),
+                "p90_ms": round(sorted(ms)[int(0.9 * (len(ms) - 1))], 5), "gbps": round(nbytes / avg / 1e6, 1),
+                "frac_of_peak": round(nbytes / avg / 1e6 / HBM_PEAK_GBPS, 4)}
+
+    kernels = {"rs_local": kstats(rs_ms, rs_bytes), "ag_copyout": kstats(co_ms, co_bytes)}
+
+    # CU-budget sweep (grid-limited budgets; results are bit-identical by design)
+    sweep = []
+    if not args.no_sweep:
+        base = plan.options()
+        for budget in (8, 16, 32, 64, 128, 256):
+            plan.set_options(cu_budget=budget, wg_per_cu=base["wg_per_cu"], chunk_elems=base["chunk_elems"],
+                             flags=base["flags"])
+            row = {"cu_budget": budget}
+            for name, fn, nbytes in (("rs_local", rs, rs_bytes), ("ag_copyout", co, co_bytes)):
+                fn()
+                e = [(ev(), ev()) for _ in range(10)]
+                for a, b in e:
+                    a.record(stream)
+                    fn()
+                    b.record(stream)
+                stream.synchronize()
+                avg = sum(a.elapsed_time(b) for a, b in e) / len(e)
+                row[name] = {"avg_ms": round(avg, 5), "gbps": round(nbytes / avg / 1e6, 1),
+                             "gbps_per_cu": round(nbytes / avg / 1e6 / budget, 2)}
+            sweep.append(row)
+        plan.set_options(**{k: base[k] for k in ("wg_per_cu", "chunk_elems", "flags")},
+                         cu_budget=opts["cu_budget"])
+
+    # plain device-to-device copy of the copy-out's byte count (context)
+    with torch.cuda.stream(stream):
+        src = torch.empty(co_bytes // 2, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        e = [(ev(), ev()) for _ in range(10)]
+        for a, b in e:
+            a.record(stream)
+            dst.copy_(src)
+            b.record(stream)
+    stream.synchronize()
+    d2d_ms = sum(a.elapsed_time(b) for a, b in e) / len(e)
+    d2d = {"bytes": co_bytes, "avg_ms": round(d2d_ms, 5), "gbps": round(co_bytes / d2d_ms / 1e6, 1)}
+    del src, dst
+
+    # CPU oracle on the same workload, and a bitwise check of this run's outputs
+    cpu = None
+    parity = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        host_grads = [[g.view(torch.int16).cpu().numpy().view(np.uint16) for g in row] for row in grads]
+        host_rm = rank_major.view(torch.int16).cpu().numpy().view(np.uint16)
+        threads = min(16, os.cpu_count() or 1)
+        times = []
+        want = want_co = None
+        spent = 0.0
+        while len(times) < 3 and spent < 20.0:
+            t = time.perf_counter()
+            want = oracle.rs_local(W, w.shapes, host_grads, nthreads=threads)
+            want_co = oracle.copyout(W, w.shapes, host_rm, nthreads=threads)
+            dt = time.perf_counter() - t
+            times.append(dt)
+            spent += dt
+        med = statistics.median(times)
+        cpu = {"value": round((rs_bytes + co_bytes) / med / 1e9, 2), "unit": "GB/s", "cores": threads,
+               "kind": "oracle",
+               "sample": f"one full step of {w.name} (reduce-scatter + copy-out), median of {len(times)} runs, "
+                         f"{med:.2f} s each, {threads} threads"}
+        ok = all(np.array_equal(outs[r].cpu().numpy().view(np.uint32), want[r].view(np.uint32)) for r in range(W))
+        ok_co = all(np.array_equal(params[p].view(torch.int16).cpu().numpy().view(np.uint16), want_co[p])
+                    for p in range(w.nparams))
+        parity = {"rs_local": "bit-exact" if ok else "MISMATCH", "ag_copyout": "bit-exact" if ok_co else "MISMATCH"}
+
+    rs_k = kernels["rs_local"]
+    achieved = rs_bytes / (rs_k["avg_ms"] * 1e-3) / 1e9
+    value = (rs_bytes + co_bytes) / (ms_per_step * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "world": W, "params": w.nparams, "elements": sum_dk, "shard_elems": S,
+                   "bytes_per_step": rs_bytes + co_bytes, "options": plan.options()},
+        "frac_of_peak": round(value / HBM_PEAK_GBPS, 4),
+        "roofline": {"bound": "hbm", "kernel": "rs_local_kernel", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic_for(f"rs_local/{w.name}")},
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        "event_ms_per_step": round(step_ms_events, 5),
+        "cu_sweep": sweep,
+        "d2d_copy": d2d,
+        "parity": parity,
+    }
+    print(json.dumps(line), flush=True)
+    if parity and "MISMATCH" in parity.values():
+        return 3
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,195 @@
+/*
+ * tide.h -- C ABI of the layout-aware FSDP2 collective local stages on one
+ * MI355X (gfx950) GPU.
+ *
+ * Two operations, after "The Endgame of FSDP Communication: Layout-Aware
+ * Collectives on Copy Engines, RDMA, and NVSwitch" (Wang et al.):
+ *
+ *   reduce-scatter local stage (Section 4, Equation 5; Section 4.1): W ranks'
+ *     per-parameter bf16 gradients, all resident in this GPU's memory, are
+ *     summed into W packed per-rank fp32 shards.  The dimension-0 shard
+ *     placement of Section 2.1 is folded into the addressing: no packed
+ *     intermediate buffer (Equation 3) is formed.
+ *
+ *   all-gather copy-out (Section 2.1): a flat rank-major bf16 buffer is
+ *     scattered into per-parameter tensors.
+ *
+ * Shard geometry (Section 2.1), in ELEMENTS.  Parameter p has shape
+ * (d_0, ..., d_{m-1}), m >= 1, viewed as D_p = d_0 rows of K_p = d_1*...*d_{m-1}
+ * elements (K_p = 1 for m = 1).  Each of the W ranks owns R_p = ceil(D_p / W)
+ * rows: rank r owns rows [r R_p, (r+1) R_p), rows at or past D_p are padding.
+ * Shard size n_p = R_p K_p, prefix offset o_p = sum_{i<p} n_i (no alignment
+ * padding between parameters), per-rank shard size S = sum_p n_p.  The real
+ * element count of rank r's shard of p is
+ *   n_real(p, r) = clamp(D_p - r R_p, 0, R_p) * K_p.
+ *
+ * Conventions for every call:
+ *   - Every call returns a tide_status; TIDE_OK is 0.  On failure,
+ *     tide_last_error() holds a message (thread-local, valid until the
+ *     calling thread's next tide_* call).
+ *   - Argument checks happen before any device work: a call that fails them
+ *     enqueues nothing and leaves every output untouched.
+ *   - Device buffers are owned by the caller and must stay alive until the
+ *     work enqueued on `stream` has finished.  Host arrays passed in are read
+ *     during the call only.
+ *   - `stream` is a hipStream_t (NULL means the null stream).  Calls are
+ *     asynchronous on it; nothing blocks the host except the one-time
+ *     device set-up of a plan (see below).
+ *   - Outputs must not overlap inputs or each other.
+ *   - A plan may be used by one host thread and one stream at a time: its
+ *     device pointer tables are rewritten (stream-ordered) when a call passes
+ *     different pointers from the previous call.
+ *   - Results never depend on tide_options: every option only changes how the
+ *     work is split, never which additions happen or in what order.
+ */
+#ifndef TIDE_H
+#define TIDE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TIDE_OK = 0,
+    TIDE_ERR_INVALID = -1,     /* null or out-of-range argument, bad shape, unknown/destroyed plan */
+    TIDE_ERR_RANGE = -2,       /* a size overflows int64 or exceeds a documented limit */
+    TIDE_ERR_ALIGN = -3,       /* a pointer is not aligned to its element size */
+    TIDE_ERR_NOMEM = -4,       /* host, pinned or device allocation failed */
+    TIDE_ERR_HIP = -5,         /* a HIP runtime call failed (its text is in tide_last_error) */
+    TIDE_ERR_UNSUPPORTED = -6  /* alpha != 1 or accumulate != 0: not provided */
+} tide_status;
+
+/* Largest number of simulated ranks a plan may have. */
+#define TIDE_MAX_WORLD 256
+
+/* tide_options.flags */
+#define TIDE_FLAG_NT_LOADS 0x1u  /* stream global loads with the non-temporal hint */
+#define TIDE_FLAG_NT_STORES 0x2u /* write outputs with the non-temporal hint */
+
+/*
+ * Launch knobs.  A field of 0 selects the default.  None of them changes any
+ * result bit (Section 4.3: tuning knobs preserve operand grouping).
+ *   cu_budget   workgroups are launched for this many CUs' worth of the
+ *               persistent grid (grid = cu_budget * wg_per_cu, at most one
+ *               workgroup per chunk); default: every CU of the device.
+ *               Workgroups are dispatched round-robin over the 8 XCDs, so a
+ *               budget is a grid size, not a CU mask.
+ *   wg_per_cu   workgroups (256 threads each) per budgeted CU; default 8.
+ *   chunk_elems elements per work chunk, a multiple of 8; default 4096.
+ *   flags       TIDE_FLAG_* bits.
+ */
+typedef struct {
+    int32_t cu_budget;
+    int32_t wg_per_cu;
+    int64_t chunk_elems;
+    uint32_t flags;
+} tide_options;
+
+typedef struct tide_plan tide_plan; /* opaque, owned by the library */
+
+/*
+ * Create a plan for W = `world` simulated ranks and P = `nparams` parameters.
+ *   world      1 <= W <= TIDE_MAX_WORLD
+ *   nparams    P >= 1
+ *   ndims      [P] number of dimensions of each parameter, each >= 1
+ *   dims       all dimensions, concatenated in parameter order
+ *              (sum_p ndims[p] entries), each >= 0
+ *   opt        launch knobs, or NULL for defaults
+ *   out_plan   receives the plan
+ * Host only: no device call is made.  The plan's device tables are allocated
+ * and uploaded by the first reduce-scatter or copy-out call that uses it, on
+ * the device current at that time (that first call blocks the host for the
+ * allocation); the plan is bound to that device afterwards.
+ * Errors: TIDE_ERR_INVALID (bad counts, shapes, null pointers),
+ * TIDE_ERR_RANGE (sizes overflow int64), TIDE_ERR_NOMEM.
+ */
+tide_status tide_plan_create(int32_t world, int32_t nparams, const int32_t* ndims, const int64_t* dims,
+                             const tide_options* opt, tide_plan** out_plan);
+
+/*
+ * Shard geometry of a plan, in elements (Section 2.1).  Any output pointer
+ * may be NULL.
+ *   rows_per_rank  [P] R_p
+ *   shard_offset   [P] o_p
+ *   shard_elems    [1] S
+ */
+tide_status tide_plan_layout(const tide_plan* plan, int64_t* rows_per_rank, int64_t* shard_offset,
+                             int64_t* shard_elems);
+
+/*
+ * The plan's work segments, for inspection and tests.  op 0 = reduce-scatter,
+ * 1 = copy-out.  Each segment is 6 int64 values:
+ *   kind     0 = sum of the W ranks' sources, 1 = zero fill (padding),
+ *            2 = copy
+ *   src_idx  reduce-scatter: parameter p; copy-out: 0 (the rank-major buffer)
+ *   dst_idx  reduce-scatter: destination rank r; copy-out: parameter p
+ *   src_off  element offset in each source tensor (in the rank-major buffer
+ *            for the copy-out)
+ *   dst_off  element offset in the destination tensor
+ *   len      elements (> 0)
+ * Writes min(capacity, count) segments to `table` (may be NULL when
+ * capacity is 0) and the total count to *count.
+ */
+tide_status tide_plan_segments(const tide_plan* plan, int32_t op, int64_t* table, int64_t capacity,
+                               int64_t* count);
+
+/* Replace the launch knobs (NULL = defaults).  Results are unaffected. */
+tide_status tide_plan_set_options(tide_plan* plan, const tide_options* opt);
+
+/* The launch knobs in effect, with defaults resolved where known (cu_budget
+ * is resolved once the plan is bound to a device, 0 before). */
+tide_status tide_plan_get_options(const tide_plan* plan, tide_options* out);
+
+/*
+ * Reduce-scatter local stage (Section 4, Equation 5; Section 4.3).
+ *   grads   [W*P] host array of device pointers; grads[u*P + p] is rank u's
+ *           bf16 gradient of parameter p: D_p*K_p elements, row-major, 2-byte
+ *           aligned.  May be NULL only where D_p*K_p = 0.
+ *   out     [W] host array of device pointers; out[r] receives rank r's
+ *           packed fp32 shard: S elements, 4-byte aligned, written in full.
+ *   alpha, accumulate
+ *           Equation 5's scale and accumulate flag.  Only alpha = 1.0f and
+ *           accumulate = 0 are provided (else TIDE_ERR_UNSUPPORTED).
+ * For r in [0, W), p in [0, P), e in [0, n_p):
+ *   out[r][o_p + e] = g_0 + g_1 + ... + g_{W-1}   for e < n_real(p, r),
+ *                     with g_u = grads[u*P+p][r R_p K_p + e] widened exactly
+ *                     to fp32, added left to right (rank order 0..W-1) in
+ *                     IEEE binary32, round to nearest even, subnormals kept;
+ *   out[r][o_p + e] = +0.0f                        for padding (e >= n_real).
+ * The result is bit-identical for every tide_options setting.
+ * Errors: TIDE_ERR_INVALID (null plan/arrays/pointers), TIDE_ERR_ALIGN,
+ * TIDE_ERR_UNSUPPORTED, TIDE_ERR_NOMEM, TIDE_ERR_HIP.
+ */
+tide_status tide_reduce_scatter_local(tide_plan* plan, const uint16_t* const* grads, float* const* out,
+                                      float alpha, int32_t accumulate, void* stream);
+
+/*
+ * All-gather copy-out (Section 2.1).
+ *   rank_major  device pointer to W*S bf16 elements, 2-byte aligned: rank
+ *               r's shard of parameter p starts at element r*S + o_p.
+ *   params      [P] host array of device pointers; params[p] receives the
+ *               D_p*K_p elements of parameter p (row-major, 2-byte aligned).
+ *               May be NULL only where D_p*K_p = 0.
+ * For every p, r and e < n_real(p, r):
+ *   params[p][r R_p K_p + e] = rank_major[r S + o_p + e]   (16-bit moves)
+ * Padding elements of the rank-major buffer are never read; every element
+ * of every params[p] is written exactly once.
+ * Errors: TIDE_ERR_INVALID, TIDE_ERR_ALIGN, TIDE_ERR_NOMEM, TIDE_ERR_HIP.
+ */
+tide_status tide_allgather_copyout(tide_plan* plan, const uint16_t* rank_major, uint16_t* const* params,
+                                   void* stream);
+
+/* Free a plan and its device tables (waits for the device to finish using
+ * them).  NULL is accepted. */
+void tide_plan_destroy(tide_plan* plan);
+
+/* Message describing the calling thread's last failure ("" if none). */
+const char* tide_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TIDE_H */

@@ -1,0 +1,18 @@
+"""Layout-aware FSDP2 collective local stages on MI355X (gfx950).
+
+  Plan                   host shard-layout plan (dimension-0 shards, padding)
+  reduce_scatter_local   W ranks' bf16 gradients -> W packed fp32 shards
+  allgather_copyout      rank-major bf16 buffer -> per-parameter tensors
+
+The work runs in the HIP library libtide.so (include/tide.h); importing this
+package fails if that library has not been built.
+"""
+from .tide import (  # noqa: F401
+    FLAG_NT_LOADS,
+    FLAG_NT_STORES,
+    MAX_WORLD,
+    Plan,
+    TideError,
+    allgather_copyout,
+    reduce_scatter_local,
+)

@@ -1,0 +1,148 @@
+// Host shard-layout planner: the dimension-0 shard geometry of "The Endgame of
+// FSDP Communication" (Wang et al.), Section 2.1, turned into the segment
+// table the kernels walk.  The placement is decided here once per plan, so a
+// call only passes tensor pointers (Section 6: gradient pointers as kernel
+// parameters, a segment table uploaded at registration).
+#include <string>
+#include <vector>
+
+#include "tide_internal.h"
+
+namespace tide {
+
+tide_status build_geometry(int32_t world, int32_t nparams, const int32_t* ndims, const int64_t* dims,
+                           Geometry* g, std::string* why) {
+  if (world < 1 || world > TIDE_MAX_WORLD) {
+    *why = "world must be in [1, " + std::to_string(TIDE_MAX_WORLD) + "], got " + std::to_string(world);
+    return TIDE_ERR_INVALID;
+  }
+  if (nparams < 1) {
+    *why = "nparams must be >= 1, got " + std::to_string(nparams);
+    return TIDE_ERR_INVALID;
+  }
+  if (ndims == nullptr || dims == nullptr) {
+    *why = "ndims and dims must not be NULL";
+    return TIDE_ERR_INVALID;
+  }
+  g->world = world;
+  g->nparams = nparams;
+  g->D.assign(nparams, 0);
+  g->K.assign(nparams, 0);
+  g->R.assign(nparams, 0);
+  g->n.assign(nparams, 0);
+  g->o.assign(nparams, 0);
+  int64_t pos = 0, offset = 0;
+  for (int32_t p = 0; p < nparams; ++p) {
+    if (ndims[p] < 1) {
+      *why = "parameter " + std::to_string(p) + " has " + std::to_string(ndims[p]) +
+             " dimensions; at least 1 is required";
+      return TIDE_ERR_INVALID;
+    }
+    int64_t rows = dims[pos];
+    int64_t row_len = 1;
+    for (int32_t j = 0; j < ndims[p]; ++j) {
+      if (dims[pos + j] < 0) {
+        *why = "parameter " + std::to_string(p) + " has a negative dimension";
+        return TIDE_ERR_INVALID;
+      }
+      if (j > 0 && __builtin_mul_overflow(row_len, dims[pos + j], &row_len)) {
+        *why = "parameter " + std::to_string(p) + " is too large";
+        return TIDE_ERR_RANGE;
+      }
+    }
+    pos += ndims[p];
+    int64_t numel, shard;
+    const int64_t rows_per_rank = rows / world + (rows % world != 0);
+    if (__builtin_mul_overflow(rows, row_len, &numel) ||
+        __builtin_mul_overflow(rows_per_rank, row_len, &shard) ||
+        __builtin_mul_overflow(shard, int64_t(world), &numel)) {
+      *why = "parameter " + std::to_string(p) + " is too large";
+      return TIDE_ERR_RANGE;
+    }
+    g->D[p] = rows;
+    g->K[p] = row_len;
+    g->R[p] = rows_per_rank;
+    g->n[p] = shard;
+    g->o[p] = offset;
+    if (__builtin_add_overflow(offset, shard, &offset)) {
+      *why = "the per-rank shard overflows int64";
+      return TIDE_ERR_RANGE;
+    }
+  }
+  int64_t whole;
+  if (__builtin_mul_overflow(offset, int64_t(world), &whole)) {
+    *why = "W * S overflows int64";
+    return TIDE_ERR_RANGE;
+  }
+  g->S = offset;
+  return TIDE_OK;
+}
+
+int64_t real_elems(const Geometry& g, int32_t p, int32_t r) {
+  const int64_t first_row = int64_t(r) * g.R[p];
+  int64_t rows = g.D[p] - first_row;
+  if (rows < 0) rows = 0;
+  if (rows > g.R[p]) rows = g.R[p];
+  return rows * g.K[p];
+}
+
+std::vector<Seg> rs_segments(const Geometry& g) {
+  std::vector<Seg> segs;
+  for (int32_t r = 0; r < g.world; ++r) {
+    for (int32_t p = 0; p < g.nparams; ++p) {
+      const int64_t real = real_elems(g, p, r);
+      const int64_t src = int64_t(r) * g.n[p];  // first element of rows [r R_p, ...) in G_p
+      if (real > 0) segs.push_back(Seg{src, g.o[p], real, 0, p, r, kSum, 0});
+      if (g.n[p] > real) segs.push_back(Seg{0, g.o[p] + real, g.n[p] - real, 0, p, r, kZero, 0});
+    }
+  }
+  return segs;
+}
+
+std::vector<Seg> copyout_segments(const Geometry& g) {
+  std::vector<Seg> segs;
+  for (int32_t r = 0; r < g.world; ++r) {
+    for (int32_t p = 0; p < g.nparams; ++p) {
+      const int64_t real = real_elems(g, p, r);
+      if (real > 0) segs.push_back(Seg{int64_t(r) * g.S + g.o[p], int64_t(r) * g.n[p], real, 0, 0, p, kCopy, 0});
+    }
+  }
+  return segs;
+}
+
+int64_t assign_chunks(std::vector<Seg>* segs, int64_t chunk) {
+  int64_t total = 0;
+  for (Seg& s : *segs) {
+    const int64_t c = s.len / chunk + (s.len % chunk != 0);
+    s.chunk_begin = total;
+    total += c;
+  }
+  return total;
+}
+
+tide_status resolve_options(const tide_options* in, tide_options* out, std::string* why) {
+  tide_options o{0, 0, 0, 0};
+  if (in) o = *in;
+  if (o.cu_budget < 0 || o.wg_per_cu < 0 || o.chunk_elems < 0) {
+    *why = "tide_options fields must be >= 0";
+    return TIDE_ERR_INVALID;
+  }
+  if (o.wg_per_cu == 0) o.wg_per_cu = kDefaultWgPerCu;
+  if (o.chunk_elems == 0) o.chunk_elems = kDefaultChunk;
+  if (o.chunk_elems % 8 != 0 || o.chunk_elems > kMaxChunk) {
+    *why = "chunk_elems must be a multiple of 8 and at most 2^30";
+    return TIDE_ERR_INVALID;
+  }
+  if (o.wg_per_cu > 64) {
+    *why = "wg_per_cu must be at most 64";
+    return TIDE_ERR_RANGE;
+  }
+  if (o.flags & ~(TIDE_FLAG_NT_LOADS | TIDE_FLAG_NT_STORES)) {
+    *why = "unknown bits in tide_options.flags";
+    return TIDE_ERR_INVALID;
+  }
+  *out = o;
+  return TIDE_OK;
+}
+
+}  // namespace tide

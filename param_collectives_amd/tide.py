@@ -1,0 +1,219 @@
+"""Python binding of libtide (include/tide.h): argument marshalling only.
+
+Every step of the reduce-scatter local stage and the all-gather copy-out runs
+in the HIP library; this module turns torch tensors into device pointers and
+the current HIP stream, checks that each tensor has the size, dtype, device
+and contiguity the plan expects (so that no kernel is launched on a buffer
+smaller than the plan assumes), and raises on a non-zero status.  There is no
+fallback: without the compiled library, importing this module fails.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(_HERE, "libtide.so")
+
+TIDE_OK = 0
+STATUS_NAMES = {
+    0: "TIDE_OK",
+    -1: "TIDE_ERR_INVALID",
+    -2: "TIDE_ERR_RANGE",
+    -3: "TIDE_ERR_ALIGN",
+    -4: "TIDE_ERR_NOMEM",
+    -5: "TIDE_ERR_HIP",
+    -6: "TIDE_ERR_UNSUPPORTED",
+}
+FLAG_NT_LOADS = 0x1
+FLAG_NT_STORES = 0x2
+MAX_WORLD = 256
+
+# Every symbol include/tide.h declares.
+EXPORTS = (
+    "tide_plan_create",
+    "tide_plan_layout",
+    "tide_plan_segments",
+    "tide_plan_set_options",
+    "tide_plan_get_options",
+    "tide_reduce_scatter_local",
+    "tide_allgather_copyout",
+    "tide_plan_destroy",
+    "tide_last_error",
+)
+
+
+class TideError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class Options(ctypes.Structure):
+    _fields_ = [("cu_budget", ctypes.c_int32), ("wg_per_cu", ctypes.c_int32),
+                ("chunk_elems", ctypes.c_int64), ("flags", ctypes.c_uint32)]
+
+
+def _load():
+    if not os.path.exists(LIBRARY):
+        raise ImportError(f"{LIBRARY} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
+                          "(the HIP path has no fallback)")
+    lib = ctypes.CDLL(LIBRARY)
+    vp, i32, i64, i64p = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.POINTER(ctypes.c_int64)
+    lib.tide_plan_create.argtypes = [i32, i32, ctypes.POINTER(i32), i64p, ctypes.POINTER(Options),
+                                     ctypes.POINTER(vp)]
+    lib.tide_plan_layout.argtypes = [vp, i64p, i64p, i64p]
+    lib.tide_plan_segments.argtypes = [vp, i32, i64p, i64, i64p]
+    lib.tide_plan_set_options.argtypes = [vp, ctypes.POINTER(Options)]
+    lib.tide_plan_get_options.argtypes = [vp, ctypes.POINTER(Options)]
+    lib.tide_reduce_scatter_local.argtypes = [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.c_float, i32, vp]
+    lib.tide_allgather_copyout.argtypes = [vp, vp, ctypes.POINTER(vp), vp]
+    lib.tide_plan_destroy.argtypes = [vp]
+    lib.tide_plan_destroy.restype = None
+    lib.tide_last_error.argtypes = []
+    lib.tide_last_error.restype = ctypes.c_char_p
+    for name in EXPORTS[:-2]:
+        getattr(lib, name).restype = ctypes.c_int
+    return lib
+
+
+lib = _load()
+
+
+def _check(status):
+    if status != TIDE_OK:
+        raise TideError(status, lib.tide_last_error().decode(errors="replace"))
+
+
+def _options(cu_budget=0, wg_per_cu=0, chunk_elems=0, flags=0):
+    return Options(int(cu_budget), int(wg_per_cu), int(chunk_elems), int(flags))
+
+
+def _ptr_array(values):
+    return (ctypes.c_void_p * max(len(values), 1))(*[int(v) if v else None for v in values])
+
+
+class Plan:
+    """A shard-layout plan for `world` simulated ranks and the given parameter
+    shapes (tide_plan_create)."""
+
+    def __init__(self, world, shapes, cu_budget=0, wg_per_cu=0, chunk_elems=0, flags=0):
+        self.world = int(world)
+        self.shapes = [tuple(int(d) for d in s) for s in shapes]
+        ndims = (ctypes.c_int32 * max(len(self.shapes), 1))(*[len(s) for s in self.shapes])
+        flat = [d for s in self.shapes for d in s]
+        dims = (ctypes.c_int64 * max(len(flat), 1))(*flat)
+        handle = ctypes.c_void_p()
+        opt = _options(cu_budget, wg_per_cu, chunk_elems, flags)
+        _check(lib.tide_plan_create(self.world, len(self.shapes), ndims, dims, ctypes.byref(opt),
+                                    ctypes.byref(handle)))
+        self.handle = handle
+        R = np.zeros(len(self.shapes), dtype=np.int64)
+        o = np.zeros(len(self.shapes), dtype=np.int64)
+        S = np.zeros(1, dtype=np.int64)
+        _check(lib.tide_plan_layout(self.handle, R.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                    o.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                    S.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))))
+        self.rows_per_rank, self.shard_offset, self.shard_elems = R, o, int(S[0])
+        self.numel = [int(np.prod(s, dtype=np.int64)) for s in self.shapes]
+
+    def segments(self, op):
+        """The work segments (op 0: reduce-scatter, 1: copy-out) as an int64
+        array of rows (kind, src_idx, dst_idx, src_off, dst_off, len)."""
+        count = ctypes.c_int64()
+        _check(lib.tide_plan_segments(self.handle, int(op), None, 0, ctypes.byref(count)))
+        table = np.zeros((max(count.value, 1), 6), dtype=np.int64)
+        _check(lib.tide_plan_segments(self.handle, int(op), table.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                      count.value, ctypes.byref(count)))
+        return table[:count.value]
+
+    def set_options(self, cu_budget=0, wg_per_cu=0, chunk_elems=0, flags=0):
+        opt = _options(cu_budget, wg_per_cu, chunk_elems, flags)
+        _check(lib.tide_plan_set_options(self.handle, ctypes.byref(opt)))
+
+    def options(self):
+        opt = Options()
+        _check(lib.tide_plan_get_options(self.handle, ctypes.byref(opt)))
+        return {"cu_budget": opt.cu_budget, "wg_per_cu": opt.wg_per_cu, "chunk_elems": opt.chunk_elems,
+                "flags": opt.flags}
+
+    def destroy(self):
+        if getattr(self, "handle", None):
+            lib.tide_plan_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+    # ------------------------------------------------------------ raw calls
+
+    def reduce_scatter_local_raw(self, grad_ptrs, out_ptrs, alpha=1.0, accumulate=0, stream=0):
+        """tide_reduce_scatter_local on raw device addresses: grad_ptrs[u*P+p],
+        out_ptrs[r] (ints), stream a hipStream_t handle (int)."""
+        _check(lib.tide_reduce_scatter_local(self.handle, _ptr_array(grad_ptrs), _ptr_array(out_ptrs),
+                                             float(alpha), int(accumulate), ctypes.c_void_p(int(stream) or None)))
+
+    def allgather_copyout_raw(self, rank_major_ptr, param_ptrs, stream=0):
+        """tide_allgather_copyout on raw device addresses."""
+        _check(lib.tide_allgather_copyout(self.handle, ctypes.c_void_p(int(rank_major_ptr) or None),
+                                          _ptr_array(param_ptrs), ctypes.c_void_p(int(stream) or None)))
+
+
+def _stream_handle(stream):
+    import torch
+
+    s = torch.cuda.current_stream() if stream is None else stream
+    return int(s.cuda_stream)
+
+
+def _require(t, dtype, numel, what):
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what}: expected a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{what}: expected a GPU tensor, got {t.device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{what}: expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what}: expected a contiguous tensor")
+    if t.numel() != numel:
+        raise ValueError(f"{what}: expected {numel} elements, got {t.numel()}")
+
+
+def reduce_scatter_local(plan, grads, outs, alpha=1.0, accumulate=False, stream=None):
+    """Reduce-scatter local stage: grads[u][p] (bf16, plan.shapes[p]) for u in
+    [0, W) -> outs[r] (fp32, plan.shard_elems elements) for r in [0, W)."""
+    import torch
+
+    W, P = plan.world, len(plan.shapes)
+    if len(grads) != W or any(len(row) != P for row in grads):
+        raise ValueError(f"grads must be {W} lists of {P} tensors")
+    if len(outs) != W:
+        raise ValueError(f"outs must hold {W} tensors")
+    ptrs = []
+    for u in range(W):
+        for p in range(P):
+            _require(grads[u][p], torch.bfloat16, plan.numel[p], f"grads[{u}][{p}]")
+            ptrs.append(grads[u][p].data_ptr())
+    for r in range(W):
+        _require(outs[r], torch.float32, plan.shard_elems, f"outs[{r}]")
+    plan.reduce_scatter_local_raw(ptrs, [o.data_ptr() for o in outs], alpha, int(bool(accumulate)),
+                                  _stream_handle(stream))
+
+
+def allgather_copyout(plan, rank_major, params, stream=None):
+    """All-gather copy-out: rank_major (bf16, W*S elements) -> params[p]
+    (bf16, plan.shapes[p])."""
+    import torch
+
+    P = len(plan.shapes)
+    _require(rank_major, torch.bfloat16, plan.world * plan.shard_elems, "rank_major")
+    if len(params) != P:
+        raise ValueError(f"params must hold {P} tensors")
+    for p in range(P):
+        _require(params[p], torch.bfloat16, plan.numel[p], f"params[{p}]")
+    plan.allgather_copyout_raw(rank_major.data_ptr(), [t.data_ptr() for t in params], _stream_handle(stream))

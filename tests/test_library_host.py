@@ -1,0 +1,232 @@
+"""Host-side checks of the HIP library (no GPU needed): it loads, exports
+every symbol the header declares, its planner agrees with the oracle's, its
+segment table describes exactly the oracle's result, and argument errors are
+reported before any device work."""
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from tests import oracle_pins
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def tide():
+    from param_collectives_amd import tide
+
+    return tide
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "tide.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tide_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol(tide):
+    declared = header_functions()
+    assert declared == sorted(tide.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", tide.LIBRARY], check=True, capture_output=True,
+                         text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    missing = [s for s in declared if s not in exported]
+    assert not missing, missing
+    for name in declared:
+        assert hasattr(tide.lib, name)
+
+
+def test_library_has_no_oracle_dependency(tide):
+    out = subprocess.run(["ldd", tide.LIBRARY], check=True, capture_output=True, text=True).stdout
+    assert "oracle" not in out
+    syms = subprocess.run(["nm", "-D", tide.LIBRARY], check=True, capture_output=True, text=True).stdout
+    assert "oracle_" not in syms
+
+
+CASES = [
+    (4, oracle_pins.TINY_SHAPES),
+    (8, [(4096, 4096), (1024, 4096), (4096,)]),
+    (8, [(6, 5120), (5120,), (13824, 5120)]),
+    (1, [(5, 3), (7,)]),
+    (3, [(0, 4), (2, 0), (1,), (10, 1, 3)]),
+    (256, [(300, 2), (1,)]),
+]
+
+
+@pytest.mark.parametrize("world,shapes", CASES)
+def test_layout_matches_oracle(tide, oracle_mod, world, shapes):
+    plan = tide.Plan(world, shapes)
+    geo = oracle_mod.plan(world, shapes)
+    assert list(plan.rows_per_rank) == list(geo["R"])
+    assert list(plan.shard_offset) == list(geo["o"])
+    assert plan.shard_elems == geo["S"]
+
+
+@pytest.mark.parametrize("world,shapes", CASES)
+def test_segments_describe_the_oracle_layout(tide, oracle_mod, world, shapes):
+    """Each (rank, parameter) pair's real part is one sum segment reading
+    n_real elements at the owner's first row, and its padding one zero
+    segment; copy-out segments move exactly the real elements."""
+    plan = tide.Plan(world, shapes)
+    geo = oracle_mod.plan(world, shapes)
+    rs = plan.segments(0)
+    co = plan.segments(1)
+    assert np.all(rs[:, 5] > 0) and np.all(co[:, 5] > 0)
+    for p in range(len(shapes)):
+        for r in range(world):
+            real = geo["n_real"][p, r]
+            pad = geo["n"][p] - real
+            sums = rs[(rs[:, 0] == 0) & (rs[:, 1] == p) & (rs[:, 2] == r)]
+            zeros = rs[(rs[:, 0] == 1) & (rs[:, 1] == p) & (rs[:, 2] == r)]
+            copies = co[(co[:, 2] == p) & (co[:, 4] == r * geo["n"][p])]
+            if real:
+                assert len(sums) == 1 and tuple(sums[0, 3:]) == (r * geo["n"][p], geo["o"][p], real)
+                assert len(copies) == 1 and tuple(copies[0, 3:]) == (geo["rank_major_offset"][p, r],
+                                                                    r * geo["R"][p] * geo["K"][p], real)
+            else:
+                assert len(sums) == 0
+            if pad:
+                assert len(zeros) == 1 and tuple(zeros[0, 4:]) == (geo["o"][p] + real, pad)
+            else:
+                assert len(zeros) == 0
+    assert rs[:, 5].sum() == world * geo["S"]  # every output element written once
+    assert co[:, 5].sum() == sum(int(np.prod(s)) for s in shapes)
+
+
+def _emulate_rs(plan, grads_f32):
+    """Walk the library's segment table on the CPU (rank order, fp32)."""
+    W, S = plan.world, plan.shard_elems
+    outs = [np.full(S, np.nan, dtype=np.float32) for _ in range(W)]
+    for kind, p, r, so, do, n in plan.segments(0):
+        if kind == 1:
+            outs[r][do:do + n] = 0.0
+        else:
+            acc = grads_f32[0][p].reshape(-1)[so:so + n].copy()
+            for u in range(1, W):
+                acc = acc + grads_f32[u][p].reshape(-1)[so:so + n]
+            outs[r][do:do + n] = acc
+    return outs
+
+
+def test_segment_table_walk_reproduces_oracle(tide, oracle_mod):
+    rng = np.random.default_rng(5)
+    for world, shapes in CASES[:5]:
+        if sum(int(np.prod(s)) for s in shapes) > 10**6:
+            continue
+        plan = tide.Plan(world, shapes)
+        grads = [[oracle_pins.rand_bf16(rng, s) for s in shapes] for _ in range(world)]
+        want = oracle_mod.rs_local(world, shapes, grads)
+        f32 = [[oracle_pins.f32_from_bf16(g) for g in row] for row in grads]
+        got = _emulate_rs(plan, f32)
+        for r in range(world):
+            assert oracle_pins.same_bits(got[r], want[r])
+
+
+# ------------------------------------------------------------ error paths
+
+
+def _status(excinfo):
+    return excinfo.value.status
+
+
+def test_plan_create_rejects_bad_arguments(tide):
+    with pytest.raises(tide.TideError) as e:
+        tide.Plan(0, [(4,)])
+    assert _status(e) == -1
+    with pytest.raises(tide.TideError) as e:
+        tide.Plan(tide.MAX_WORLD + 1, [(4,)])
+    assert _status(e) == -1
+    with pytest.raises(tide.TideError) as e:
+        tide.Plan(2, [])
+    assert _status(e) == -1
+    with pytest.raises(tide.TideError) as e:
+        tide.Plan(2, [()])
+    assert _status(e) == -1
+    with pytest.raises(tide.TideError) as e:
+        tide.Plan(2, [(3, -2)])
+    assert _status(e) == -1
+    with pytest.raises(tide.TideError) as e:
+        tide.Plan(2, [(2**40, 2**30)])
+    assert _status(e) == -2
+    with pytest.raises(tide.TideError) as e:
+        tide.Plan(2, [(4,)], chunk_elems=12)
+    assert _status(e) == -1
+    with pytest.raises(tide.TideError) as e:
+        tide.Plan(2, [(4,)], wg_per_cu=-1)
+    assert _status(e) == -1
+    with pytest.raises(tide.TideError) as e:
+        tide.Plan(2, [(4,)], flags=0x80)
+    assert _status(e) == -1
+
+
+# Host addresses that are never dereferenced: every call below must fail its
+# argument checks before any device work.
+FAKE = 0x7F0000000000
+
+
+def test_reduce_scatter_argument_errors(tide):
+    plan = tide.Plan(4, oracle_pins.TINY_SHAPES)
+    W, P = 4, 4
+    good_g = [FAKE + 0x1000 * i for i in range(W * P)]
+    good_o = [FAKE + 0x100000 + 0x1000 * r for r in range(W)]
+    cases = [
+        (dict(alpha=2.0), -6),
+        (dict(accumulate=1), -6),
+        (dict(grad_ptrs=good_g[:5] + [0] + good_g[6:]), -1),
+        (dict(grad_ptrs=good_g[:5] + [FAKE + 1] + good_g[6:]), -3),
+        (dict(out_ptrs=good_o[:2] + [0] + good_o[3:]), -1),
+        (dict(out_ptrs=good_o[:2] + [FAKE + 2] + good_o[3:]), -3),
+    ]
+    for kw, status in cases:
+        args = dict(grad_ptrs=good_g, out_ptrs=good_o, alpha=1.0, accumulate=0)
+        args.update(kw)
+        with pytest.raises(tide.TideError) as e:
+            plan.reduce_scatter_local_raw(args["grad_ptrs"], args["out_ptrs"], args["alpha"], args["accumulate"])
+        assert _status(e) == status, kw
+        assert tide.lib.tide_last_error()
+
+
+def test_copyout_argument_errors(tide):
+    plan = tide.Plan(4, oracle_pins.TINY_SHAPES)
+    good_p = [FAKE + 0x1000 * i for i in range(4)]
+    with pytest.raises(tide.TideError) as e:
+        plan.allgather_copyout_raw(FAKE, good_p[:1] + [0] + good_p[2:])
+    assert _status(e) == -1
+    with pytest.raises(tide.TideError) as e:
+        plan.allgather_copyout_raw(FAKE, good_p[:1] + [FAKE + 3] + good_p[2:])
+    assert _status(e) == -3
+    with pytest.raises(tide.TideError) as e:
+        plan.allgather_copyout_raw(FAKE + 1, good_p)
+    assert _status(e) == -3
+    with pytest.raises(tide.TideError) as e:
+        plan.allgather_copyout_raw(0, good_p)
+    assert _status(e) == -1
+
+
+def test_destroyed_plan_is_rejected(tide):
+    plan = tide.Plan(2, [(4,)])
+    handle = plan.handle
+    plan.destroy()
+    import ctypes
+
+    R = (ctypes.c_int64 * 1)()
+    assert tide.lib.tide_plan_layout(handle, R, None, None) == -1
+    assert b"destroyed" in tide.lib.tide_last_error()
+    tide.lib.tide_plan_destroy(handle)  # a second destroy is harmless
+    tide.lib.tide_plan_destroy(None)
+
+
+def test_options_round_trip_and_validation(tide):
+    plan = tide.Plan(8, [(64, 64)], cu_budget=16, wg_per_cu=2, chunk_elems=1024, flags=tide.FLAG_NT_LOADS)
+    assert plan.options() == {"cu_budget": 16, "wg_per_cu": 2, "chunk_elems": 1024, "flags": 1}
+    before = plan.segments(0).copy()
+    plan.set_options(chunk_elems=8)
+    assert plan.options()["chunk_elems"] == 8
+    assert np.array_equal(plan.segments(0), before)  # knobs never change the work
+    with pytest.raises(tide.TideError):
+        plan.set_options(chunk_elems=7)
+    with pytest.raises(tide.TideError):
+        plan.set_options(wg_per_cu=1000)
