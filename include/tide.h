@@ -64,20 +64,24 @@ typedef enum {
 /* Largest number of simulated ranks a plan may have. */
 #define TIDE_MAX_WORLD 256
 
-/* tide_options.flags */
-#define TIDE_FLAG_NT_LOADS 0x1u  /* stream global loads with the non-temporal hint */
-#define TIDE_FLAG_NT_STORES 0x2u /* write outputs with the non-temporal hint */
+/* tide_options.flags.  By default both kernels stream: loads and stores
+ * carry the non-temporal hint (the data is touched once). */
+#define TIDE_FLAG_CACHED_LOADS 0x1u  /* plain (temporal) loads instead */
+#define TIDE_FLAG_CACHED_STORES 0x2u /* plain (temporal) stores instead */
 
 /*
- * Launch knobs.  A field of 0 selects the default.  None of them changes any
- * result bit (Section 4.3: tuning knobs preserve operand grouping).
- *   cu_budget   workgroups are launched for this many CUs' worth of the
- *               persistent grid (grid = cu_budget * wg_per_cu, at most one
- *               workgroup per chunk); default: every CU of the device.
- *               Workgroups are dispatched round-robin over the 8 XCDs, so a
- *               budget is a grid size, not a CU mask.
- *   wg_per_cu   workgroups (256 threads each) per budgeted CU; default 8.
- *   chunk_elems elements per work chunk, a multiple of 8; default 4096.
+ * Launch knobs.  A numeric field of 0 selects the default of the operation
+ * being launched.  None of them changes any result bit (Section 4.3: tuning
+ * knobs preserve operand grouping).
+ *   cu_budget   the persistent grid has cu_budget * wg_per_cu workgroups
+ *               (fewer if there are fewer chunks than waves); default: the
+ *               device's CU count.  Workgroups are dispatched round-robin over
+ *               the 8 XCDs, so a budget is a grid size, not a CU mask.
+ *   wg_per_cu   workgroups (256 threads, four waves) per budgeted CU;
+ *               default 1.
+ *   chunk_elems elements per chunk (the unit a wave takes), a multiple of 8,
+ *               at most 2^30; default 1024 (reduce-scatter), 4096 (copy-out).
+ *               A plan may have at most 2^31 - 1 chunks per operation.
  *   flags       TIDE_FLAG_* bits.
  */
 typedef struct {
@@ -102,8 +106,8 @@ typedef struct tide_plan tide_plan; /* opaque, owned by the library */
  * and uploaded by the first reduce-scatter or copy-out call that uses it, on
  * the device current at that time (that first call blocks the host for the
  * allocation); the plan is bound to that device afterwards.
- * Errors: TIDE_ERR_INVALID (bad counts, shapes, null pointers),
- * TIDE_ERR_RANGE (sizes overflow int64), TIDE_ERR_NOMEM.
+ * Errors: TIDE_ERR_INVALID (bad counts, shapes, options, null pointers),
+ * TIDE_ERR_RANGE (sizes overflow int64, too many chunks), TIDE_ERR_NOMEM.
  */
 tide_status tide_plan_create(int32_t world, int32_t nparams, const int32_t* ndims, const int64_t* dims,
                              const tide_options* opt, tide_plan** out_plan);
@@ -135,12 +139,14 @@ tide_status tide_plan_layout(const tide_plan* plan, int64_t* rows_per_rank, int6
 tide_status tide_plan_segments(const tide_plan* plan, int32_t op, int64_t* table, int64_t capacity,
                                int64_t* count);
 
-/* Replace the launch knobs (NULL = defaults).  Results are unaffected. */
+/* Replace the launch knobs (NULL = defaults).  Results are unaffected.
+ * Errors: TIDE_ERR_INVALID, TIDE_ERR_RANGE (too many chunks). */
 tide_status tide_plan_set_options(tide_plan* plan, const tide_options* opt);
 
-/* The launch knobs in effect, with defaults resolved where known (cu_budget
- * is resolved once the plan is bound to a device, 0 before). */
-tide_status tide_plan_get_options(const tide_plan* plan, tide_options* out);
+/* The launch knobs in effect for op 0 (reduce-scatter) or 1 (copy-out), with
+ * defaults resolved (cu_budget is resolved once the plan is bound to a
+ * device, 0 before). */
+tide_status tide_plan_get_options(const tide_plan* plan, int32_t op, tide_options* out);
 
 /*
  * Reduce-scatter local stage (Section 4, Equation 5; Section 4.3).

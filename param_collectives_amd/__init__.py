@@ -8,8 +8,8 @@ The work runs in the HIP library libtide.so (include/tide.h); importing this
 package fails if that library has not been built.
 """
 from .tide import (  # noqa: F401
-    FLAG_NT_LOADS,
-    FLAG_NT_STORES,
+    FLAG_CACHED_LOADS,
+    FLAG_CACHED_STORES,
     MAX_WORLD,
     Plan,
     TideError,

@@ -1,0 +1,439 @@
+// C ABI of libtide (include/tide.h): plan lifetime, argument checks, device
+// tables and kernel launches for the layout-aware FSDP2 collective local
+// stages ("The Endgame of FSDP Communication", Wang et al., Sections 2.1, 4
+// and 6).  Host code only; the kernels are in kernels.hip.
+//
+// Device state of a plan (allocated on its first launch, on the device that
+// is current then):
+//   chunk table   per operation, the first-chunk index of every segment
+//                 (fixed by the plan and its chunk size; re-uploaded when the
+//                 chunk size changes);
+//   call table    per operation, every segment's resolved source and
+//                 destination pointers and vector-body start, rebuilt on the
+//                 host and re-uploaded only when a call passes pointers that
+//                 differ from the previous call's (Section 6: no per-call
+//                 metadata copy in steady state).
+// Uploads go through pinned staging buffers with hipMemcpyAsync on the
+// caller's stream, so they are ordered before the launch that reads them.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <unordered_set>
+#include <vector>
+
+#include "tide_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+tide_status fail(tide_status st, const std::string& msg) {
+  g_last_error = msg;
+  return st;
+}
+
+tide_status hip_fail(hipError_t e, const char* what) {
+  return fail(TIDE_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// One host->device upload channel: a pinned staging buffer whose previous
+// copy must have finished before it is rewritten.
+struct Upload {
+  void* host = nullptr;
+  size_t bytes = 0;
+  hipEvent_t done = nullptr;
+  bool pending = false;
+};
+
+// Device tables of one operation.
+struct OpState {
+  std::vector<tide::Seg> segs;
+  std::vector<int32_t> chunk_begin;  // host copy, [nseg + 1]
+  bool chunks_stale = true;
+  int32_t* d_chunk_begin = nullptr;
+  void* d_call = nullptr;            // [CallHdr x nseg | pointers x nseg*(nsrc+1)]
+  size_t call_bytes = 0;
+  std::vector<const void*> key;      // pointers of the last uploaded call table
+  bool key_valid = false;
+  std::vector<tide::CallHdr> hdr;    // host scratch for building the call table
+  std::vector<const void*> ptrs;
+  std::vector<unsigned char> call_host;
+  Upload up_chunks, up_call;
+};
+
+}  // namespace
+
+struct tide_plan {
+  uint64_t magic = 0;
+  tide::Geometry geo;
+  tide_options given{};  // as passed (0 = default)
+  OpState rs, co;
+  int device = -1;
+  int cu_count = 0;
+};
+
+namespace {
+
+constexpr uint64_t kMagic = 0x7469646570616e32ull;
+std::mutex g_plans_mu;
+std::unordered_set<const tide_plan*> g_plans;
+
+bool live(const tide_plan* p) {
+  if (p == nullptr) return false;
+  std::lock_guard<std::mutex> lock(g_plans_mu);
+  return g_plans.count(p) != 0 && p->magic == kMagic;
+}
+
+int32_t nsrc_of(const tide_plan* p, tide::Op op) { return op == tide::kOpRs ? p->geo.world : 1; }
+
+tide_status rebuild_chunks(tide_plan* p, const tide_options& given) {
+  std::string why;
+  std::vector<int32_t> rs_cb, co_cb;
+  const tide_options rs_opt = tide::effective_options(given, tide::kOpRs, 0);
+  const tide_options co_opt = tide::effective_options(given, tide::kOpCo, 0);
+  tide_status st = tide::chunk_table(p->rs.segs, rs_opt.chunk_elems, &rs_cb, &why);
+  if (st == TIDE_OK) st = tide::chunk_table(p->co.segs, co_opt.chunk_elems, &co_cb, &why);
+  if (st != TIDE_OK) return fail(st, why);
+  p->rs.chunk_begin.swap(rs_cb);
+  p->co.chunk_begin.swap(co_cb);
+  p->rs.chunks_stale = p->co.chunks_stale = true;
+  return TIDE_OK;
+}
+
+tide_status make_upload(Upload* u, size_t bytes) {
+  u->bytes = bytes;
+  if (bytes == 0) return TIDE_OK;
+  hipError_t e = hipHostMalloc(&u->host, bytes, hipHostMallocDefault);
+  if (e != hipSuccess) {
+    u->host = nullptr;
+    return fail(TIDE_ERR_NOMEM, std::string("hipHostMalloc: ") + hipGetErrorString(e));
+  }
+  e = hipEventCreateWithFlags(&u->done, hipEventDisableTiming);
+  if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags");
+  return TIDE_OK;
+}
+
+void free_upload(Upload* u) {
+  if (u->done) {
+    if (u->pending) (void)hipEventSynchronize(u->done);
+    (void)hipEventDestroy(u->done);
+  }
+  if (u->host) (void)hipHostFree(u->host);
+  *u = Upload{};
+}
+
+tide_status upload(Upload* u, void* dev, const void* src, size_t bytes, hipStream_t stream) {
+  if (bytes == 0) return TIDE_OK;
+  if (u->pending) {
+    hipError_t e = hipEventSynchronize(u->done);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    u->pending = false;
+  }
+  std::memcpy(u->host, src, bytes);
+  hipError_t e = hipMemcpyAsync(dev, u->host, bytes, hipMemcpyHostToDevice, stream);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync");
+  e = hipEventRecord(u->done, stream);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  u->pending = true;
+  return TIDE_OK;
+}
+
+template <typename T>
+tide_status dev_alloc(T** out, size_t bytes) {
+  *out = nullptr;
+  if (bytes == 0) return TIDE_OK;
+  hipError_t e = hipMalloc(reinterpret_cast<void**>(out), bytes);
+  if (e != hipSuccess) {
+    *out = nullptr;
+    return fail(TIDE_ERR_NOMEM, std::string("hipMalloc: ") + hipGetErrorString(e));
+  }
+  return TIDE_OK;
+}
+
+void release_op(OpState* s) {
+  free_upload(&s->up_chunks);
+  free_upload(&s->up_call);
+  if (s->d_chunk_begin) (void)hipFree(s->d_chunk_begin);
+  if (s->d_call) (void)hipFree(s->d_call);
+  s->d_chunk_begin = nullptr;
+  s->d_call = nullptr;
+  s->key_valid = false;
+  s->chunks_stale = true;
+}
+
+void release_device(tide_plan* p) {
+  if (p->device < 0) return;
+  int prev = -1;
+  (void)hipGetDevice(&prev);
+  (void)hipSetDevice(p->device);
+  release_op(&p->rs);
+  release_op(&p->co);
+  p->device = -1;
+  if (prev >= 0) (void)hipSetDevice(prev);
+}
+
+tide_status alloc_op(OpState* s, int32_t nsrc) {
+  const size_t nseg = s->segs.size();
+  s->call_bytes = nseg * sizeof(tide::CallHdr) + nseg * size_t(nsrc + 1) * sizeof(void*);
+  tide_status st;
+  if ((st = dev_alloc(&s->d_chunk_begin, (nseg + 1) * sizeof(int32_t))) != TIDE_OK) return st;
+  if ((st = dev_alloc(&s->d_call, s->call_bytes)) != TIDE_OK) return st;
+  if ((st = make_upload(&s->up_chunks, (nseg + 1) * sizeof(int32_t))) != TIDE_OK) return st;
+  return make_upload(&s->up_call, s->call_bytes);
+}
+
+// Bind the plan to the current device on first use.
+tide_status bind_device(tide_plan* p) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (p->device >= 0) {
+    if (dev != p->device)
+      return fail(TIDE_ERR_INVALID, "plan is bound to device " + std::to_string(p->device) + " but device " +
+                                        std::to_string(dev) + " is current");
+    return TIDE_OK;
+  }
+  int cus = 0;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+  p->device = dev;
+  p->cu_count = cus;
+  tide_status st = alloc_op(&p->rs, p->geo.world);
+  if (st == TIDE_OK) st = alloc_op(&p->co, 1);
+  if (st != TIDE_OK) {
+    const std::string why = g_last_error;
+    release_device(p);
+    return fail(st, why);
+  }
+  return TIDE_OK;
+}
+
+// Upload what is stale, then launch.
+template <typename BuildCall>
+tide_status run_op(tide_plan* p, tide::Op op, const std::vector<const void*>& key, BuildCall build,
+                   hipStream_t stream) {
+  OpState& s = op == tide::kOpRs ? p->rs : p->co;
+  const int32_t nchunks = s.chunk_begin.back();
+  if (nchunks == 0) return TIDE_OK;  // nothing to write
+  tide_status st = bind_device(p);
+  if (st != TIDE_OK) return st;
+  if (s.chunks_stale) {
+    st = upload(&s.up_chunks, s.d_chunk_begin, s.chunk_begin.data(), s.chunk_begin.size() * sizeof(int32_t),
+                stream);
+    if (st != TIDE_OK) return st;
+    s.chunks_stale = false;
+  }
+  if (!s.key_valid || s.key != key) {
+    s.key_valid = false;
+    build(&s.hdr, &s.ptrs);
+    const size_t hb = s.hdr.size() * sizeof(tide::CallHdr), pb = s.ptrs.size() * sizeof(void*);
+    s.call_host.resize(hb + pb);
+    std::memcpy(s.call_host.data(), s.hdr.data(), hb);
+    std::memcpy(s.call_host.data() + hb, s.ptrs.data(), pb);
+    st = upload(&s.up_call, s.d_call, s.call_host.data(), hb + pb, stream);
+    if (st != TIDE_OK) return st;
+    s.key = key;
+    s.key_valid = true;
+  }
+  const tide_options eff = tide::effective_options(p->given, op, p->cu_count);
+  int64_t grid = int64_t(eff.cu_budget) * eff.wg_per_cu;
+  const int64_t useful = (int64_t(nchunks) + tide::kWavesPerGroup - 1) / tide::kWavesPerGroup;
+  if (grid > useful) grid = useful;
+  if (grid < 1) grid = 1;
+  tide::KernelArgs a;
+  a.hdr = static_cast<const tide::CallHdr*>(s.d_call);
+  a.ptrs = reinterpret_cast<const void* const*>(static_cast<unsigned char*>(s.d_call) +
+                                                s.segs.size() * sizeof(tide::CallHdr));
+  a.chunk_begin = s.d_chunk_begin;
+  a.nseg = int32_t(s.segs.size());
+  a.nsrc = nsrc_of(p, op);
+  a.nchunks = nchunks;
+  a.chunk = int32_t(eff.chunk_elems);
+  a.flags = eff.flags;
+  const int rc = op == tide::kOpRs ? tide::launch_rs_local(a, grid, stream) : tide::launch_ag_copyout(a, grid, stream);
+  if (rc != 0)
+    return hip_fail(hipError_t(rc), op == tide::kOpRs ? "rs_local_kernel launch" : "ag_copyout_kernel launch");
+  return TIDE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+tide_status tide_plan_create(int32_t world, int32_t nparams, const int32_t* ndims, const int64_t* dims,
+                             const tide_options* opt, tide_plan** out_plan) {
+  g_last_error.clear();
+  if (out_plan == nullptr) return fail(TIDE_ERR_INVALID, "out_plan must not be NULL");
+  *out_plan = nullptr;
+  std::string why;
+  tide_options given;
+  tide_status st = tide::check_options(opt, &given, &why);
+  if (st != TIDE_OK) return fail(st, why);
+  tide_plan* p = new (std::nothrow) tide_plan();
+  if (p == nullptr) return fail(TIDE_ERR_NOMEM, "out of host memory");
+  st = tide::build_geometry(world, nparams, ndims, dims, &p->geo, &why);
+  if (st != TIDE_OK) {
+    delete p;
+    return fail(st, why);
+  }
+  try {
+    p->rs.segs = tide::rs_segments(p->geo);
+    p->co.segs = tide::copyout_segments(p->geo);
+  } catch (...) {
+    delete p;
+    return fail(TIDE_ERR_NOMEM, "out of host memory");
+  }
+  if (p->rs.segs.size() >= size_t(INT32_MAX) || p->co.segs.size() >= size_t(INT32_MAX)) {
+    delete p;
+    return fail(TIDE_ERR_RANGE, "too many segments");
+  }
+  p->given = given;
+  st = rebuild_chunks(p, given);
+  if (st != TIDE_OK) {
+    const std::string msg = g_last_error;
+    delete p;
+    return fail(st, msg);
+  }
+  p->magic = kMagic;
+  {
+    std::lock_guard<std::mutex> lock(g_plans_mu);
+    g_plans.insert(p);
+  }
+  *out_plan = p;
+  return TIDE_OK;
+}
+
+tide_status tide_plan_layout(const tide_plan* plan, int64_t* rows_per_rank, int64_t* shard_offset,
+                             int64_t* shard_elems) {
+  g_last_error.clear();
+  if (!live(plan)) return fail(TIDE_ERR_INVALID, "unknown or destroyed plan");
+  for (int32_t p = 0; p < plan->geo.nparams; ++p) {
+    if (rows_per_rank) rows_per_rank[p] = plan->geo.R[p];
+    if (shard_offset) shard_offset[p] = plan->geo.o[p];
+  }
+  if (shard_elems) *shard_elems = plan->geo.S;
+  return TIDE_OK;
+}
+
+tide_status tide_plan_segments(const tide_plan* plan, int32_t op, int64_t* table, int64_t capacity,
+                               int64_t* count) {
+  g_last_error.clear();
+  if (!live(plan)) return fail(TIDE_ERR_INVALID, "unknown or destroyed plan");
+  if (op != 0 && op != 1) return fail(TIDE_ERR_INVALID, "op must be 0 (reduce-scatter) or 1 (copy-out)");
+  if (count == nullptr || capacity < 0 || (capacity > 0 && table == nullptr))
+    return fail(TIDE_ERR_INVALID, "bad table/capacity/count");
+  const std::vector<tide::Seg>& segs = op == 0 ? plan->rs.segs : plan->co.segs;
+  *count = int64_t(segs.size());
+  const int64_t n = capacity < *count ? capacity : *count;
+  for (int64_t i = 0; i < n; ++i) {
+    const tide::Seg& s = segs[size_t(i)];
+    int64_t* row = table + 6 * i;
+    row[0] = s.kind;
+    row[1] = s.src_idx;
+    row[2] = s.dst_idx;
+    row[3] = s.src_off;
+    row[4] = s.dst_off;
+    row[5] = s.len;
+  }
+  return TIDE_OK;
+}
+
+tide_status tide_plan_set_options(tide_plan* plan, const tide_options* opt) {
+  g_last_error.clear();
+  if (!live(plan)) return fail(TIDE_ERR_INVALID, "unknown or destroyed plan");
+  std::string why;
+  tide_options given;
+  tide_status st = tide::check_options(opt, &given, &why);
+  if (st != TIDE_OK) return fail(st, why);
+  st = rebuild_chunks(plan, given);
+  if (st != TIDE_OK) return st;
+  plan->given = given;
+  return TIDE_OK;
+}
+
+tide_status tide_plan_get_options(const tide_plan* plan, int32_t op, tide_options* out) {
+  g_last_error.clear();
+  if (!live(plan)) return fail(TIDE_ERR_INVALID, "unknown or destroyed plan");
+  if (op != 0 && op != 1) return fail(TIDE_ERR_INVALID, "op must be 0 (reduce-scatter) or 1 (copy-out)");
+  if (out == nullptr) return fail(TIDE_ERR_INVALID, "out must not be NULL");
+  *out = tide::effective_options(plan->given, op == 0 ? tide::kOpRs : tide::kOpCo, plan->cu_count);
+  return TIDE_OK;
+}
+
+tide_status tide_reduce_scatter_local(tide_plan* plan, const uint16_t* const* grads, float* const* out,
+                                      float alpha, int32_t accumulate, void* stream) {
+  g_last_error.clear();
+  if (!live(plan)) return fail(TIDE_ERR_INVALID, "unknown or destroyed plan");
+  if (grads == nullptr || out == nullptr) return fail(TIDE_ERR_INVALID, "grads and out must not be NULL");
+  if (!(alpha == 1.0f) || accumulate != 0)
+    return fail(TIDE_ERR_UNSUPPORTED, "only alpha = 1 and accumulate = 0 are provided");
+  const tide::Geometry& g = plan->geo;
+  const int64_t W = g.world, P = g.nparams;
+  for (int64_t u = 0; u < W; ++u) {
+    for (int64_t p = 0; p < P; ++p) {
+      const uint16_t* ptr = grads[u * P + p];
+      if (g.D[p] * g.K[p] == 0) continue;
+      if (ptr == nullptr) return fail(TIDE_ERR_INVALID, "grads[" + std::to_string(u * P + p) + "] is NULL");
+      if (reinterpret_cast<uintptr_t>(ptr) & 1)
+        return fail(TIDE_ERR_ALIGN, "grads[" + std::to_string(u * P + p) + "] is not 2-byte aligned");
+    }
+  }
+  for (int64_t r = 0; r < W; ++r) {
+    if (g.S == 0) continue;
+    if (out[r] == nullptr) return fail(TIDE_ERR_INVALID, "out[" + std::to_string(r) + "] is NULL");
+    if (reinterpret_cast<uintptr_t>(out[r]) & 3)
+      return fail(TIDE_ERR_ALIGN, "out[" + std::to_string(r) + "] is not 4-byte aligned");
+  }
+  std::vector<const void*> key(grads, grads + W * P);
+  key.insert(key.end(), out, out + W);
+  return run_op(
+      plan, tide::kOpRs, key,
+      [&](std::vector<tide::CallHdr>* hdr, std::vector<const void*>* ptrs) {
+        tide::rs_call_table(g, plan->rs.segs, grads, out, hdr, ptrs);
+      },
+      static_cast<hipStream_t>(stream));
+}
+
+tide_status tide_allgather_copyout(tide_plan* plan, const uint16_t* rank_major, uint16_t* const* params,
+                                   void* stream) {
+  g_last_error.clear();
+  if (!live(plan)) return fail(TIDE_ERR_INVALID, "unknown or destroyed plan");
+  if (params == nullptr) return fail(TIDE_ERR_INVALID, "params must not be NULL");
+  const tide::Geometry& g = plan->geo;
+  const int64_t P = g.nparams;
+  for (int64_t p = 0; p < P; ++p) {
+    if (g.D[p] * g.K[p] == 0) continue;
+    if (params[p] == nullptr) return fail(TIDE_ERR_INVALID, "params[" + std::to_string(p) + "] is NULL");
+    if (reinterpret_cast<uintptr_t>(params[p]) & 1)
+      return fail(TIDE_ERR_ALIGN, "params[" + std::to_string(p) + "] is not 2-byte aligned");
+  }
+  if (plan->co.chunk_begin.back() == 0) return TIDE_OK;  // nothing to write
+  if (rank_major == nullptr) return fail(TIDE_ERR_INVALID, "rank_major must not be NULL");
+  if (reinterpret_cast<uintptr_t>(rank_major) & 1) return fail(TIDE_ERR_ALIGN, "rank_major is not 2-byte aligned");
+  std::vector<const void*> key(params, params + P);
+  key.push_back(rank_major);
+  return run_op(
+      plan, tide::kOpCo, key,
+      [&](std::vector<tide::CallHdr>* hdr, std::vector<const void*>* ptrs) {
+        tide::co_call_table(g, plan->co.segs, rank_major, params, hdr, ptrs);
+      },
+      static_cast<hipStream_t>(stream));
+}
+
+void tide_plan_destroy(tide_plan* plan) {
+  if (plan == nullptr) return;
+  {
+    std::lock_guard<std::mutex> lock(g_plans_mu);
+    if (g_plans.erase(plan) == 0) return;  // unknown or already destroyed
+  }
+  release_device(plan);
+  plan->magic = 0;
+  delete plan;
+}
+
+const char* tide_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -88,12 +88,12 @@ int64_t real_elems(const Geometry& g, int32_t p, int32_t r) {
 
 std::vector<Seg> rs_segments(const Geometry& g) {
   std::vector<Seg> segs;
-  for (int32_t r = 0; r < g.world; ++r) {
-    for (int32_t p = 0; p < g.nparams; ++p) {
+  for (int32_t p = 0; p < g.nparams; ++p) {
+    for (int32_t r = 0; r < g.world; ++r) {
       const int64_t real = real_elems(g, p, r);
       const int64_t src = int64_t(r) * g.n[p];  // first element of rows [r R_p, ...) in G_p
-      if (real > 0) segs.push_back(Seg{src, g.o[p], real, 0, p, r, kSum, 0});
-      if (g.n[p] > real) segs.push_back(Seg{0, g.o[p] + real, g.n[p] - real, 0, p, r, kZero, 0});
+      if (real > 0) segs.push_back(Seg{src, g.o[p], real, p, r, kSum});
+      if (g.n[p] > real) segs.push_back(Seg{0, g.o[p] + real, g.n[p] - real, p, r, kZero});
     }
   }
   return segs;
@@ -101,34 +101,38 @@ std::vector<Seg> rs_segments(const Geometry& g) {
 
 std::vector<Seg> copyout_segments(const Geometry& g) {
   std::vector<Seg> segs;
-  for (int32_t r = 0; r < g.world; ++r) {
-    for (int32_t p = 0; p < g.nparams; ++p) {
+  for (int32_t p = 0; p < g.nparams; ++p) {
+    for (int32_t r = 0; r < g.world; ++r) {
       const int64_t real = real_elems(g, p, r);
-      if (real > 0) segs.push_back(Seg{int64_t(r) * g.S + g.o[p], int64_t(r) * g.n[p], real, 0, 0, p, kCopy, 0});
+      if (real > 0) segs.push_back(Seg{int64_t(r) * g.S + g.o[p], int64_t(r) * g.n[p], real, 0, p, kCopy});
     }
   }
   return segs;
 }
 
-int64_t assign_chunks(std::vector<Seg>* segs, int64_t chunk) {
+tide_status chunk_table(const std::vector<Seg>& segs, int64_t chunk, std::vector<int32_t>* chunk_begin,
+                        std::string* why) {
+  chunk_begin->assign(segs.size() + 1, 0);
   int64_t total = 0;
-  for (Seg& s : *segs) {
-    const int64_t c = s.len / chunk + (s.len % chunk != 0);
-    s.chunk_begin = total;
-    total += c;
+  for (size_t s = 0; s < segs.size(); ++s) {
+    (*chunk_begin)[s] = int32_t(total);
+    total += segs[s].len / chunk + (segs[s].len % chunk != 0);
+    if (total > INT32_MAX) {
+      *why = "more than 2^31 - 1 chunks: use a larger chunk_elems";
+      return TIDE_ERR_RANGE;
+    }
   }
-  return total;
+  (*chunk_begin)[segs.size()] = int32_t(total);
+  return TIDE_OK;
 }
 
-tide_status resolve_options(const tide_options* in, tide_options* out, std::string* why) {
+tide_status check_options(const tide_options* in, tide_options* out, std::string* why) {
   tide_options o{0, 0, 0, 0};
   if (in) o = *in;
   if (o.cu_budget < 0 || o.wg_per_cu < 0 || o.chunk_elems < 0) {
     *why = "tide_options fields must be >= 0";
     return TIDE_ERR_INVALID;
   }
-  if (o.wg_per_cu == 0) o.wg_per_cu = kDefaultWgPerCu;
-  if (o.chunk_elems == 0) o.chunk_elems = kDefaultChunk;
   if (o.chunk_elems % 8 != 0 || o.chunk_elems > kMaxChunk) {
     *why = "chunk_elems must be a multiple of 8 and at most 2^30";
     return TIDE_ERR_INVALID;
@@ -137,12 +141,78 @@ tide_status resolve_options(const tide_options* in, tide_options* out, std::stri
     *why = "wg_per_cu must be at most 64";
     return TIDE_ERR_RANGE;
   }
-  if (o.flags & ~(TIDE_FLAG_NT_LOADS | TIDE_FLAG_NT_STORES)) {
+  if (o.flags & ~(TIDE_FLAG_CACHED_LOADS | TIDE_FLAG_CACHED_STORES)) {
     *why = "unknown bits in tide_options.flags";
     return TIDE_ERR_INVALID;
   }
   *out = o;
   return TIDE_OK;
+}
+
+tide_options effective_options(const tide_options& given, Op op, int32_t cu_count) {
+  tide_options o = given;
+  if (o.cu_budget == 0) o.cu_budget = cu_count;
+  if (o.wg_per_cu == 0) o.wg_per_cu = op == kOpRs ? kRsWgPerCu : kCoWgPerCu;
+  if (o.chunk_elems == 0) o.chunk_elems = op == kOpRs ? kRsChunk : kCoChunk;
+  return o;
+}
+
+namespace {
+
+// Elements to skip from `addr` (an element address of `esize` bytes) until it
+// is `align`-byte aligned.
+int64_t skip_to(uintptr_t addr, int64_t esize, uintptr_t align) {
+  return int64_t(((align - (addr & (align - 1))) & (align - 1)) / uintptr_t(esize));
+}
+
+}  // namespace
+
+void rs_call_table(const Geometry& g, const std::vector<Seg>& segs, const uint16_t* const* grads,
+                   float* const* out, std::vector<CallHdr>* hdr, std::vector<const void*>* ptrs) {
+  const int32_t W = g.world, P = g.nparams;
+  hdr->resize(segs.size());
+  ptrs->assign(segs.size() * size_t(W + 1), nullptr);
+  for (size_t s = 0; s < segs.size(); ++s) {
+    const Seg& sg = segs[s];
+    const void** row = ptrs->data() + s * size_t(W + 1);
+    float* dst = out[sg.dst_idx] + sg.dst_off;
+    row[W] = dst;
+    const uintptr_t d = reinterpret_cast<uintptr_t>(dst);
+    int32_t head = -1;
+    if (sg.kind == kZero) {
+      head = int32_t(skip_to(d, 4, 16));  // 16-byte zero stores
+    } else {
+      // 8-byte source loads and 16-byte destination stores, 4 elements each
+      const uint16_t* s0 = grads[int64_t(0) * P + sg.src_idx] + sg.src_off;
+      const uintptr_t phase = reinterpret_cast<uintptr_t>(s0) & 7;
+      bool same = true;
+      for (int32_t u = 0; u < W; ++u) {
+        const uint16_t* su = grads[int64_t(u) * P + sg.src_idx] + sg.src_off;
+        row[u] = su;
+        same = same && (reinterpret_cast<uintptr_t>(su) & 7) == phase;
+      }
+      const int64_t h = skip_to(reinterpret_cast<uintptr_t>(s0), 2, 8);
+      if (same && ((d + uintptr_t(4 * h)) & 15) == 0) head = int32_t(h);
+    }
+    (*hdr)[s] = CallHdr{sg.len, sg.kind, head};
+  }
+}
+
+void co_call_table(const Geometry& g, const std::vector<Seg>& segs, const uint16_t* rank_major,
+                   uint16_t* const* params, std::vector<CallHdr>* hdr, std::vector<const void*>* ptrs) {
+  (void)g;
+  hdr->resize(segs.size());
+  ptrs->assign(segs.size() * 2, nullptr);
+  for (size_t s = 0; s < segs.size(); ++s) {
+    const Seg& sg = segs[s];
+    const uint16_t* src = rank_major + sg.src_off;
+    uint16_t* dst = params[sg.dst_idx] + sg.dst_off;
+    (*ptrs)[2 * s] = src;
+    (*ptrs)[2 * s + 1] = dst;
+    const uintptr_t ps = reinterpret_cast<uintptr_t>(src) & 15, pd = reinterpret_cast<uintptr_t>(dst) & 15;
+    const int32_t head = ps == pd ? int32_t(skip_to(reinterpret_cast<uintptr_t>(src), 2, 16)) : -1;
+    (*hdr)[s] = CallHdr{sg.len, sg.kind, head};
+  }
 }
 
 }  // namespace tide

@@ -1,5 +1,6 @@
-// Private types shared by the host planner (plan.cpp) and the device code
-// (tide.hip) of the layout-aware FSDP2 collective local stages.
+// Private types shared by the host planner (plan.cpp), the C ABI (capi.cpp)
+// and the device code (kernels.hip) of the layout-aware FSDP2 collective local
+// stages.
 #pragma once
 
 #include <cstdint>
@@ -10,25 +11,40 @@
 
 namespace tide {
 
-constexpr int kThreads = 256;              // threads per workgroup (four wave64s)
-constexpr int32_t kDefaultWgPerCu = 8;      // 2048 threads per CU: full occupancy at <= 64 VGPRs
-constexpr int64_t kDefaultChunk = 4096;     // elements per chunk
+constexpr int kThreads = 256;        // threads per workgroup: four wave64s, each an independent worker
+constexpr int kWavesPerGroup = kThreads / 64;
 constexpr int64_t kMaxChunk = int64_t(1) << 30;
+constexpr int32_t kMaxStagedSegs = 16383;  // chunk-index table entries staged in LDS (64 KiB)
+
+// Per-operation defaults, measured on MI355X over the four layer workloads:
+// one workgroup (four waves) per CU keeps the HBM read/write mix most
+// efficient for both kernels; the reduce-scatter prefers small chunks (the
+// grid then sweeps a narrow window of every tensor), the copy-out larger ones.
+constexpr int32_t kRsWgPerCu = 1;
+constexpr int64_t kRsChunk = 1024;
+constexpr int32_t kCoWgPerCu = 1;
+constexpr int64_t kCoChunk = 4096;
 
 enum SegKind : int32_t { kSum = 0, kZero = 1, kCopy = 2 };
+enum Op : int32_t { kOpRs = 0, kOpCo = 1 };
 
-// One contiguous run of work.  Device layout: 48 bytes, naturally aligned.
+// One contiguous run of work, fixed by the plan (host only).
 struct Seg {
-  int64_t src_off;      // element offset into each source tensor
-  int64_t dst_off;      // element offset into the destination tensor
-  int64_t len;          // elements, > 0
-  int64_t chunk_begin;  // index of this segment's first chunk in the plan
-  int32_t src_idx;      // reduce-scatter: parameter p; copy-out: 0
-  int32_t dst_idx;      // reduce-scatter: destination rank r; copy-out: parameter p
-  int32_t kind;         // SegKind
-  int32_t reserved;     // 0
+  int64_t src_off;  // element offset into each source tensor
+  int64_t dst_off;  // element offset into the destination tensor
+  int64_t len;      // elements, > 0
+  int32_t src_idx;  // reduce-scatter: parameter p; copy-out: 0
+  int32_t dst_idx;  // reduce-scatter: destination rank r; copy-out: parameter p
+  int32_t kind;     // SegKind
 };
-static_assert(sizeof(Seg) == 48, "Seg layout");
+
+// Per-call segment header on the device (16 bytes).
+struct CallHdr {
+  int64_t len;   // elements
+  int32_t kind;  // SegKind
+  int32_t head;  // elements before the first aligned vector group; -1: no vector body
+};
+static_assert(sizeof(CallHdr) == 16, "CallHdr layout");
 
 // Shard geometry of "The Endgame of FSDP Communication", Section 2.1, in
 // elements: D_p rows of K_p, R_p = ceil(D_p / W) rows per rank, n_p = R_p K_p,
@@ -40,25 +56,58 @@ struct Geometry {
   int64_t S = 0;
 };
 
-// Builds the geometry; returns TIDE_OK or an error with `why` filled in.
 tide_status build_geometry(int32_t world, int32_t nparams, const int32_t* ndims, const int64_t* dims,
                            Geometry* g, std::string* why);
 
 // Real (non-padding) elements of parameter p in rank r's shard.
 int64_t real_elems(const Geometry& g, int32_t p, int32_t r);
 
-// Segment lists (chunk fields left 0; see assign_chunks).
-//  reduce-scatter: for r, then p: a kSum segment of the real elements and a
-//    kZero segment of the padding elements (each only when non-empty);
-//  copy-out: for r, then p: a kCopy segment of the real elements.
+// Segments are ordered parameter-major (p, then r), so that the chunks the
+// grid works on at any moment read consecutive row blocks of the same W
+// gradient tensors.
+//  reduce-scatter: a kSum segment of the real elements and a kZero segment of
+//    the padding elements of each (p, r) (each only when non-empty);
+//  copy-out: a kCopy segment of the real elements of each (p, r).
 std::vector<Seg> rs_segments(const Geometry& g);
 std::vector<Seg> copyout_segments(const Geometry& g);
 
-// Chunk split for a chunk size: segment s owns chunks [chunk_begin,
-// chunk_begin + ceil(len / chunk)); returns the total number of chunks.
-int64_t assign_chunks(std::vector<Seg>* segs, int64_t chunk);
+// chunk_begin[s] = index of segment s's first chunk, chunk_begin[nseg] = total;
+// segment s owns ceil(len / chunk) chunks.  Fails (TIDE_ERR_RANGE) when the
+// total does not fit in int32.
+tide_status chunk_table(const std::vector<Seg>& segs, int64_t chunk, std::vector<int32_t>* chunk_begin,
+                        std::string* why);
 
-// Resolve defaults and check ranges; returns TIDE_OK or an error with `why`.
-tide_status resolve_options(const tide_options* in, tide_options* out, std::string* why);
+// Options as given (0 = default) -> effective options for one operation.
+tide_status check_options(const tide_options* in, tide_options* out, std::string* why);
+tide_options effective_options(const tide_options& given, Op op, int32_t cu_count);
+
+// Per-call tables.  Vector groups are 4 elements for the reduce-scatter
+// (8-byte bf16 loads, 16-byte fp32 stores) and 8 elements for the copy-out
+// (16-byte loads and stores).  A segment gets a vector body when every source
+// and the destination reach their group alignment at the same element.
+//  reduce-scatter: ptrs per segment = [W source pointers at the segment's
+//    first element, destination pointer]; zero segments have null sources.
+//  copy-out: ptrs per segment = [source, destination].
+void rs_call_table(const Geometry& g, const std::vector<Seg>& segs, const uint16_t* const* grads,
+                   float* const* out, std::vector<CallHdr>* hdr, std::vector<const void*>* ptrs);
+void co_call_table(const Geometry& g, const std::vector<Seg>& segs, const uint16_t* rank_major,
+                   uint16_t* const* params, std::vector<CallHdr>* hdr, std::vector<const void*>* ptrs);
+
+// Device-side launch arguments (kernels.hip).
+struct KernelArgs {
+  const CallHdr* hdr;       // [nseg]
+  const void* const* ptrs;  // [nseg * (nsrc + 1)]
+  const int32_t* chunk_begin;  // [nseg + 1]
+  int32_t nseg;
+  int32_t nsrc;  // W (reduce-scatter) or 1 (copy-out)
+  int32_t nchunks;
+  int32_t chunk;  // elements per chunk
+  uint32_t flags;
+};
+
+// Launch with `grid` workgroups of kThreads on `stream`; returns the launch
+// status (hipError_t as int).
+int launch_rs_local(const KernelArgs& a, int64_t grid, void* stream);
+int launch_ag_copyout(const KernelArgs& a, int64_t grid, void* stream);
 
 }  // namespace tide

@@ -1,0 +1,251 @@
+"""Collect and summarize rocprofv3 measurements of the two kernels.
+
+    python -m param_collectives_amd.profiling trace    --workload W --out DIR
+    python -m param_collectives_amd.profiling counters --workload W --out DIR
+    python -m param_collectives_amd.profiling summarize --workload W --out DIR --profiles profiles/
+
+`trace` runs bench.py under `rocprofv3 --kernel-trace --stats` (one
+process); `counters` runs one `rocprofv3 --pmc` pass per counter group (a
+group never exceeds one hardware block's counter slots) on single-kernel
+launches of bench.py, including a calibration copy of known size;
+`summarize` reads those outputs and writes short text summaries and
+profiles/hbm_traffic.json.
+
+HBM traffic: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by the
+ratio of known bytes to counted bytes for a plain copy of known size (the
+copy-out kernel on one flat tensor), per direction, and the result is tied to
+the SHA-256 of the kernel source, so that a stale figure is never reported.
+rocprofv3 is always started as a child process with the program to profile
+directly after `--`.
+"""
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import shlex
+import sqlite3
+import statistics
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+KERNEL_SOURCE = os.path.join(HERE, "csrc", "kernels.hip")
+KERNEL_REGEX = "rs_local_kernel|ag_copyout_kernel"
+COUNTER_PASSES = {
+    "fetch": ["FETCH_SIZE"],
+    "write": ["WRITE_SIZE"],
+}
+
+
+def _portable(cmd_text, out_root=None):
+    """A recorded command with this checkout's absolute paths replaced by
+    placeholders: <repo> for the repository root, <out> for the output folder."""
+    text = cmd_text
+    if out_root:
+        text = text.replace(out_root, "<out>")
+    text = text.replace(ROOT + "/", "<repo>/").replace(sys.executable, "python")
+    return text
+
+
+def source_digest():
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def _run(cmd, log):
+    print("+", " ".join(shlex.quote(c) for c in cmd), flush=True)
+    env = dict(os.environ, TMPDIR=os.environ.get("TMPDIR", "/tmp"))
+    with open(log, "w") as f:
+        rc = subprocess.run(cmd, stdout=f, stderr=subprocess.STDOUT, cwd="/tmp", env=env, timeout=600).returncode
+    print(f"  exit {rc} (log {log})", flush=True)
+    if rc != 0:
+        raise SystemExit(rc)
+
+
+def bench_cmd(workload, extra):
+    return [sys.executable, os.path.join(ROOT, "bench.py"), "--workload", workload, *extra]
+
+
+def collect_trace(workload, out, steps=10):
+    os.makedirs(out, exist_ok=True)
+    cmd = ["rocprofv3", "--kernel-trace", "--stats", "-f", "csv", "-d", os.path.join(out, "trace"), "-o", "trace",
+           "--", *bench_cmd(workload, ["--steps", str(steps), "--warmup", "2", "--no-cpu-baseline", "--no-sweep"])]
+    _run(cmd, os.path.join(out, "trace.log"))
+    with open(os.path.join(out, "trace.cmd"), "w") as f:
+        f.write(_portable(" ".join(shlex.quote(c) for c in cmd), out) + "\n")
+
+
+def collect_counters(workload, out, launches=3):
+    os.makedirs(out, exist_ok=True)
+    cmds = {}
+    for only in ("rs", "co", "calib"):
+        for name, counters in COUNTER_PASSES.items():
+            d = os.path.join(out, f"pmc_{only}_{name}")
+            cmd = ["rocprofv3", "--pmc", *counters, "--kernel-include-regex", KERNEL_REGEX, "-f", "csv", "-d", d,
+                   "-o", "pmc", "--", *bench_cmd(workload, ["--only", only, "--launches", str(launches)])]
+            _run(cmd, d + ".log")
+            cmds[f"{only}_{name}"] = _portable(" ".join(shlex.quote(c) for c in cmd), out)
+    with open(os.path.join(out, "counters.cmd.json"), "w") as f:
+        json.dump(cmds, f, indent=1)
+
+
+def _normalise(text):
+    """Commands recorded on another machine: keep only repo-relative parts."""
+    import re
+
+    text = re.sub(r"-d \S*/gpurun_out/[^/ ]+/", "-d <out>/", text)
+    text = re.sub(r"\S*/bench\.py", "<repo>/bench.py", text)
+    text = re.sub(r"\S*/python3?(?= )", "python", text)
+    return text
+
+
+def _read_counter(d, counter):
+    """Per-dispatch values of one counter, summed over its instances."""
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    per = {}
+    names = {}
+    for fn in files:
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                key = r["Dispatch_Id"]
+                per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+                names[key] = r["Kernel_Name"]
+    return [(names[k], v) for k, v in sorted(per.items(), key=lambda kv: int(kv[0]))]
+
+
+def _short(name):
+    for k in ("rs_local_kernel", "ag_copyout_kernel"):
+        if k in name:
+            return k
+    return name[:60]
+
+
+def _kernel_stats(out):
+    files = glob.glob(os.path.join(out, "trace", "**", "*kernel_stats.csv"), recursive=True)
+    rows = []
+    for fn in files:
+        with open(fn) as f:
+            rows += list(csv.DictReader(f))
+    if rows:
+        return rows
+    dbs = glob.glob(os.path.join(out, "trace", "**", "*.db"), recursive=True)
+    for db in dbs:
+        con = sqlite3.connect(db)
+        for name, calls, total, avg, pct in con.execute("select name, total_calls, total_duration, average, percentage "
+                                                        "from top_kernels"):
+            rows.append({"Name": name, "Calls": calls, "TotalDurationNs": total, "AverageNs": avg, "Percentage": pct})
+    return rows
+
+
+def summarize(workload, out, profiles):
+    os.makedirs(profiles, exist_ok=True)
+    digest = source_digest()
+    # kernel trace
+    stats = _kernel_stats(out)
+    lines = [f"# rocprofv3 kernel trace: {workload}", ""]
+    try:
+        lines.append("command (run in /tmp): " + _normalise(open(os.path.join(out, "trace.cmd")).read().strip()))
+    except OSError:
+        pass
+    lines.append(f"kernel source sha256: {digest}")
+    lines.append("")
+    lines.append(f"{'kernel':<22} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}")
+    for r in stats:
+        name = _short(r.get("Name", r.get("KernelName", "")))
+        if name not in ("rs_local_kernel", "ag_copyout_kernel"):
+            continue
+        avg = float(r.get("AverageNs", 0)) / 1e3
+        mn = float(r.get("MinNs", 0) or 0) / 1e3
+        mx = float(r.get("MaxNs", 0) or 0) / 1e3
+        lines.append(f"{name:<22} {r.get('Calls', ''):>6} {avg:>10.2f} {mn:>10.2f} {mx:>10.2f} "
+                     f"{float(r.get('Percentage', 0)):>6.1f}")
+    if stats:
+        with open(os.path.join(profiles, f"kernel_trace_{workload}.txt"), "w") as f:
+            f.write("\n".join(lines) + "\n")
+    # counters
+    cdir = out
+    if not os.path.isdir(os.path.join(cdir, "pmc_calib_fetch")):
+        return
+    cmds = {k: _normalise(v) for k, v in json.load(open(os.path.join(cdir, "counters.cmd.json"))).items()}
+
+    def med(only, name, counter, kernel):
+        vals = [v for n, v in _read_counter(os.path.join(cdir, f"pmc_{only}_{name}"), counter) if kernel in n]
+        return statistics.median(vals) if vals else None
+
+    import synth
+
+    w = synth.workload(workload)
+    sum_dk = sum(w.numel(p) for p in range(w.nparams))
+    R = [-(-s[0] // w.world) for s in w.shapes]
+    K = [w.numel(p) // s[0] if s[0] else 0 for p, s in enumerate(w.shapes)]
+    S = sum(r * k for r, k in zip(R, K))
+    calib_bytes = 2 * w.world * S  # the calibration copy moves W*S bf16 each way
+    cf = med("calib", "fetch", "FETCH_SIZE", "ag_copyout")
+    cw = med("calib", "write", "WRITE_SIZE", "ag_copyout")
+    cal = {"kernel": "ag_copyout_kernel on one flat tensor of W*S bf16", "bytes_read": calib_bytes,
+           "bytes_written": calib_bytes, "fetch_kib": cf, "write_kib": cw,
+           "fetch_factor": calib_bytes / (cf * 1024.0), "write_factor": calib_bytes / (cw * 1024.0)}
+    kernels = {}
+    for only, kname, alg_r, alg_w in (("rs", "rs_local", 2 * w.world * sum_dk, 4 * w.world * S),
+                                      ("co", "ag_copyout", 2 * sum_dk, 2 * sum_dk)):
+        f = med(only, "fetch", "FETCH_SIZE", kname)
+        wr = med(only, "write", "WRITE_SIZE", kname)
+        traffic_r = f * 1024.0 * cal["fetch_factor"]
+        traffic_w = wr * 1024.0 * cal["write_factor"]
+        kernels[f"{kname}/{workload}"] = {
+            "fetch_kib": f, "write_kib": wr, "hbm_read_bytes": traffic_r, "hbm_write_bytes": traffic_w,
+            "algorithmic_read_bytes": alg_r, "algorithmic_write_bytes": alg_w,
+            "read_ratio": traffic_r / alg_r, "write_ratio": traffic_w / alg_w}
+    path = os.path.join(profiles, "hbm_traffic.json")
+    try:
+        t = json.load(open(path))
+        if t.get("source_sha256") != digest:
+            t = {}
+    except (OSError, ValueError):
+        t = {}
+    t["source_sha256"] = digest
+    t["calibration"] = cal
+    t.setdefault("kernels", {}).update(kernels)
+    t.setdefault("commands", {})[workload] = cmds
+    with open(path, "w") as fo:
+        json.dump(t, fo, indent=1, sort_keys=True)
+    txt = [f"# HBM traffic per dispatch from rocprofv3 counters: {workload}", "",
+           f"kernel source sha256: {digest}", "",
+           "calibration (plain copy of known size, copy-out kernel on one flat tensor):",
+           f"  {calib_bytes} B each way; FETCH_SIZE {cf:.0f} KiB, WRITE_SIZE {cw:.0f} KiB;"
+           f" factors read {cal['fetch_factor']:.4f}, write {cal['write_factor']:.4f}", ""]
+    for k, v in kernels.items():
+        txt.append(f"{k}: FETCH_SIZE {v['fetch_kib']:.0f} KiB, WRITE_SIZE {v['write_kib']:.0f} KiB -> "
+                   f"read {v['hbm_read_bytes'] / 1e9:.4f} GB ({v['read_ratio']:.3f} x algorithmic), "
+                   f"write {v['hbm_write_bytes'] / 1e9:.4f} GB ({v['write_ratio']:.3f} x algorithmic)")
+    txt += ["", "commands (each run in /tmp; <repo> is the repository root, <out> the output folder):"]
+    txt += [f"  {k}: {c}" for k, c in sorted(cmds.items())]
+    with open(os.path.join(profiles, f"hbm_traffic_{workload}.txt"), "w") as f:
+        f.write("\n".join(txt) + "\n")
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("action", choices=["trace", "counters", "summarize"])
+    ap.add_argument("--workload", default="llama3.1-8b-layer")
+    ap.add_argument("--out", required=True)
+    ap.add_argument("--profiles", default=os.path.join(ROOT, "profiles"))
+    args = ap.parse_args(argv)
+    if ROOT not in sys.path:
+        sys.path.insert(0, ROOT)
+    out = os.path.abspath(args.out)
+    if args.action == "trace":
+        collect_trace(args.workload, out)
+    elif args.action == "counters":
+        collect_counters(args.workload, out)
+    else:
+        summarize(args.workload, out, args.profiles)
+
+
+if __name__ == "__main__":
+    main()

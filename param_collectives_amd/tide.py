@@ -25,8 +25,8 @@ STATUS_NAMES = {
     -5: "TIDE_ERR_HIP",
     -6: "TIDE_ERR_UNSUPPORTED",
 }
-FLAG_NT_LOADS = 0x1
-FLAG_NT_STORES = 0x2
+FLAG_CACHED_LOADS = 0x1
+FLAG_CACHED_STORES = 0x2
 MAX_WORLD = 256
 
 # Every symbol include/tide.h declares.
@@ -65,7 +65,7 @@ def _load():
     lib.tide_plan_layout.argtypes = [vp, i64p, i64p, i64p]
     lib.tide_plan_segments.argtypes = [vp, i32, i64p, i64, i64p]
     lib.tide_plan_set_options.argtypes = [vp, ctypes.POINTER(Options)]
-    lib.tide_plan_get_options.argtypes = [vp, ctypes.POINTER(Options)]
+    lib.tide_plan_get_options.argtypes = [vp, i32, ctypes.POINTER(Options)]
     lib.tide_reduce_scatter_local.argtypes = [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.c_float, i32, vp]
     lib.tide_allgather_copyout.argtypes = [vp, vp, ctypes.POINTER(vp), vp]
     lib.tide_plan_destroy.argtypes = [vp]
@@ -131,9 +131,10 @@ class Plan:
         opt = _options(cu_budget, wg_per_cu, chunk_elems, flags)
         _check(lib.tide_plan_set_options(self.handle, ctypes.byref(opt)))
 
-    def options(self):
+    def options(self, op=0):
+        """Effective launch knobs for op 0 (reduce-scatter) or 1 (copy-out)."""
         opt = Options()
-        _check(lib.tide_plan_get_options(self.handle, ctypes.byref(opt)))
+        _check(lib.tide_plan_get_options(self.handle, int(op), ctypes.byref(opt)))
         return {"cu_budget": opt.cu_budget, "wg_per_cu": opt.wg_per_cu, "chunk_elems": opt.chunk_elems,
                 "flags": opt.flags}
 

@@ -220,8 +220,9 @@ def test_destroyed_plan_is_rejected(tide):
 
 
 def test_options_round_trip_and_validation(tide):
-    plan = tide.Plan(8, [(64, 64)], cu_budget=16, wg_per_cu=2, chunk_elems=1024, flags=tide.FLAG_NT_LOADS)
-    assert plan.options() == {"cu_budget": 16, "wg_per_cu": 2, "chunk_elems": 1024, "flags": 1}
+    plan = tide.Plan(8, [(64, 64)], cu_budget=16, wg_per_cu=2, chunk_elems=1024, flags=tide.FLAG_CACHED_LOADS)
+    assert plan.options(0) == {"cu_budget": 16, "wg_per_cu": 2, "chunk_elems": 1024, "flags": 1}
+    assert plan.options(1) == {"cu_budget": 16, "wg_per_cu": 2, "chunk_elems": 1024, "flags": 1}
     before = plan.segments(0).copy()
     plan.set_options(chunk_elems=8)
     assert plan.options()["chunk_elems"] == 8
@@ -230,3 +231,18 @@ def test_options_round_trip_and_validation(tide):
         plan.set_options(chunk_elems=7)
     with pytest.raises(tide.TideError):
         plan.set_options(wg_per_cu=1000)
+    # zero fields take each operation's default (cu_budget resolves on a device)
+    plan.set_options()
+    assert plan.options(0) == {"cu_budget": 0, "wg_per_cu": 1, "chunk_elems": 1024, "flags": 0}
+    assert plan.options(1) == {"cu_budget": 0, "wg_per_cu": 1, "chunk_elems": 4096, "flags": 0}
+
+
+def test_too_many_chunks_is_a_range_error(tide):
+    with pytest.raises(tide.TideError) as e:
+        tide.Plan(1, [(2**34,)], chunk_elems=8)
+    assert _status(e) == -2
+    plan = tide.Plan(1, [(2**34,)])  # 2^24 chunks of the default size
+    with pytest.raises(tide.TideError) as e:
+        plan.set_options(chunk_elems=8)
+    assert _status(e) == -2
+    assert plan.options(0)["chunk_elems"] == 1024  # unchanged after the failed call
