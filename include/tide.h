@@ -80,7 +80,7 @@ typedef enum {
  *   wg_per_cu   workgroups (256 threads, four waves) per budgeted CU;
  *               default 1.
  *   chunk_elems elements per chunk (the unit a wave takes), a multiple of 8,
- *               at most 2^30; default 1024 (reduce-scatter), 4096 (copy-out).
+ *               at most 2^28; default 1024 (reduce-scatter), 4096 (copy-out).
  *               A plan may have at most 2^31 - 1 chunks per operation.
  *   flags       TIDE_FLAG_* bits.
  */

@@ -146,8 +146,16 @@ __device__ __forceinline__ Chunk chunk_range(const CallHdr& h, int64_t j, int64_
 }
 
 // Wave index in the grid and the wave count.
+// Workgroups are dispatched round robin over the 8 XCDs (workgroup b runs on
+// XCD b mod 8).  When the grid is a multiple of 8, workgroup b is renumbered
+// so that each XCD owns a contiguous eighth of the waves, and hence of every
+// window of chunks: one XCD's L2 and translation caches then see contiguous
+// addresses.  (Measured: 1-3% over the plain numbering on MI355X.)
 __device__ __forceinline__ void wave_slot(int32_t* w, int32_t* nw) {
-  *w = sgpr(int32_t(blockIdx.x) * tide::kWavesPerGroup + int32_t(threadIdx.x >> 6));
+  int32_t b = int32_t(blockIdx.x);
+  const int32_t G = int32_t(gridDim.x);
+  if ((G & 7) == 0) b = (b & 7) * (G >> 3) + (b >> 3);
+  *w = sgpr(b * tide::kWavesPerGroup + int32_t(threadIdx.x >> 6));
   *nw = int32_t(gridDim.x) * tide::kWavesPerGroup;
 }
 
@@ -182,6 +190,11 @@ __device__ __forceinline__ void add4(u32x2 v, float a[4]) {
 // Groups each lane has in flight per step (measured on MI355X: two groups of
 // W 8-byte loads for the reduce-scatter, four 16-byte loads for the copy).
 constexpr int kRsUnroll = 2;
+
+// Buffer-resource word 3 for raw (untyped) byte-addressed buffers on gfx9-class
+// GPUs, and the cache-policy operand bit that marks an access non-temporal.
+constexpr int kRawBuffer = 0x00020000;
+constexpr int kPolicyNT = 2;
 constexpr int kCoUnroll = 4;
 
 template <int WT, bool CL, bool CS>
@@ -197,12 +210,19 @@ __device__ __forceinline__ void sum_body(const uint16_t* const* src, int32_t W, 
     // U groups per lane per step, U*WT independent loads in flight; the
     // remainder of a partial chunk goes one group per lane per step.
     int64_t base = 0;
+    // Source loads go through buffer resources covering exactly this chunk's
+    // body (scalar base, 32-bit lane offsets, hardware range check).
+    __amdgpu_buffer_rsrc_t rs[WT];
+#pragma unroll
+    for (int u = 0; u < WT; ++u)
+      rs[u] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(s[u]), 0, int((vhi - vlo) * 2), kRawBuffer);
     for (; base + 64 * U <= ng; base += 64 * U) {
       u32x2 v[U][WT];
 #pragma unroll
       for (int k = 0; k < U; ++k) {
 #pragma unroll
-        for (int u = 0; u < WT; ++u) v[k][u] = load<u32x2, CL>(s[u] + (base + g + 64 * k) * 4);
+        for (int u = 0; u < WT; ++u)
+          v[k][u] = __builtin_amdgcn_raw_buffer_load_b64(rs[u], int((base + g + 64 * k) * 8), 0, CL ? 0 : kPolicyNT);
       }
 #pragma unroll
       for (int k = 0; k < U; ++k) {

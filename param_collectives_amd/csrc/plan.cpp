@@ -134,7 +134,7 @@ tide_status check_options(const tide_options* in, tide_options* out, std::string
     return TIDE_ERR_INVALID;
   }
   if (o.chunk_elems % 8 != 0 || o.chunk_elems > kMaxChunk) {
-    *why = "chunk_elems must be a multiple of 8 and at most 2^30";
+    *why = "chunk_elems must be a multiple of 8 and at most 2^28";
     return TIDE_ERR_INVALID;
   }
   if (o.wg_per_cu > 64) {

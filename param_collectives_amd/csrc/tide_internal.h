@@ -11,9 +11,9 @@
 
 namespace tide {
 
-constexpr int kThreads = 256;        // threads per workgroup: four wave64s, each an independent worker
+constexpr int kThreads = 256;  // threads per workgroup: four wave64s, each an independent worker
 constexpr int kWavesPerGroup = kThreads / 64;
-constexpr int64_t kMaxChunk = int64_t(1) << 30;
+constexpr int64_t kMaxChunk = int64_t(1) << 28;  // keeps a chunk's byte offsets within 32 bits
 constexpr int32_t kMaxStagedSegs = 16383;  // chunk-index table entries staged in LDS (64 KiB)
 
 // Per-operation defaults, measured on MI355X over the four layer workloads:

@@ -322,3 +322,42 @@ def test_full_size_workload_bit_exact(tide, oracle_mod, name):
     for p in range(w.nparams):
         assert np.array_equal(gpu_util.bf16_bits(params[p]).reshape(w.shapes[p]), want_co[p]), (name, p)
     print(f"[full-size] {name}: copy-out bit-exact", flush=True)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("world,shape", [(1, (2**31 + 1000,)), (2, (2**31 + 3 * 1024 + 5,))])
+def test_offsets_beyond_two_to_the_31(tide, oracle_mod, world, shape):
+    """One tensor of more than 2^31 elements (byte offsets beyond 2^32, a
+    segment longer than 2^31 elements when W = 1, a ragged last rank when
+    W = 2): every output element of both operations."""
+    import torch
+
+    print(f"\n[int64] W={world} shape={shape}", flush=True)
+    plan = tide.Plan(world, [shape])
+    g = torch.Generator(device="cuda")
+    g.manual_seed(31 + world)
+    grads = [[torch.randn(shape, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)]
+             for _ in range(world)]
+    outs = [torch.empty(plan.shard_elems, dtype=torch.float32, device="cuda") for _ in range(world)]
+    tide.reduce_scatter_local(plan, grads, outs)
+    torch.cuda.synchronize()
+    got = [o.cpu().numpy() for o in outs]
+    del outs
+    host = [[gpu_util.bf16_bits(row[0]).reshape(shape)] for row in grads]
+    want = oracle_mod.rs_local(world, [shape], host, nthreads=world)
+    for r in range(world):
+        gpu_util.assert_same_f32(got[r], want[r], f"rank {r}")
+    del got, want
+    # copy-out of the same size: the gradients of rank 0 padded into a rank-major buffer
+    rm = torch.empty(world * plan.shard_elems, dtype=torch.bfloat16, device="cuda")
+    rm.view(torch.int16).fill_(0x7FC1)
+    flat = grads[0][0].reshape(-1)
+    n = plan.shard_elems
+    for r in range(world):
+        lo, hi = r * n, min((r + 1) * n, flat.numel())
+        if hi > lo:
+            rm[r * n:r * n + (hi - lo)] = flat[lo:hi]
+    param = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+    tide.allgather_copyout(plan, rm, [param])
+    torch.cuda.synchronize()
+    assert torch.equal(param.view(torch.int16), grads[0][0].view(torch.int16))

@@ -231,6 +231,9 @@ def test_options_round_trip_and_validation(tide):
         plan.set_options(chunk_elems=7)
     with pytest.raises(tide.TideError):
         plan.set_options(wg_per_cu=1000)
+    with pytest.raises(tide.TideError):
+        plan.set_options(chunk_elems=2**28 + 8)
+    plan.set_options(chunk_elems=2**28)
     # zero fields take each operation's default (cu_budget resolves on a device)
     plan.set_options()
     assert plan.options(0) == {"cu_budget": 0, "wg_per_cu": 1, "chunk_elems": 1024, "flags": 0}
