@@ -9,6 +9,8 @@ shard-layout plan is made once, before timing (it is per-registration work).
 
 Reported (one JSON line): effective HBM GB/s of the step, i.e. algorithmic
 bytes read plus written by both kernels divided by the step time, with
+  * the all-gather copy-in (fp32 master shards -> rank-major bf16, fused
+    cast) timed beside the step, not part of it;
   * per-kernel figures from HIP events recorded on the kernels' own stream;
   * the roofline of the dominant kernel (the reduce-scatter) against MI355X's
     8 TB/s HBM peak, and its measured HBM traffic when a counter summary for
@@ -51,7 +53,7 @@ def parse_args(argv=None):
     ap.add_argument("--flags", type=int, default=0)
     ap.add_argument("--no-sweep", action="store_true", help="skip the CU-budget sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
-    ap.add_argument("--only", choices=["rs", "co", "calib"],
+    ap.add_argument("--only", choices=["rs", "co", "ci", "calib"],
                     help="launch just one kernel --launches times (for counter collection) and exit")
     ap.add_argument("--launches", type=int, default=5)
     return ap.parse_args(argv)
@@ -127,6 +129,17 @@ def main(argv=None):
                 tide.allgather_copyout(cplan, rank_major, [dst], stream=stream)
             stream.synchronize()
             print(json.dumps({"only": "calib", "launches": args.launches, "bytes_read": 2 * n, "bytes_written": 2 * n}))
+        elif args.only == "ci":
+            gen = torch.Generator(device="cuda")
+            gen.manual_seed(synth.device_seed(w.index, 2000))
+            masters = [torch.randn(s, generator=gen, device="cuda", dtype=torch.float32) * w.sigma for s in w.shapes]
+            shards = [[m[min(r * int(R), s[0]):min((r + 1) * int(R), s[0])]
+                       for m, s, R in zip(masters, w.shapes, plan.rows_per_rank)] for r in range(W)]
+            for _ in range(args.launches):
+                tide.allgather_copyin(plan, shards, rank_major, stream=stream)
+            stream.synchronize()
+            print(json.dumps({"only": "ci", "workload": w.name, "launches": args.launches,
+                              "bytes": 4 * sum_dk + 2 * W * S}))
         else:
             fn = rs if args.only == "rs" else co
             for _ in range(args.launches):
@@ -192,6 +205,26 @@ def main(argv=None):
                              "gbps_per_cu": round(nbytes / avg / 1e6 / budget, 2)}
             sweep.append(row)
         plan.set_options(**opts)
+
+    # the all-gather copy-in (fp32 master shards of every rank -> rank-major
+    # bf16, cast fused), measured beside the step: 4*sum(D*K) read, 2*W*S written
+    ci_bytes = 4 * sum_dk + 2 * W * S
+    with torch.cuda.stream(stream):
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(synth.device_seed(w.index, 2000))
+        masters = [torch.randn(s, generator=gen, device="cuda", dtype=torch.float32) * w.sigma for s in w.shapes]
+        shards = [[m[min(r * int(R), s[0]):min((r + 1) * int(R), s[0])]
+                   for m, s, R in zip(masters, w.shapes, plan.rows_per_rank)] for r in range(W)]
+        ci_out = torch.empty(W * S, dtype=torch.bfloat16, device="cuda")
+        tide.allgather_copyin(plan, shards, ci_out, stream=stream)
+        e = [(ev(), ev()) for _ in range(10)]
+        for a, b_ in e:
+            a.record(stream)
+            tide.allgather_copyin(plan, shards, ci_out, stream=stream)
+            b_.record(stream)
+    stream.synchronize()
+    kernels["ag_copyin_f32"] = kstats([a.elapsed_time(b_) for a, b_ in e], ci_bytes)
+    del masters, shards, ci_out
 
     # plain device-to-device copy of the copy-out's byte count (context)
     with torch.cuda.stream(stream):

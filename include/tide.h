@@ -2,7 +2,7 @@
  * tide.h -- C ABI of the layout-aware FSDP2 collective local stages on one
  * MI355X (gfx950) GPU.
  *
- * Two operations, after "The Endgame of FSDP Communication: Layout-Aware
+ * Three operations, after "The Endgame of FSDP Communication: Layout-Aware
  * Collectives on Copy Engines, RDMA, and NVSwitch" (Wang et al.):
  *
  *   reduce-scatter local stage (Section 4, Equation 5; Section 4.1): W ranks'
@@ -13,6 +13,10 @@
  *
  *   all-gather copy-out (Section 2.1): a flat rank-major bf16 buffer is
  *     scattered into per-parameter tensors.
+ *
+ *   all-gather copy-in (Section 2.1, with the cast of Section 3.1): every
+ *     rank's local fp32 (or bf16) shards are packed into the rank-major bf16
+ *     buffer the all-gather would produce; the inverse of the copy-out.
  *
  * Shard geometry (Section 2.1), in ELEMENTS.  Parameter p has shape
  * (d_0, ..., d_{m-1}), m >= 1, viewed as D_p = d_0 rows of K_p = d_1*...*d_{m-1}
@@ -61,6 +65,10 @@ typedef enum {
     TIDE_ERR_UNSUPPORTED = -6  /* alpha != 1 or accumulate != 0: not provided */
 } tide_status;
 
+/* Element types of the copy-in's shards. */
+#define TIDE_DTYPE_BF16 0
+#define TIDE_DTYPE_F32 1
+
 /* Largest number of simulated ranks a plan may have. */
 #define TIDE_MAX_WORLD 256
 
@@ -80,7 +88,8 @@ typedef enum {
  *   wg_per_cu   workgroups (256 threads, four waves) per budgeted CU;
  *               default 1.
  *   chunk_elems elements per chunk (the unit a wave takes), a multiple of 8,
- *               at most 2^28; default 1024 (reduce-scatter), 4096 (copy-out).
+ *               at most 2^28; default 1024 (reduce-scatter), 4096 (copy-out
+ *               and copy-in).
  *               A plan may have at most 2^31 - 1 chunks per operation.
  *   flags       TIDE_FLAG_* bits.
  */
@@ -124,14 +133,17 @@ tide_status tide_plan_layout(const tide_plan* plan, int64_t* rows_per_rank, int6
 
 /*
  * The plan's work segments, for inspection and tests.  op 0 = reduce-scatter,
- * 1 = copy-out.  Each segment is 6 int64 values:
+ * 1 = copy-out, 2 = copy-in.  Each segment is 6 int64 values:
  *   kind     0 = sum of the W ranks' sources, 1 = zero fill (padding),
- *            2 = copy
- *   src_idx  reduce-scatter: parameter p; copy-out: 0 (the rank-major buffer)
- *   dst_idx  reduce-scatter: destination rank r; copy-out: parameter p
+ *            2 = copy (the copy-in casts instead when its shards are fp32)
+ *   src_idx  reduce-scatter: parameter p; copy-out: 0 (the rank-major buffer);
+ *            copy-in: shard index r*P + p
+ *   dst_idx  reduce-scatter: destination rank r; copy-out: parameter p;
+ *            copy-in: 0 (the rank-major buffer)
  *   src_off  element offset in each source tensor (in the rank-major buffer
  *            for the copy-out)
- *   dst_off  element offset in the destination tensor
+ *   dst_off  element offset in the destination tensor (in the rank-major
+ *            buffer for the copy-in)
  *   len      elements (> 0)
  * Writes min(capacity, count) segments to `table` (may be NULL when
  * capacity is 0) and the total count to *count.
@@ -143,7 +155,7 @@ tide_status tide_plan_segments(const tide_plan* plan, int32_t op, int64_t* table
  * Errors: TIDE_ERR_INVALID, TIDE_ERR_RANGE (too many chunks). */
 tide_status tide_plan_set_options(tide_plan* plan, const tide_options* opt);
 
-/* The launch knobs in effect for op 0 (reduce-scatter) or 1 (copy-out), with
+/* The launch knobs in effect for op 0 (reduce-scatter), 1 (copy-out) or 2 (copy-in), with
  * defaults resolved (cu_budget is resolved once the plan is bound to a
  * device, 0 before). */
 tide_status tide_plan_get_options(const tide_plan* plan, int32_t op, tide_options* out);
@@ -186,6 +198,25 @@ tide_status tide_reduce_scatter_local(tide_plan* plan, const uint16_t* const* gr
  */
 tide_status tide_allgather_copyout(tide_plan* plan, const uint16_t* rank_major, uint16_t* const* params,
                                    void* stream);
+
+/*
+ * All-gather copy-in (Section 2.1; the mixed-precision cast of Section 3.1):
+ * every rank's local shards are packed into the rank-major buffer the
+ * all-gather produces.
+ *   shards       [W*P] host array of device pointers; shards[r*P + p] is rank
+ *                r's local shard of parameter p: its n_real(p, r) elements
+ *                (rows [r R_p, r R_p + n_real/K_p) of the parameter, row-major),
+ *                aligned to the element size.  May be NULL where n_real = 0.
+ *   shard_dtype  TIDE_DTYPE_F32: fp32 shards, cast to bf16 by round to
+ *                nearest even (a NaN stays a quiet NaN of the same sign with
+ *                its top payload bits); TIDE_DTYPE_BF16: bf16 shards, copied.
+ *   rank_major   device pointer to W*S bf16 elements, 2-byte aligned, written
+ *                in full: rank r's shard of p at r*S + o_p, bf16 +0 (0x0000)
+ *                in the padding of each slot.
+ * Errors: TIDE_ERR_INVALID, TIDE_ERR_ALIGN, TIDE_ERR_NOMEM, TIDE_ERR_HIP.
+ */
+tide_status tide_allgather_copyin(tide_plan* plan, const void* const* shards, int32_t shard_dtype,
+                                  uint16_t* rank_major, void* stream);
 
 /* Free a plan and its device tables (waits for the device to finish using
  * them).  NULL is accepted. */

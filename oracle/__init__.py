@@ -12,7 +12,10 @@ Collectives on Copy Engines, RDMA, and NVSwitch", Wang et al.):
                     in rank order 0..W-1 in binary32 (Section 4.3);
   * ``copyout``  -- Section 2.1, rank-major all-gather output to per-parameter
                     storage;
-  * ``pack``     -- Section 2.1, the inverse (FSDP2's copy-in), padding zero.
+  * ``pack``     -- Section 2.1, the inverse (FSDP2's copy-in), padding zero;
+  * ``copyin``   -- Sections 2.1 and 3.1: every rank's local shards (fp32 cast
+                    to bf16 by round to nearest even, or bf16 as is) into the
+                    rank-major buffer, padding zero.
 
 bf16 values are carried as ``numpy.uint16`` bit patterns throughout.
 """
@@ -40,6 +43,10 @@ def _bind(lib):
     lib.oracle_copyout.restype = ctypes.c_int
     lib.oracle_pack.argtypes = [i32, i32, i32p, i64p, vpp, ctypes.c_void_p, i32]
     lib.oracle_pack.restype = ctypes.c_int
+    lib.oracle_copyin.argtypes = [i32, i32, i32p, i64p, vpp, i32, ctypes.c_void_p, i32]
+    lib.oracle_copyin.restype = ctypes.c_int
+    lib.oracle_cast_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    lib.oracle_cast_bf16.restype = ctypes.c_int
     return lib
 
 
@@ -149,6 +156,40 @@ class Oracle:
         return rm[: world * geo["S"]]
 
 
+    def copyin(self, world, shapes, shards, nthreads=1):
+        """shards[r][p]: rank r's local shard of parameter p, n_real(p, r)
+        elements, all float32 (cast) or all uint16 bf16 bits (copied).
+        Returns the rank-major buffer (W*S uint16)."""
+        geo = self.plan(world, shapes)
+        P = len(shapes)
+        if len(shards) != world or any(len(s) != P for s in shards):
+            raise ValueError("shards must be indexed [rank][parameter]")
+        dtypes = {np.asarray(a).dtype for row in shards for a in row}
+        if dtypes not in ({np.dtype(np.float32)}, {np.dtype(np.uint16)}):
+            raise TypeError(f"shards must be all float32 or all uint16, got {dtypes}")
+        f32 = dtypes == {np.dtype(np.float32)}
+        flat = []
+        for r in range(world):
+            for p in range(P):
+                a = np.ascontiguousarray(shards[r][p]).reshape(-1)
+                if a.size != geo["n_real"][p, r]:
+                    raise ValueError(f"shards[{r}][{p}]: expected {geo['n_real'][p, r]} elements, got {a.size}")
+                flat.append(a if a.size else np.zeros(1, dtype=a.dtype))
+        rm = np.empty(max(world * geo["S"], 1), dtype=np.uint16)
+        ndims, dims = _shape_args(shapes)
+        rc = self.lib.oracle_copyin(world, P, _i32p(ndims), _i64p(dims), _ptrs(flat), 1 if f32 else 0,
+                                    rm.ctypes.data, int(nthreads))
+        _check(rc, "oracle_copyin")
+        return rm[: world * geo["S"]]
+
+    def cast_bf16(self, x):
+        """float32 array -> bf16 bits (uint16), the copy-in's cast."""
+        x = np.ascontiguousarray(x, dtype=np.float32).reshape(-1)
+        out = np.empty(max(x.size, 1), dtype=np.uint16)
+        _check(self.lib.oracle_cast_bf16(x.ctypes.data, x.size, out.ctypes.data), "oracle_cast_bf16")
+        return out[: x.size]
+
+
 _default = None
 
 
@@ -173,3 +214,11 @@ def copyout(world, shapes, rank_major, nthreads=1):
 
 def pack(world, shapes, params, nthreads=1):
     return _get().pack(world, shapes, params, nthreads)
+
+
+def copyin(world, shapes, shards, nthreads=1):
+    return _get().copyin(world, shapes, shards, nthreads)
+
+
+def cast_bf16(x):
+    return _get().cast_bf16(x)

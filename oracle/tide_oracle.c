@@ -1,6 +1,6 @@
 /*
- * CPU oracle for the layout-aware FSDP2 reduce-scatter local stage and the
- * all-gather copy-out.
+ * CPU oracle for the layout-aware FSDP2 reduce-scatter local stage, the
+ * all-gather copy-out and the all-gather copy-in.
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may include, link,
  * load or call this file.  Only the test suite, the package's smoke check and
@@ -15,7 +15,9 @@
  *       landing offset (Equation 2) and the rows each destination owns;
  *     - Section 4 "TIDE-RS": the reduce-scatter result (Equation 5);
  *     - Section 4.3 "Numerical Semantics and Determinism": fp32 accumulation
- *       that never narrows a partial.
+ *       that never narrows a partial;
+ *     - Section 3.1 "In-Place Shards and Paced Doubling": mixed-precision
+ *       groups cast their fp32 shards to bf16 on the way into the all-gather.
  *
  * Readings taken where the pages leave a step open (each is also listed with
  * the design notes of this repository):
@@ -30,6 +32,10 @@
  *   - output elements of padding rows (rows at or past D_p) are +0.0f;
  *   - the copy-out writes the unpadded per-parameter tensor of D_p * K_p
  *     elements and never reads the padding of a shard;
+ *   - the copy-in takes each rank's local shard as its n_real(p, r) elements
+ *     (unpadded rows), casts fp32 to bf16 by round to nearest even (a NaN
+ *     stays a quiet NaN of the same sign and top payload bits), and writes
+ *     bf16 +0 into the padding;
  *   - a parameter must have at least one dimension; a 1-D parameter has
  *     K_p = 1; zero-sized dimensions are allowed.
  *
@@ -216,6 +222,8 @@ static void ieee_mode_leave(unsigned saved) { _mm_setcsr(saved); }
  * ------------------------------------------------------------------------ */
 typedef struct {
     const geometry* g;
+    const void* const* shards;    /* [W*P], index r*P + p */
+    int32_t shard_dtype;          /* 0 = bf16 bits, 1 = fp32 */
     const uint16_t* const* grads; /* [W*P], index u*P + p */
     float* const* out;            /* [W] */
     const uint16_t* rank_major;   /* [W*S] */
@@ -257,6 +265,40 @@ static void copyout_task(const job* j, int32_t r, int32_t p) {
     const uint16_t* src = j->rank_major + (int64_t)r * g->S + g->o[p];
     uint16_t* dst = j->params[p] + (int64_t)r * g->R[p] * g->K[p];
     for (int64_t e = 0; e < real; ++e) dst[e] = src[e];
+}
+
+/* fp32 -> bf16, round to nearest, ties to even, done on the bit pattern:
+ * add half of the dropped 16-bit tail (minus one unless the kept part is
+ * odd) and truncate; overflow carries into the exponent and gives +-inf.
+ * A NaN stays a NaN of the same sign with its top payload bits and the quiet
+ * bit set. */
+static uint16_t f32_to_bf16_rne(float f) {
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x0040u);
+    uint32_t keep_odd = (u >> 16) & 1u;
+    return (uint16_t)((u + 0x7FFFu + keep_odd) >> 16);
+}
+
+/* All-gather copy-in, one task: rank r's local shard of parameter p (its
+ * n_real(p, r) elements, fp32 master weights cast to bf16, or bf16 as is) is
+ * written into the rank-major buffer at r S + o_p, the padding of the slot as
+ * bf16 +0.  (FSDP2's copy-in, Section 2.1; the cast is the mixed-precision
+ * one of Section 3.1.) */
+static void copyin_task(const job* j, int32_t r, int32_t p) {
+    const geometry* g = j->g;
+    int64_t real = real_rows(g, p, r) * g->K[p];
+    uint16_t* dst = j->rank_major_out + (int64_t)r * g->S + g->o[p];
+    const void* src = j->shards[(int64_t)r * g->P + p];
+    for (int64_t e = 0; e < g->n[p]; ++e) {
+        if (e >= real) {
+            dst[e] = 0;
+        } else if (j->shard_dtype == 1) {
+            dst[e] = f32_to_bf16_rne(((const float*)src)[e]);
+        } else {
+            dst[e] = ((const uint16_t*)src)[e];
+        }
+    }
 }
 
 /* Pack (the inverse of the copy-out; FSDP2's all-gather copy-in): rank r's
@@ -396,4 +438,41 @@ int oracle_pack(int32_t W, int32_t P, const int32_t* ndims, const int64_t* dims,
     rc = run_tasks(j, pack_task, nthreads);
     geometry_free(&g);
     return rc;
+}
+
+/*
+ * oracle_copyin: every rank's all-gather copy-in, giving the rank-major buffer
+ * the all-gather would produce.
+ *   shards       [W*P]  shards[r*P + p] is rank r's local shard of parameter p:
+ *                       n_real(p, r) elements (its rows of the parameter)
+ *   shard_dtype  0 = bf16 bit patterns (copied), 1 = fp32 (cast to bf16)
+ *   rank_major   [W*S]  written in full
+ */
+int oracle_copyin(int32_t W, int32_t P, const int32_t* ndims, const int64_t* dims, const void* const* shards,
+                  int32_t shard_dtype, uint16_t* rank_major, int32_t nthreads) {
+    geometry g;
+    int rc = geometry_build(W, P, ndims, dims, &g);
+    if (rc != ORACLE_OK) return rc;
+    if (rank_major == NULL || shards == NULL || (shard_dtype != 0 && shard_dtype != 1)) {
+        geometry_free(&g);
+        return ORACLE_INVALID;
+    }
+    job j;
+    memset(&j, 0, sizeof j);
+    j.g = &g;
+    j.shards = shards;
+    j.shard_dtype = shard_dtype;
+    j.rank_major_out = rank_major;
+    rc = run_tasks(j, copyin_task, nthreads);
+    geometry_free(&g);
+    return rc;
+}
+
+/* oracle_cast_bf16: the element cast on its own (n values), for pinning. */
+int oracle_cast_bf16(const float* x, int64_t n, uint16_t* out) {
+    if ((x == NULL || out == NULL) && n > 0) return ORACLE_INVALID;
+    unsigned saved = ieee_mode_enter();
+    for (int64_t i = 0; i < n; ++i) out[i] = f32_to_bf16_rne(x[i]);
+    ieee_mode_leave(saved);
+    return ORACLE_OK;
 }

@@ -3,6 +3,7 @@
   Plan                   host shard-layout plan (dimension-0 shards, padding)
   reduce_scatter_local   W ranks' bf16 gradients -> W packed fp32 shards
   allgather_copyout      rank-major bf16 buffer -> per-parameter tensors
+  allgather_copyin       every rank's fp32/bf16 shards -> rank-major bf16 buffer
 
 The work runs in the HIP library libtide.so (include/tide.h); importing this
 package fails if that library has not been built.
@@ -12,7 +13,10 @@ from .tide import (  # noqa: F401
     FLAG_CACHED_STORES,
     MAX_WORLD,
     Plan,
+    DTYPE_BF16,
+    DTYPE_F32,
     TideError,
+    allgather_copyin,
     allgather_copyout,
     reduce_scatter_local,
 )

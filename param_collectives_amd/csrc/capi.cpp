@@ -70,7 +70,7 @@ struct tide_plan {
   uint64_t magic = 0;
   tide::Geometry geo;
   tide_options given{};  // as passed (0 = default)
-  OpState rs, co;
+  OpState rs, co, ci;
   int device = -1;
   int cu_count = 0;
 };
@@ -89,17 +89,21 @@ bool live(const tide_plan* p) {
 
 int32_t nsrc_of(const tide_plan* p, tide::Op op) { return op == tide::kOpRs ? p->geo.world : 1; }
 
+OpState& op_state(tide_plan* p, tide::Op op) { return op == tide::kOpRs ? p->rs : op == tide::kOpCo ? p->co : p->ci; }
+
 tide_status rebuild_chunks(tide_plan* p, const tide_options& given) {
   std::string why;
-  std::vector<int32_t> rs_cb, co_cb;
-  const tide_options rs_opt = tide::effective_options(given, tide::kOpRs, 0);
-  const tide_options co_opt = tide::effective_options(given, tide::kOpCo, 0);
-  tide_status st = tide::chunk_table(p->rs.segs, rs_opt.chunk_elems, &rs_cb, &why);
-  if (st == TIDE_OK) st = tide::chunk_table(p->co.segs, co_opt.chunk_elems, &co_cb, &why);
-  if (st != TIDE_OK) return fail(st, why);
-  p->rs.chunk_begin.swap(rs_cb);
-  p->co.chunk_begin.swap(co_cb);
-  p->rs.chunks_stale = p->co.chunks_stale = true;
+  std::vector<int32_t> cb[3];
+  const tide::Op ops[3] = {tide::kOpRs, tide::kOpCo, tide::kOpCi};
+  for (int i = 0; i < 3; ++i) {
+    const tide_options eff = tide::effective_options(given, ops[i], 0);
+    tide_status st = tide::chunk_table(op_state(p, ops[i]).segs, eff.chunk_elems, &cb[i], &why);
+    if (st != TIDE_OK) return fail(st, why);
+  }
+  for (int i = 0; i < 3; ++i) {
+    op_state(p, ops[i]).chunk_begin.swap(cb[i]);
+    op_state(p, ops[i]).chunks_stale = true;
+  }
   return TIDE_OK;
 }
 
@@ -171,6 +175,7 @@ void release_device(tide_plan* p) {
   (void)hipSetDevice(p->device);
   release_op(&p->rs);
   release_op(&p->co);
+  release_op(&p->ci);
   p->device = -1;
   if (prev >= 0) (void)hipSetDevice(prev);
 }
@@ -203,6 +208,7 @@ tide_status bind_device(tide_plan* p) {
   p->cu_count = cus;
   tide_status st = alloc_op(&p->rs, p->geo.world);
   if (st == TIDE_OK) st = alloc_op(&p->co, 1);
+  if (st == TIDE_OK) st = alloc_op(&p->ci, 1);
   if (st != TIDE_OK) {
     const std::string why = g_last_error;
     release_device(p);
@@ -214,8 +220,8 @@ tide_status bind_device(tide_plan* p) {
 // Upload what is stale, then launch.
 template <typename BuildCall>
 tide_status run_op(tide_plan* p, tide::Op op, const std::vector<const void*>& key, BuildCall build,
-                   hipStream_t stream) {
-  OpState& s = op == tide::kOpRs ? p->rs : p->co;
+                   hipStream_t stream, bool f32 = false) {
+  OpState& s = op_state(p, op);
   const int32_t nchunks = s.chunk_begin.back();
   if (nchunks == 0) return TIDE_OK;  // nothing to write
   tide_status st = bind_device(p);
@@ -253,9 +259,13 @@ tide_status run_op(tide_plan* p, tide::Op op, const std::vector<const void*>& ke
   a.nchunks = nchunks;
   a.chunk = int32_t(eff.chunk_elems);
   a.flags = eff.flags;
-  const int rc = op == tide::kOpRs ? tide::launch_rs_local(a, grid, stream) : tide::launch_ag_copyout(a, grid, stream);
+  const int rc = op == tide::kOpRs   ? tide::launch_rs_local(a, grid, stream)
+                 : op == tide::kOpCo ? tide::launch_ag_copyout(a, grid, stream)
+                                     : tide::launch_ag_copyin(a, f32, grid, stream);
   if (rc != 0)
-    return hip_fail(hipError_t(rc), op == tide::kOpRs ? "rs_local_kernel launch" : "ag_copyout_kernel launch");
+    return hip_fail(hipError_t(rc), op == tide::kOpRs   ? "rs_local_kernel launch"
+                                    : op == tide::kOpCo ? "ag_copyout_kernel launch"
+                                                        : "ag_copyin_kernel launch");
   return TIDE_OK;
 }
 
@@ -282,11 +292,13 @@ tide_status tide_plan_create(int32_t world, int32_t nparams, const int32_t* ndim
   try {
     p->rs.segs = tide::rs_segments(p->geo);
     p->co.segs = tide::copyout_segments(p->geo);
+    p->ci.segs = tide::copyin_segments(p->geo);
   } catch (...) {
     delete p;
     return fail(TIDE_ERR_NOMEM, "out of host memory");
   }
-  if (p->rs.segs.size() >= size_t(INT32_MAX) || p->co.segs.size() >= size_t(INT32_MAX)) {
+  if (p->rs.segs.size() >= size_t(INT32_MAX) || p->co.segs.size() >= size_t(INT32_MAX) ||
+      p->ci.segs.size() >= size_t(INT32_MAX)) {
     delete p;
     return fail(TIDE_ERR_RANGE, "too many segments");
   }
@@ -322,10 +334,10 @@ tide_status tide_plan_segments(const tide_plan* plan, int32_t op, int64_t* table
                                int64_t* count) {
   g_last_error.clear();
   if (!live(plan)) return fail(TIDE_ERR_INVALID, "unknown or destroyed plan");
-  if (op != 0 && op != 1) return fail(TIDE_ERR_INVALID, "op must be 0 (reduce-scatter) or 1 (copy-out)");
+  if (op < 0 || op > 2) return fail(TIDE_ERR_INVALID, "op must be 0 (reduce-scatter), 1 (copy-out) or 2 (copy-in)");
   if (count == nullptr || capacity < 0 || (capacity > 0 && table == nullptr))
     return fail(TIDE_ERR_INVALID, "bad table/capacity/count");
-  const std::vector<tide::Seg>& segs = op == 0 ? plan->rs.segs : plan->co.segs;
+  const std::vector<tide::Seg>& segs = op == 0 ? plan->rs.segs : op == 1 ? plan->co.segs : plan->ci.segs;
   *count = int64_t(segs.size());
   const int64_t n = capacity < *count ? capacity : *count;
   for (int64_t i = 0; i < n; ++i) {
@@ -357,9 +369,9 @@ tide_status tide_plan_set_options(tide_plan* plan, const tide_options* opt) {
 tide_status tide_plan_get_options(const tide_plan* plan, int32_t op, tide_options* out) {
   g_last_error.clear();
   if (!live(plan)) return fail(TIDE_ERR_INVALID, "unknown or destroyed plan");
-  if (op != 0 && op != 1) return fail(TIDE_ERR_INVALID, "op must be 0 (reduce-scatter) or 1 (copy-out)");
+  if (op < 0 || op > 2) return fail(TIDE_ERR_INVALID, "op must be 0 (reduce-scatter), 1 (copy-out) or 2 (copy-in)");
   if (out == nullptr) return fail(TIDE_ERR_INVALID, "out must not be NULL");
-  *out = tide::effective_options(plan->given, op == 0 ? tide::kOpRs : tide::kOpCo, plan->cu_count);
+  *out = tide::effective_options(plan->given, tide::Op(op), plan->cu_count);
   return TIDE_OK;
 }
 
@@ -421,6 +433,40 @@ tide_status tide_allgather_copyout(tide_plan* plan, const uint16_t* rank_major, 
         tide::co_call_table(g, plan->co.segs, rank_major, params, hdr, ptrs);
       },
       static_cast<hipStream_t>(stream));
+}
+
+tide_status tide_allgather_copyin(tide_plan* plan, const void* const* shards, int32_t shard_dtype,
+                                  uint16_t* rank_major, void* stream) {
+  g_last_error.clear();
+  if (!live(plan)) return fail(TIDE_ERR_INVALID, "unknown or destroyed plan");
+  if (shards == nullptr) return fail(TIDE_ERR_INVALID, "shards must not be NULL");
+  if (shard_dtype != TIDE_DTYPE_BF16 && shard_dtype != TIDE_DTYPE_F32)
+    return fail(TIDE_ERR_INVALID, "shard_dtype must be TIDE_DTYPE_BF16 or TIDE_DTYPE_F32");
+  const tide::Geometry& g = plan->geo;
+  const int64_t W = g.world, P = g.nparams;
+  const uintptr_t align = shard_dtype == TIDE_DTYPE_F32 ? 4 : 2;
+  for (int64_t r = 0; r < W; ++r) {
+    for (int64_t p = 0; p < P; ++p) {
+      if (tide::real_elems(g, int32_t(p), int32_t(r)) == 0) continue;
+      const void* s = shards[r * P + p];
+      if (s == nullptr) return fail(TIDE_ERR_INVALID, "shards[" + std::to_string(r * P + p) + "] is NULL");
+      if (reinterpret_cast<uintptr_t>(s) & (align - 1))
+        return fail(TIDE_ERR_ALIGN, "shards[" + std::to_string(r * P + p) + "] is not aligned to its element size");
+    }
+  }
+  if (plan->ci.chunk_begin.back() == 0) return TIDE_OK;  // nothing to write
+  if (rank_major == nullptr) return fail(TIDE_ERR_INVALID, "rank_major must not be NULL");
+  if (reinterpret_cast<uintptr_t>(rank_major) & 1) return fail(TIDE_ERR_ALIGN, "rank_major is not 2-byte aligned");
+  const bool f32 = shard_dtype == TIDE_DTYPE_F32;
+  std::vector<const void*> key(shards, shards + W * P);
+  key.push_back(rank_major);
+  key.push_back(reinterpret_cast<const void*>(uintptr_t(shard_dtype)));
+  return run_op(
+      plan, tide::kOpCi, key,
+      [&](std::vector<tide::CallHdr>* hdr, std::vector<const void*>* ptrs) {
+        tide::ci_call_table(g, plan->ci.segs, shards, f32, rank_major, hdr, ptrs);
+      },
+      static_cast<hipStream_t>(stream), f32);
 }
 
 void tide_plan_destroy(tide_plan* plan) {

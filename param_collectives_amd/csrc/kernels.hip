@@ -8,6 +8,9 @@
 //                      order in fp32 (Section 4.3), padding rows written +0.
 //   ag_copyout_kernel  all-gather copy-out (Section 2.1): rank-major bf16
 //                      buffer -> per-parameter tensors.
+//   ag_copyin_kernel   all-gather copy-in (Sections 2.1, 3.1): every rank's
+//                      local shards (fp32 cast to bf16, or bf16) -> the
+//                      rank-major bf16 buffer, padding +0.
 //
 // Both are HBM-bandwidth bound: no MFMA, no atomics, no communication between
 // waves.  Structure (shared):
@@ -344,7 +347,7 @@ __global__ __launch_bounds__(tide::kThreads) void rs_local_kernel(const CallHdr*
 struct CoDesc {
   CallHdr h;
   int32_t j, nch;
-  const uint16_t* src;
+  const void* src;
   uint16_t* dst;
 };
 
@@ -355,8 +358,28 @@ __device__ __forceinline__ void co_fetch(const Tables& a, const int32_t* cb, int
   d->j = c - first;
   d->nch = sgpr(cb[s + 1]) - first;
   d->h = a.hdr[s];
-  d->src = static_cast<const uint16_t*>(a.ptrs[2 * int64_t(s)]);
+  d->src = a.ptrs[2 * int64_t(s)];
   d->dst = static_cast<uint16_t*>(const_cast<void*>(a.ptrs[2 * int64_t(s) + 1]));
+}
+
+// bf16 words of [vlo, vhi) (groups of 8, both sides 16-byte aligned).
+template <bool CL, bool CS>
+__device__ __forceinline__ void copy_body(const uint16_t* src, uint16_t* dst, int64_t vlo, int64_t vhi) {
+  const int lane = lane_id();
+  const uint16_t* sv = src + vlo;
+  uint16_t* dv = dst + vlo;
+  const int64_t ng = (vhi - vlo) >> 3;
+  constexpr int U = kCoUnroll;
+  // U 16-byte loads in flight per lane; then one group per lane per step.
+  int64_t base = 0;
+  for (; base + 64 * U <= ng; base += 64 * U) {
+    u32x4 v[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) v[k] = load<u32x4, CL>(sv + (base + lane + 64 * k) * 8);
+#pragma unroll
+    for (int k = 0; k < U; ++k) store<u32x4, CS>(dv + (base + lane + 64 * k) * 8, v[k]);
+  }
+  for (int64_t gk = base + lane; gk < ng; gk += 64) store<u32x4, CS>(dv + gk * 8, load<u32x4, CL>(sv + gk * 8));
 }
 
 template <bool CL, bool CS, bool STAGED>
@@ -378,23 +401,87 @@ __global__ __launch_bounds__(tide::kThreads) void ag_copyout_kernel(const CallHd
     const int32_t cn = c + nw;
     if (cn < a.nchunks) co_fetch(a, cb, &cur, cn, &next);
     const Chunk r = chunk_range(d.h, d.j, d.nch, a.chunk, 8);
-    for (int64_t e = r.lo + lane; e < r.vlo; e += 64) store2(d.dst + e, load2(d.src + e));
-    for (int64_t e = r.vhi + lane; e < r.hi; e += 64) store2(d.dst + e, load2(d.src + e));
-    if (r.vhi > r.vlo) {
-      const uint16_t* sv = d.src + r.vlo;
-      uint16_t* dv = d.dst + r.vlo;
-      const int64_t ng = (r.vhi - r.vlo) >> 3;
-      constexpr int U = kCoUnroll;
-      // U 16-byte loads in flight per lane; then one group per lane per step.
-      int64_t base = 0;
-      for (; base + 64 * U <= ng; base += 64 * U) {
-        u32x4 v[U];
+    const uint16_t* src = static_cast<const uint16_t*>(d.src);
+    for (int64_t e = r.lo + lane; e < r.vlo; e += 64) store2(d.dst + e, load2(src + e));
+    for (int64_t e = r.vhi + lane; e < r.hi; e += 64) store2(d.dst + e, load2(src + e));
+    if (r.vhi > r.vlo) copy_body<CL, CS>(src, d.dst, r.vlo, r.vhi);
+    c = cn;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// All-gather copy-in
+// ---------------------------------------------------------------------------
+
+// fp32 -> bf16, round to nearest even, on the bit pattern; a NaN stays a NaN
+// of the same sign with its top payload bits and the quiet bit set.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x0040u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ u32x2 cast4(f32x4 v) {
+  return u32x2{f32_to_bf16(v.x) | (f32_to_bf16(v.y) << 16), f32_to_bf16(v.z) | (f32_to_bf16(v.w) << 16)};
+}
+
+// fp32 [vlo, vhi) -> bf16 (groups of 4: 16-byte loads, 8-byte stores, each
+// contiguous across the wave).
+template <bool CL, bool CS>
+__device__ __forceinline__ void cast_body(const float* src, uint16_t* dst, int64_t vlo, int64_t vhi) {
+  const int lane = lane_id();
+  const float* sv = src + vlo;
+  uint16_t* dv = dst + vlo;
+  const int64_t ng = (vhi - vlo) >> 2;
+  constexpr int U = kCoUnroll;
+  int64_t base = 0;
+  for (; base + 64 * U <= ng; base += 64 * U) {
+    f32x4 v[U];
 #pragma unroll
-        for (int k = 0; k < U; ++k) v[k] = load<u32x4, CL>(sv + (base + lane + 64 * k) * 8);
+    for (int k = 0; k < U; ++k) v[k] = load<f32x4, CL>(sv + (base + lane + 64 * k) * 4);
 #pragma unroll
-        for (int k = 0; k < U; ++k) store<u32x4, CS>(dv + (base + lane + 64 * k) * 8, v[k]);
-      }
-      for (int64_t gk = base + lane; gk < ng; gk += 64) store<u32x4, CS>(dv + gk * 8, load<u32x4, CL>(sv + gk * 8));
+    for (int k = 0; k < U; ++k) store<u32x2, CS>(dv + (base + lane + 64 * k) * 4, cast4(v[k]));
+  }
+  for (int64_t gk = base + lane; gk < ng; gk += 64)
+    store<u32x2, CS>(dv + gk * 4, cast4(load<f32x4, CL>(sv + gk * 4)));
+}
+
+template <bool F32, bool CL, bool CS, bool STAGED>
+__global__ __launch_bounds__(tide::kThreads) void ag_copyin_kernel(const CallHdr* __restrict__ hdr,
+                                                                   const void* const* __restrict__ ptrs,
+                                                                   const int32_t* __restrict__ chunk_begin,
+                                                                   int32_t nseg, int32_t nchunks, int32_t chunk) {
+  const Tables a{hdr, ptrs, nseg, 1, nchunks, chunk};
+  const int32_t* cb = chunk_table<STAGED>(chunk_begin, nseg);
+  int32_t w, nw;
+  wave_slot(&w, &nw);
+  int32_t cur = 0;
+  int32_t c = w;
+  CoDesc next;
+  if (c < a.nchunks) co_fetch(a, cb, &cur, c, &next);
+  const int lane = lane_id();
+  while (c < a.nchunks) {
+    const CoDesc d = next;
+    const int32_t cn = c + nw;
+    if (cn < a.nchunks) co_fetch(a, cb, &cur, cn, &next);
+    if (d.h.kind == tide::kZero) {
+      // padding of the rank-major slot: bf16 +0
+      const Chunk r = chunk_range(d.h, d.j, d.nch, a.chunk, 8);
+      for (int64_t e = r.lo + lane; e < r.vlo; e += 64) store2(d.dst + e, 0);
+      for (int64_t e = r.vhi + lane; e < r.hi; e += 64) store2(d.dst + e, 0);
+      for (int64_t e = r.vlo + int64_t(lane) * 8; e < r.vhi; e += 512) store<u32x4, CS>(d.dst + e, u32x4{0, 0, 0, 0});
+    } else if constexpr (F32) {
+      const Chunk r = chunk_range(d.h, d.j, d.nch, a.chunk, 4);
+      const float* src = static_cast<const float*>(d.src);
+      for (int64_t e = r.lo + lane; e < r.vlo; e += 64) store2(d.dst + e, uint16_t(f32_to_bf16(load<float, true>(src + e))));
+      for (int64_t e = r.vhi + lane; e < r.hi; e += 64) store2(d.dst + e, uint16_t(f32_to_bf16(load<float, true>(src + e))));
+      if (r.vhi > r.vlo) cast_body<CL, CS>(src, d.dst, r.vlo, r.vhi);
+    } else {
+      const Chunk r = chunk_range(d.h, d.j, d.nch, a.chunk, 8);
+      const uint16_t* src = static_cast<const uint16_t*>(d.src);
+      for (int64_t e = r.lo + lane; e < r.vlo; e += 64) store2(d.dst + e, load2(src + e));
+      for (int64_t e = r.vhi + lane; e < r.hi; e += 64) store2(d.dst + e, load2(src + e));
+      if (r.vhi > r.vlo) copy_body<CL, CS>(src, d.dst, r.vlo, r.vhi);
     }
     c = cn;
   }
@@ -472,6 +559,43 @@ int launch_ag_copyout(const KernelArgs& a, int64_t grid, void* stream) {
     TIDE_CO(false, false);
   }
 #undef TIDE_CO
+  return int(hipGetLastError());
+}
+
+int launch_ag_copyin(const KernelArgs& a, bool f32, int64_t grid, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  bool staged;
+  const size_t lds = staged_bytes(a, &staged);
+  const bool cl = a.flags & TIDE_FLAG_CACHED_LOADS, cs = a.flags & TIDE_FLAG_CACHED_STORES;
+  const dim3 g{unsigned(grid), 1, 1}, b{unsigned(kThreads), 1, 1};
+#define TIDE_CI(F, CL, CS)                                                                       \
+  do {                                                                                            \
+    if (staged)                                                                                   \
+      hipLaunchKernelGGL((ag_copyin_kernel<F, CL, CS, true>), g, b, lds, s, a.hdr, a.ptrs,        \
+                         a.chunk_begin, a.nseg, a.nchunks, a.chunk);                              \
+    else                                                                                          \
+      hipLaunchKernelGGL((ag_copyin_kernel<F, CL, CS, false>), g, b, 0, s, a.hdr, a.ptrs,         \
+                         a.chunk_begin, a.nseg, a.nchunks, a.chunk);                              \
+  } while (0)
+#define TIDE_CI_F(F)              \
+  do {                            \
+    if (cl && cs) {               \
+      TIDE_CI(F, true, true);     \
+    } else if (cl) {              \
+      TIDE_CI(F, true, false);    \
+    } else if (cs) {              \
+      TIDE_CI(F, false, true);    \
+    } else {                      \
+      TIDE_CI(F, false, false);   \
+    }                             \
+  } while (0)
+  if (f32) {
+    TIDE_CI_F(true);
+  } else {
+    TIDE_CI_F(false);
+  }
+#undef TIDE_CI_F
+#undef TIDE_CI
   return int(hipGetLastError());
 }
 

@@ -110,6 +110,20 @@ std::vector<Seg> copyout_segments(const Geometry& g) {
   return segs;
 }
 
+std::vector<Seg> copyin_segments(const Geometry& g) {
+  std::vector<Seg> segs;
+  for (int32_t p = 0; p < g.nparams; ++p) {
+    for (int32_t r = 0; r < g.world; ++r) {
+      const int64_t real = real_elems(g, p, r);
+      const int64_t slot = int64_t(r) * g.S + g.o[p];
+      const int32_t shard = r * g.nparams + p;
+      if (real > 0) segs.push_back(Seg{0, slot, real, shard, 0, kCopy});
+      if (g.n[p] > real) segs.push_back(Seg{0, slot + real, g.n[p] - real, shard, 0, kZero});
+    }
+  }
+  return segs;
+}
+
 tide_status chunk_table(const std::vector<Seg>& segs, int64_t chunk, std::vector<int32_t>* chunk_begin,
                         std::string* why) {
   chunk_begin->assign(segs.size() + 1, 0);
@@ -152,8 +166,8 @@ tide_status check_options(const tide_options* in, tide_options* out, std::string
 tide_options effective_options(const tide_options& given, Op op, int32_t cu_count) {
   tide_options o = given;
   if (o.cu_budget == 0) o.cu_budget = cu_count;
-  if (o.wg_per_cu == 0) o.wg_per_cu = op == kOpRs ? kRsWgPerCu : kCoWgPerCu;
-  if (o.chunk_elems == 0) o.chunk_elems = op == kOpRs ? kRsChunk : kCoChunk;
+  if (o.wg_per_cu == 0) o.wg_per_cu = op == kOpRs ? kRsWgPerCu : op == kOpCo ? kCoWgPerCu : kCiWgPerCu;
+  if (o.chunk_elems == 0) o.chunk_elems = op == kOpRs ? kRsChunk : op == kOpCo ? kCoChunk : kCiChunk;
   return o;
 }
 
@@ -212,6 +226,36 @@ void co_call_table(const Geometry& g, const std::vector<Seg>& segs, const uint16
     const uintptr_t ps = reinterpret_cast<uintptr_t>(src) & 15, pd = reinterpret_cast<uintptr_t>(dst) & 15;
     const int32_t head = ps == pd ? int32_t(skip_to(reinterpret_cast<uintptr_t>(src), 2, 16)) : -1;
     (*hdr)[s] = CallHdr{sg.len, sg.kind, head};
+  }
+}
+
+void ci_call_table(const Geometry& g, const std::vector<Seg>& segs, const void* const* shards, bool f32,
+                   uint16_t* rank_major, std::vector<CallHdr>* hdr, std::vector<const void*>* ptrs) {
+  (void)g;
+  hdr->resize(segs.size());
+  ptrs->assign(segs.size() * 2, nullptr);
+  for (size_t s = 0; s < segs.size(); ++s) {
+    const Seg& sg = segs[s];
+    uint16_t* dst = rank_major + sg.dst_off;
+    const uintptr_t d = reinterpret_cast<uintptr_t>(dst);
+    (*ptrs)[2 * s + 1] = dst;
+    int32_t kind = sg.kind, head = -1;
+    if (sg.kind == kZero) {
+      head = int32_t(skip_to(d, 2, 16));  // 16-byte zero stores
+    } else if (f32) {
+      kind = kCast;
+      const float* src = static_cast<const float*>(shards[sg.src_idx]) + sg.src_off;
+      (*ptrs)[2 * s] = src;
+      // 16-byte fp32 loads feeding 8-byte bf16 stores: 4 elements
+      const int64_t h = skip_to(reinterpret_cast<uintptr_t>(src), 4, 16);
+      if (((d + uintptr_t(2 * h)) & 7) == 0) head = int32_t(h);
+    } else {
+      const uint16_t* src = static_cast<const uint16_t*>(shards[sg.src_idx]) + sg.src_off;
+      (*ptrs)[2 * s] = src;
+      const uintptr_t ps = reinterpret_cast<uintptr_t>(src) & 15;
+      if (ps == (d & 15)) head = int32_t(skip_to(reinterpret_cast<uintptr_t>(src), 2, 16));
+    }
+    (*hdr)[s] = CallHdr{sg.len, kind, head};
   }
 }
 

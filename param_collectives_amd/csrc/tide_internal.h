@@ -24,9 +24,11 @@ constexpr int32_t kRsWgPerCu = 1;
 constexpr int64_t kRsChunk = 1024;
 constexpr int32_t kCoWgPerCu = 1;
 constexpr int64_t kCoChunk = 4096;
+constexpr int32_t kCiWgPerCu = 1;
+constexpr int64_t kCiChunk = 4096;
 
-enum SegKind : int32_t { kSum = 0, kZero = 1, kCopy = 2 };
-enum Op : int32_t { kOpRs = 0, kOpCo = 1 };
+enum SegKind : int32_t { kSum = 0, kZero = 1, kCopy = 2, kCast = 3 };
+enum Op : int32_t { kOpRs = 0, kOpCo = 1, kOpCi = 2 };
 
 // One contiguous run of work, fixed by the plan (host only).
 struct Seg {
@@ -68,8 +70,12 @@ int64_t real_elems(const Geometry& g, int32_t p, int32_t r);
 //  reduce-scatter: a kSum segment of the real elements and a kZero segment of
 //    the padding elements of each (p, r) (each only when non-empty);
 //  copy-out: a kCopy segment of the real elements of each (p, r).
+//  copy-in: a kCopy segment of the real elements of each (p, r) (the kind
+//    becomes kCast per call for fp32 shards) and a kZero segment of the
+//    slot's padding.
 std::vector<Seg> rs_segments(const Geometry& g);
 std::vector<Seg> copyout_segments(const Geometry& g);
+std::vector<Seg> copyin_segments(const Geometry& g);
 
 // chunk_begin[s] = index of segment s's first chunk, chunk_begin[nseg] = total;
 // segment s owns ceil(len / chunk) chunks.  Fails (TIDE_ERR_RANGE) when the
@@ -92,6 +98,11 @@ void rs_call_table(const Geometry& g, const std::vector<Seg>& segs, const uint16
                    float* const* out, std::vector<CallHdr>* hdr, std::vector<const void*>* ptrs);
 void co_call_table(const Geometry& g, const std::vector<Seg>& segs, const uint16_t* rank_major,
                    uint16_t* const* params, std::vector<CallHdr>* hdr, std::vector<const void*>* ptrs);
+//  copy-in: ptrs per segment = [shard (null for padding), destination];
+//    groups are 4 elements for fp32 shards (16-byte loads, 8-byte stores), 8
+//    for bf16 shards and for padding (16-byte accesses).
+void ci_call_table(const Geometry& g, const std::vector<Seg>& segs, const void* const* shards, bool f32,
+                   uint16_t* rank_major, std::vector<CallHdr>* hdr, std::vector<const void*>* ptrs);
 
 // Device-side launch arguments (kernels.hip).
 struct KernelArgs {
@@ -109,5 +120,6 @@ struct KernelArgs {
 // status (hipError_t as int).
 int launch_rs_local(const KernelArgs& a, int64_t grid, void* stream);
 int launch_ag_copyout(const KernelArgs& a, int64_t grid, void* stream);
+int launch_ag_copyin(const KernelArgs& a, bool f32, int64_t grid, void* stream);
 
 }  // namespace tide

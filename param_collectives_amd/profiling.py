@@ -33,7 +33,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 KERNEL_SOURCE = os.path.join(HERE, "csrc", "kernels.hip")
-KERNEL_REGEX = "rs_local_kernel|ag_copyout_kernel"
+KERNEL_REGEX = "rs_local_kernel|ag_copyout_kernel|ag_copyin_kernel"
 COUNTER_PASSES = {
     "fetch": ["FETCH_SIZE"],
     "write": ["WRITE_SIZE"],
@@ -81,7 +81,7 @@ def collect_trace(workload, out, steps=10):
 def collect_counters(workload, out, launches=3):
     os.makedirs(out, exist_ok=True)
     cmds = {}
-    for only in ("rs", "co", "calib"):
+    for only in ("rs", "co", "ci", "calib"):
         for name, counters in COUNTER_PASSES.items():
             d = os.path.join(out, f"pmc_{only}_{name}")
             cmd = ["rocprofv3", "--pmc", *counters, "--kernel-include-regex", KERNEL_REGEX, "-f", "csv", "-d", d,
@@ -119,7 +119,7 @@ def _read_counter(d, counter):
 
 
 def _short(name):
-    for k in ("rs_local_kernel", "ag_copyout_kernel"):
+    for k in ("rs_local_kernel", "ag_copyout_kernel", "ag_copyin_kernel"):
         if k in name:
             return k
     return name[:60]
@@ -157,7 +157,7 @@ def summarize(workload, out, profiles):
     lines.append(f"{'kernel':<22} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}")
     for r in stats:
         name = _short(r.get("Name", r.get("KernelName", "")))
-        if name not in ("rs_local_kernel", "ag_copyout_kernel"):
+        if name not in ("rs_local_kernel", "ag_copyout_kernel", "ag_copyin_kernel"):
             continue
         avg = float(r.get("AverageNs", 0)) / 1e3
         mn = float(r.get("MinNs", 0) or 0) / 1e3
@@ -192,9 +192,12 @@ def summarize(workload, out, profiles):
            "fetch_factor": calib_bytes / (cf * 1024.0), "write_factor": calib_bytes / (cw * 1024.0)}
     kernels = {}
     for only, kname, alg_r, alg_w in (("rs", "rs_local", 2 * w.world * sum_dk, 4 * w.world * S),
-                                      ("co", "ag_copyout", 2 * sum_dk, 2 * sum_dk)):
+                                      ("co", "ag_copyout", 2 * sum_dk, 2 * sum_dk),
+                                      ("ci", "ag_copyin", 4 * sum_dk, 2 * w.world * S)):
         f = med(only, "fetch", "FETCH_SIZE", kname)
         wr = med(only, "write", "WRITE_SIZE", kname)
+        if f is None or wr is None:
+            continue
         traffic_r = f * 1024.0 * cal["fetch_factor"]
         traffic_w = wr * 1024.0 * cal["write_factor"]
         kernels[f"{kname}/{workload}"] = {

@@ -27,6 +27,8 @@ STATUS_NAMES = {
 }
 FLAG_CACHED_LOADS = 0x1
 FLAG_CACHED_STORES = 0x2
+DTYPE_BF16 = 0
+DTYPE_F32 = 1
 MAX_WORLD = 256
 
 # Every symbol include/tide.h declares.
@@ -38,6 +40,7 @@ EXPORTS = (
     "tide_plan_get_options",
     "tide_reduce_scatter_local",
     "tide_allgather_copyout",
+    "tide_allgather_copyin",
     "tide_plan_destroy",
     "tide_last_error",
 )
@@ -68,6 +71,7 @@ def _load():
     lib.tide_plan_get_options.argtypes = [vp, i32, ctypes.POINTER(Options)]
     lib.tide_reduce_scatter_local.argtypes = [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.c_float, i32, vp]
     lib.tide_allgather_copyout.argtypes = [vp, vp, ctypes.POINTER(vp), vp]
+    lib.tide_allgather_copyin.argtypes = [vp, ctypes.POINTER(vp), i32, vp, vp]
     lib.tide_plan_destroy.argtypes = [vp]
     lib.tide_plan_destroy.restype = None
     lib.tide_last_error.argtypes = []
@@ -116,6 +120,9 @@ class Plan:
                                     S.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))))
         self.rows_per_rank, self.shard_offset, self.shard_elems = R, o, int(S[0])
         self.numel = [int(np.prod(s, dtype=np.int64)) for s in self.shapes]
+        # real elements of rank r's shard of parameter p
+        self.n_real = [[max(0, min(int(R[p]), s[0] - r * int(R[p]))) * (self.numel[p] // s[0] if s[0] else 0)
+                        for p, s in enumerate(self.shapes)] for r in range(self.world)]
 
     def segments(self, op):
         """The work segments (op 0: reduce-scatter, 1: copy-out) as an int64
@@ -156,6 +163,12 @@ class Plan:
         out_ptrs[r] (ints), stream a hipStream_t handle (int)."""
         _check(lib.tide_reduce_scatter_local(self.handle, _ptr_array(grad_ptrs), _ptr_array(out_ptrs),
                                              float(alpha), int(accumulate), ctypes.c_void_p(int(stream) or None)))
+
+    def allgather_copyin_raw(self, shard_ptrs, shard_dtype, rank_major_ptr, stream=0):
+        """tide_allgather_copyin on raw device addresses (shard_ptrs[r*P+p])."""
+        _check(lib.tide_allgather_copyin(self.handle, _ptr_array(shard_ptrs), int(shard_dtype),
+                                         ctypes.c_void_p(int(rank_major_ptr) or None),
+                                         ctypes.c_void_p(int(stream) or None)))
 
     def allgather_copyout_raw(self, rank_major_ptr, param_ptrs, stream=0):
         """tide_allgather_copyout on raw device addresses."""
@@ -218,3 +231,26 @@ def allgather_copyout(plan, rank_major, params, stream=None):
     for p in range(P):
         _require(params[p], torch.bfloat16, plan.numel[p], f"params[{p}]")
     plan.allgather_copyout_raw(rank_major.data_ptr(), [t.data_ptr() for t in params], _stream_handle(stream))
+
+
+def allgather_copyin(plan, shards, rank_major, stream=None):
+    """All-gather copy-in: shards[r][p] (rank r's local shard of parameter p,
+    n_real(p, r) elements, all float32 or all bfloat16) -> rank_major (bf16,
+    W*S elements; fp32 shards are cast by round to nearest even)."""
+    import torch
+
+    W, P = plan.world, len(plan.shapes)
+    if len(shards) != W or any(len(row) != P for row in shards):
+        raise ValueError(f"shards must be {W} lists of {P} tensors")
+    dtypes = {t.dtype for row in shards for t in row}
+    if dtypes not in ({torch.float32}, {torch.bfloat16}):
+        raise TypeError(f"shards must be all torch.float32 or all torch.bfloat16, got {dtypes}")
+    dtype = dtypes.pop()
+    ptrs = []
+    for r in range(W):
+        for p in range(P):
+            _require(shards[r][p], dtype, plan.n_real[r][p], f"shards[{r}][{p}]")
+            ptrs.append(shards[r][p].data_ptr())
+    _require(rank_major, torch.bfloat16, W * plan.shard_elems, "rank_major")
+    plan.allgather_copyin_raw(ptrs, DTYPE_F32 if dtype == torch.float32 else DTYPE_BF16, rank_major.data_ptr(),
+                              _stream_handle(stream))

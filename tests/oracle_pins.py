@@ -441,6 +441,84 @@ def check_copyout_matches_stock_and_skips_padding(orc, seed=13):
                 assert np.array_equal(again[p], X[p])
 
 
+# --------------------------------------------------------------- copy-in
+
+
+def check_cast_worked_golden(orc):
+    g = goldens.read("cast_worked.txt")
+    x = np.array([int(r[0], 16) for r in g["cast"]], dtype=np.uint32).view(np.float32)
+    want = np.array([int(r[1], 16) for r in g["cast"]], dtype=np.uint16)
+    got = orc.cast_bf16(x)
+    bad = [(hex(int(a)), hex(int(b)), hex(int(c))) for a, b, c in zip(x.view(np.uint32), got, want) if b != c]
+    assert not bad, bad
+
+
+def check_cast_matches_torch_rne(orc, seed=14):
+    """The cast equals torch's float32 -> bfloat16 conversion (round to nearest
+    even) on every non-NaN input, and keeps NaNs NaN."""
+    import torch
+
+    rng = np.random.default_rng(seed)
+    x = np.concatenate([
+        rng.standard_normal(200000).astype(np.float32),
+        (rng.standard_normal(20000) * 1e-39).astype(np.float32),
+        rng.integers(0, 2**32, size=200000, dtype=np.uint64).astype(np.uint32).view(np.float32),
+    ])
+    got = orc.cast_bf16(x)
+    ref = torch.from_numpy(x.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    nan = np.isnan(x)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.all((got[nan] & 0x7F80) == 0x7F80) and np.all((got[nan] & 0x7F) != 0)
+    assert np.array_equal(got[nan] >> 15, (x[nan].view(np.uint32) >> 31).astype(np.uint16))
+
+
+def shards_of(world, shapes, X):
+    """Each rank's local shard of each parameter: its real rows, as views."""
+    out = [[None] * len(shapes) for _ in range(world)]
+    for p, s in enumerate(shapes):
+        D = s[0]
+        R = -(-D // world)
+        rows = np.asarray(X[p]).reshape((D,) + tuple(s[1:]))
+        for r in range(world):
+            out[r][p] = rows[min(r * R, D):min((r + 1) * R, D)]
+    return out
+
+
+def check_copyin_bf16_equals_pack_and_round_trips(orc, seed=15):
+    rng = np.random.default_rng(seed)
+    for W in (1, 2, 3, 4, 8):
+        shapes = random_case(rng, W, int(rng.integers(1, 6)))
+        X = [rng.integers(0, 0x10000, size=s, dtype=np.uint16) for s in shapes]
+        rm = orc.copyin(W, shapes, shards_of(W, shapes, X))
+        assert np.array_equal(rm, orc.pack(W, shapes, X))
+        back = orc.copyout(W, shapes, rm)
+        for p in range(len(shapes)):
+            assert np.array_equal(back[p], X[p])
+
+
+def check_copyin_f32_is_cast_then_stock_pack(orc, seed=16):
+    """fp32 shards: the result equals the stock path, i.e. torch's bf16 cast of
+    the whole parameter followed by zero-padded rank-major packing."""
+    import torch
+
+    rng = np.random.default_rng(seed)
+    for W in (2, 4, 8):
+        shapes = random_case(rng, W, int(rng.integers(1, 6)))
+        X = [(rng.standard_normal(s) * rng.choice([1e-3, 1.0, 1e30])).astype(np.float32) for s in shapes]
+        rm = orc.copyin(W, shapes, shards_of(W, shapes, X))
+        cast = [torch.from_numpy(x.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16) for x in X]
+        R = [-(-s[0] // W) for s in shapes]
+        K = [int(np.prod(s[1:], dtype=np.int64)) for s in shapes]
+        want = []
+        for r in range(W):
+            for p, s in enumerate(shapes):
+                padded = np.zeros((W * R[p], K[p]), dtype=np.uint16)
+                padded[:s[0]] = cast[p].reshape(s[0], K[p])
+                want.append(padded[r * R[p]:(r + 1) * R[p]].reshape(-1))
+        want = np.concatenate(want) if want else np.zeros(0, np.uint16)
+        assert np.array_equal(rm, want), (W, shapes)
+
+
 ALL_CHECKS = [
     check_tiny_plan_golden,
     check_plan_invariants,
@@ -460,4 +538,8 @@ ALL_CHECKS = [
     check_copyout_worked_golden,
     check_copyout_round_trip,
     check_copyout_matches_stock_and_skips_padding,
+    check_cast_worked_golden,
+    check_cast_matches_torch_rne,
+    check_copyin_bf16_equals_pack_and_round_trips,
+    check_copyin_f32_is_cast_then_stock_pack,
 ]

@@ -361,3 +361,120 @@ def test_offsets_beyond_two_to_the_31(tide, oracle_mod, world, shape):
     tide.allgather_copyout(plan, rm, [param])
     torch.cuda.synchronize()
     assert torch.equal(param.view(torch.int16), grads[0][0].view(torch.int16))
+
+
+# ------------------------------------------------------------ copy-in
+
+
+def run_copyin(tide, plan, shard_bits_or_f32, shard_offsets=None, guard=64):
+    """Upload shards ([r][p] numpy uint16 bf16 bits or float32), run the
+    copy-in into a canary-filled rank-major buffer with guard bands, return
+    the rank-major buffer as uint16."""
+    import torch
+
+    W, P = plan.world, len(plan.shapes)
+    keep, shards = [], []
+    for r in range(W):
+        row = []
+        for p in range(P):
+            a = np.asarray(shard_bits_or_f32[r][p]).reshape(-1)
+            off = 0 if shard_offsets is None else shard_offsets[r][p]
+            if a.dtype == np.uint16:
+                base = gpu_util.to_device_bf16(np.concatenate([np.full(off, 0x7FC1, np.uint16), a]))
+            else:
+                base = torch.from_numpy(np.concatenate([np.full(off, np.nan, np.float32), a])).cuda()
+            keep.append(base)
+            row.append(base[off:])
+        shards.append(row)
+    n = W * plan.shard_elems
+    buf = torch.empty(n + 2 * guard, dtype=torch.bfloat16, device="cuda")
+    buf.view(torch.int16).fill_(0x7FC1)
+    tide.allgather_copyin(plan, shards, buf[guard:guard + n])
+    torch.cuda.synchronize()
+    h = gpu_util.bf16_bits(buf)
+    assert np.all(h[:guard] == 0x7FC1) and np.all(h[guard + n:] == 0x7FC1), "guard band overwritten"
+    return h[guard:guard + n]
+
+
+@pytest.mark.parametrize("f32", [True, False], ids=["fp32", "bf16"])
+def test_copyin_tiny_and_round_trip(tide, oracle_mod, f32):
+    w = synth.workload("tiny")
+    rng = np.random.default_rng(20)
+    X = [rng.standard_normal(s).astype(np.float32) if f32 else rng.integers(0, 0x10000, size=s, dtype=np.uint16)
+         for s in w.shapes]
+    shards = oracle_pins.shards_of(w.world, w.shapes, X)
+    plan = tide.Plan(w.world, w.shapes)
+    got = run_copyin(tide, plan, shards)
+    want = oracle_mod.copyin(w.world, w.shapes, shards)
+    assert np.array_equal(got, want)
+    # GPU round trip: copy-in then copy-out gives the (cast) parameters back
+    back = run_copyout(tide, plan, got)
+    for p in range(w.nparams):
+        ref = oracle_mod.cast_bf16(X[p]).reshape(w.shapes[p]) if f32 else X[p]
+        assert np.array_equal(back[p], ref)
+
+
+@pytest.mark.parametrize("world", [1, 3, 4, 8])
+@pytest.mark.parametrize("f32", [True, False], ids=["fp32", "bf16"])
+def test_copyin_random_shapes(tide, oracle_mod, world, f32):
+    rng = np.random.default_rng(300 + world + 7 * f32)
+    for trial in range(3):
+        shapes = random_shapes(rng, world, int(rng.integers(1, 6)))
+        shapes.append((world * 43 + 5, 257))
+        X = [(rng.standard_normal(s) * 10).astype(np.float32) if f32 else
+             rng.integers(0, 0x10000, size=s, dtype=np.uint16) for s in shapes]
+        shards = oracle_pins.shards_of(world, shapes, X)
+        plan = tide.Plan(world, shapes, chunk_elems=512)
+        assert np.array_equal(run_copyin(tide, plan, shards), oracle_mod.copyin(world, shapes, shards)), shapes
+
+
+def test_copyin_misaligned_and_special_values(tide, oracle_mod):
+    rng = np.random.default_rng(21)
+    W = 4
+    shapes = [(W * 60 + 3, 37), (11,), (W * 8, 64)]
+    specials = np.array([0x7FC00001, 0x7F800001, 0xFFA10000, 0x7F800000, 0xFF800000, 0x7F7FFFFF, 0x3F808000,
+                         0x3F818000, 0x00008000, 0x00018000, 0x80000000, 0x007FFFFF], dtype=np.uint32).view(np.float32)
+    X = [np.where(rng.random(s) < 0.2, rng.choice(specials, size=s), rng.standard_normal(s)).astype(np.float32)
+         for s in shapes]
+    shards = oracle_pins.shards_of(W, shapes, X)
+    want = oracle_mod.copyin(W, shapes, shards)
+    plan = tide.Plan(W, shapes, chunk_elems=256)
+    for offs in ([[0] * 3] * W, [[1, 2, 3]] * W, [[(r + p) % 4 for p in range(3)] for r in range(W)]):
+        assert np.array_equal(run_copyin(tide, plan, shards, shard_offsets=offs), want), offs
+    bits = [rng.integers(0, 0x10000, size=s, dtype=np.uint16) for s in shapes]
+    bshards = oracle_pins.shards_of(W, shapes, bits)
+    bwant = oracle_mod.copyin(W, shapes, bshards)
+    for offs in ([[0] * 3] * W, [[1, 3, 5]] * W, [[(r + 2 * p) % 8 for p in range(3)] for r in range(W)]):
+        assert np.array_equal(run_copyin(tide, plan, bshards, shard_offsets=offs), bwant), offs
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", FULL)
+def test_copyin_full_size_bit_exact(tide, oracle_mod, name):
+    """fp32 master shards of every rank at the full layer shapes -> the
+    rank-major bf16 buffer, every element, in the default launch options."""
+    import os
+
+    import torch
+
+    w = synth.workload(name)
+    print(f"\n[copy-in full-size] {name}", flush=True)
+    plan = tide.Plan(w.world, w.shapes)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(synth.device_seed(w.index, 2000))
+    params = [torch.randn(s, generator=g, device="cuda", dtype=torch.float32) * w.sigma for s in w.shapes]
+    shards = []
+    for r in range(w.world):
+        row = []
+        for p, s in enumerate(w.shapes):
+            R = plan.rows_per_rank[p]
+            row.append(params[p][min(r * R, s[0]):min((r + 1) * R, s[0])])
+        shards.append(row)
+    rm = torch.empty(w.world * plan.shard_elems, dtype=torch.bfloat16, device="cuda")
+    tide.allgather_copyin(plan, shards, rm)
+    torch.cuda.synchronize()
+    got = gpu_util.bf16_bits(rm)
+    host = [[t.cpu().numpy() for t in row] for row in shards]
+    want = oracle_mod.copyin(w.world, w.shapes, host, nthreads=min(16, os.cpu_count() or 1))
+    assert np.array_equal(got, want)
+    print(f"[copy-in full-size] {name}: bit-exact", flush=True)

@@ -249,3 +249,52 @@ def test_too_many_chunks_is_a_range_error(tide):
         plan.set_options(chunk_elems=8)
     assert _status(e) == -2
     assert plan.options(0)["chunk_elems"] == 1024  # unchanged after the failed call
+
+
+@pytest.mark.parametrize("world,shapes", CASES)
+def test_copyin_segments_describe_the_oracle_layout(tide, oracle_mod, world, shapes):
+    """Each (rank, parameter) slot of the rank-major buffer is one copy segment
+    of the rank's real elements followed by one zero segment of padding."""
+    plan = tide.Plan(world, shapes)
+    geo = oracle_mod.plan(world, shapes)
+    ci = plan.segments(2)
+    P = len(shapes)
+    assert np.all(ci[:, 5] > 0)
+    for p in range(P):
+        for r in range(world):
+            real = geo["n_real"][p, r]
+            pad = geo["n"][p] - real
+            slot = geo["rank_major_offset"][p, r]
+            mine = ci[ci[:, 1] == r * P + p]
+            copies, zeros = mine[mine[:, 0] == 2], mine[mine[:, 0] == 1]
+            assert len(copies) == (1 if real else 0) and len(zeros) == (1 if pad else 0)
+            if real:
+                assert tuple(copies[0, 3:]) == (0, slot, real)
+            if pad:
+                assert tuple(zeros[0, 4:]) == (slot + real, pad)
+    assert ci[:, 5].sum() == world * geo["S"]  # the whole rank-major buffer is written
+
+
+def test_copyin_argument_errors(tide):
+    plan = tide.Plan(4, oracle_pins.TINY_SHAPES)
+    good = [FAKE + 0x1000 * i for i in range(16)]
+    with pytest.raises(tide.TideError) as e:
+        plan.allgather_copyin_raw(good[:3] + [0] + good[4:], tide.DTYPE_F32, FAKE)
+    assert _status(e) == -1
+    with pytest.raises(tide.TideError) as e:
+        plan.allgather_copyin_raw(good[:3] + [FAKE + 2] + good[4:], tide.DTYPE_F32, FAKE)
+    assert _status(e) == -3
+    with pytest.raises(tide.TideError) as e:
+        plan.allgather_copyin_raw(good, 7, FAKE)
+    assert _status(e) == -1
+    with pytest.raises(tide.TideError) as e:
+        plan.allgather_copyin_raw(good, tide.DTYPE_BF16, 0)
+    assert _status(e) == -1
+    with pytest.raises(tide.TideError) as e:
+        plan.allgather_copyin_raw(good, tide.DTYPE_BF16, FAKE + 1)
+    assert _status(e) == -3
+    # rank 3 holds nothing of parameter 3 ([3,3,4] with W = 4): its shard may be NULL,
+    # but the call still fails (later) on the misaligned buffer
+    with pytest.raises(tide.TideError) as e:
+        plan.allgather_copyin_raw(good[:15] + [0], tide.DTYPE_BF16, FAKE + 1)
+    assert _status(e) == -3

@@ -50,6 +50,18 @@ MUTANTS = [
      "(e < real) ? src[e] : (uint16_t)0;", "(e < real) ? src[e] : (uint16_t)0x8000;"),
     ("row_length_drops_last_dim",
      "for (int32_t j = 1; j < ndims[p]; ++j) {", "for (int32_t j = 1; j < ndims[p] - 1; ++j) {"),
+    ("cast_rounds_half_up",
+     "return (uint16_t)((u + 0x7FFFu + keep_odd) >> 16);", "return (uint16_t)((u + 0x8000u) >> 16);"),
+    ("cast_truncates",
+     "return (uint16_t)((u + 0x7FFFu + keep_odd) >> 16);", "return (uint16_t)((u + 0u * keep_odd) >> 16);"),
+    ("cast_nan_not_quieted",
+     "if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x0040u);",
+     "if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)(u >> 16);"),
+    ("copyin_padding_not_zero",
+     "        if (e >= real) {\n            dst[e] = 0;", "        if (e >= real) {\n            dst[e] = 0x8000;"),
+    ("copyin_wrong_destination_rank",
+     "uint16_t* dst = j->rank_major_out + (int64_t)r * g->S + g->o[p];\n    const void* src = j->shards",
+     "uint16_t* dst = j->rank_major_out + (int64_t)(g->W - 1 - r) * g->S + g->o[p];\n    const void* src = j->shards"),
     ("rs_source_row_offset_uses_real_count",
      "int64_t first = (int64_t)r * g->R[p] * g->K[p];\n    float* dst",
      "int64_t first = (int64_t)r * real;\n    float* dst"),
