@@ -86,10 +86,10 @@ typedef enum {
  *               device's CU count.  Workgroups are dispatched round-robin over
  *               the 8 XCDs, so a budget is a grid size, not a CU mask.
  *   wg_per_cu   workgroups (256 threads, four waves) per budgeted CU;
- *               default 1.
+ *               default 1 (reduce-scatter, copy-out), 2 (copy-in).
  *   chunk_elems elements per chunk (the unit a wave takes), a multiple of 8,
- *               at most 2^28; default 1024 (reduce-scatter), 4096 (copy-out
- *               and copy-in).
+ *               at most 2^28; default 1024 (reduce-scatter), 4096 (copy-out),
+ *               2048 (copy-in).
  *               A plan may have at most 2^31 - 1 chunks per operation.
  *   flags       TIDE_FLAG_* bits.
  */

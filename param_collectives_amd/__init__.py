@@ -5,6 +5,9 @@
   allgather_copyout      rank-major bf16 buffer -> per-parameter tensors
   allgather_copyin       every rank's fp32/bf16 shards -> rank-major bf16 buffer
 
+The *_call variants check and marshal the tensors once and return a callable
+that launches with one library call (for buffers reused every step).
+
 The work runs in the HIP library libtide.so (include/tide.h); importing this
 package fails if that library has not been built.
 """
@@ -17,6 +20,9 @@ from .tide import (  # noqa: F401
     DTYPE_F32,
     TideError,
     allgather_copyin,
+    allgather_copyin_call,
     allgather_copyout,
+    allgather_copyout_call,
+    reduce_scatter_call,
     reduce_scatter_local,
 )

@@ -362,16 +362,10 @@ __device__ __forceinline__ void co_fetch(const Tables& a, const int32_t* cb, int
   d->dst = static_cast<uint16_t*>(const_cast<void*>(a.ptrs[2 * int64_t(s) + 1]));
 }
 
-// bf16 words of [vlo, vhi) (groups of 8, both sides 16-byte aligned).
-template <bool CL, bool CS>
-__device__ __forceinline__ void copy_body(const uint16_t* src, uint16_t* dst, int64_t vlo, int64_t vhi) {
-  const int lane = lane_id();
-  const uint16_t* sv = src + vlo;
-  uint16_t* dv = dst + vlo;
-  const int64_t ng = (vhi - vlo) >> 3;
-  constexpr int U = kCoUnroll;
-  // U 16-byte loads in flight per lane; then one group per lane per step.
-  int64_t base = 0;
+// Full steps of U groups of 8 bf16 per lane (all loads issued before the
+// stores); returns where the steps stopped.
+template <int U, bool CL, bool CS>
+__device__ __forceinline__ int64_t copy_steps(const uint16_t* sv, uint16_t* dv, int64_t base, int64_t ng, int lane) {
   for (; base + 64 * U <= ng; base += 64 * U) {
     u32x4 v[U];
 #pragma unroll
@@ -379,6 +373,20 @@ __device__ __forceinline__ void copy_body(const uint16_t* src, uint16_t* dst, in
 #pragma unroll
     for (int k = 0; k < U; ++k) store<u32x4, CS>(dv + (base + lane + 64 * k) * 8, v[k]);
   }
+  return base;
+}
+
+// bf16 words of [vlo, vhi) (groups of 8, both sides 16-byte aligned).
+template <bool CL, bool CS>
+__device__ __forceinline__ void copy_body(const uint16_t* src, uint16_t* dst, int64_t vlo, int64_t vhi) {
+  const int lane = lane_id();
+  const uint16_t* sv = src + vlo;
+  uint16_t* dv = dst + vlo;
+  const int64_t ng = (vhi - vlo) >> 3;
+  // kCoUnroll 16-byte loads in flight per lane, then two, then one.
+  int64_t base = 0;
+  base = copy_steps<kCoUnroll, CL, CS>(sv, dv, base, ng, lane);
+  base = copy_steps<2, CL, CS>(sv, dv, base, ng, lane);
   for (int64_t gk = base + lane; gk < ng; gk += 64) store<u32x4, CS>(dv + gk * 8, load<u32x4, CL>(sv + gk * 8));
 }
 
@@ -425,6 +433,18 @@ __device__ __forceinline__ u32x2 cast4(f32x4 v) {
   return u32x2{f32_to_bf16(v.x) | (f32_to_bf16(v.y) << 16), f32_to_bf16(v.z) | (f32_to_bf16(v.w) << 16)};
 }
 
+template <int U, bool CL, bool CS>
+__device__ __forceinline__ int64_t cast_steps(const float* sv, uint16_t* dv, int64_t base, int64_t ng, int lane) {
+  for (; base + 64 * U <= ng; base += 64 * U) {
+    f32x4 v[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) v[k] = load<f32x4, CL>(sv + (base + lane + 64 * k) * 4);
+#pragma unroll
+    for (int k = 0; k < U; ++k) store<u32x2, CS>(dv + (base + lane + 64 * k) * 4, cast4(v[k]));
+  }
+  return base;
+}
+
 // fp32 [vlo, vhi) -> bf16 (groups of 4: 16-byte loads, 8-byte stores, each
 // contiguous across the wave).
 template <bool CL, bool CS>
@@ -433,15 +453,9 @@ __device__ __forceinline__ void cast_body(const float* src, uint16_t* dst, int64
   const float* sv = src + vlo;
   uint16_t* dv = dst + vlo;
   const int64_t ng = (vhi - vlo) >> 2;
-  constexpr int U = kCoUnroll;
   int64_t base = 0;
-  for (; base + 64 * U <= ng; base += 64 * U) {
-    f32x4 v[U];
-#pragma unroll
-    for (int k = 0; k < U; ++k) v[k] = load<f32x4, CL>(sv + (base + lane + 64 * k) * 4);
-#pragma unroll
-    for (int k = 0; k < U; ++k) store<u32x2, CS>(dv + (base + lane + 64 * k) * 4, cast4(v[k]));
-  }
+  base = cast_steps<kCoUnroll, CL, CS>(sv, dv, base, ng, lane);
+  base = cast_steps<2, CL, CS>(sv, dv, base, ng, lane);
   for (int64_t gk = base + lane; gk < ng; gk += 64)
     store<u32x2, CS>(dv + gk * 4, cast4(load<f32x4, CL>(sv + gk * 4)));
 }

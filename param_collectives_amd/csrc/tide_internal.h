@@ -24,8 +24,8 @@ constexpr int32_t kRsWgPerCu = 1;
 constexpr int64_t kRsChunk = 1024;
 constexpr int32_t kCoWgPerCu = 1;
 constexpr int64_t kCoChunk = 4096;
-constexpr int32_t kCiWgPerCu = 1;
-constexpr int64_t kCiChunk = 4096;
+constexpr int32_t kCiWgPerCu = 2;    // the copy-in's cast body wants more waves in flight
+constexpr int64_t kCiChunk = 2048;
 
 enum SegKind : int32_t { kSum = 0, kZero = 1, kCopy = 2, kCast = 3 };
 enum Op : int32_t { kOpRs = 0, kOpCo = 1, kOpCi = 2 };

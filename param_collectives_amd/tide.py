@@ -198,9 +198,22 @@ def _require(t, dtype, numel, what):
         raise ValueError(f"{what}: expected {numel} elements, got {t.numel()}")
 
 
-def reduce_scatter_local(plan, grads, outs, alpha=1.0, accumulate=False, stream=None):
-    """Reduce-scatter local stage: grads[u][p] (bf16, plan.shapes[p]) for u in
-    [0, W) -> outs[r] (fp32, plan.shard_elems elements) for r in [0, W)."""
+class Call:
+    """One operation with its tensors checked and its pointer arrays
+    marshalled once (the buffers an FSDP2 group reuses every step); calling it
+    launches on the given (or current) stream with a single library call.
+    It holds references to the tensors, so they outlive it."""
+
+    def __init__(self, fn, args, tensors):
+        self._fn = fn
+        self._args = args
+        self._tensors = tensors
+
+    def __call__(self, stream=None):
+        _check(self._fn(*self._args, ctypes.c_void_p(_stream_handle(stream) or None)))
+
+
+def _rs_checked(plan, grads, outs):
     import torch
 
     W, P = plan.world, len(plan.shapes)
@@ -215,13 +228,25 @@ def reduce_scatter_local(plan, grads, outs, alpha=1.0, accumulate=False, stream=
             ptrs.append(grads[u][p].data_ptr())
     for r in range(W):
         _require(outs[r], torch.float32, plan.shard_elems, f"outs[{r}]")
-    plan.reduce_scatter_local_raw(ptrs, [o.data_ptr() for o in outs], alpha, int(bool(accumulate)),
-                                  _stream_handle(stream))
+    return ptrs, [o.data_ptr() for o in outs]
 
 
-def allgather_copyout(plan, rank_major, params, stream=None):
-    """All-gather copy-out: rank_major (bf16, W*S elements) -> params[p]
-    (bf16, plan.shapes[p])."""
+def reduce_scatter_call(plan, grads, outs, alpha=1.0, accumulate=False):
+    """A registered reduce-scatter (see reduce_scatter_local)."""
+    g, o = _rs_checked(plan, grads, outs)
+    return Call(lib.tide_reduce_scatter_local,
+                (plan.handle, _ptr_array(g), _ptr_array(o), ctypes.c_float(alpha), int(bool(accumulate))),
+                (plan, grads, outs))
+
+
+def reduce_scatter_local(plan, grads, outs, alpha=1.0, accumulate=False, stream=None):
+    """Reduce-scatter local stage: grads[u][p] (bf16, plan.shapes[p]) for u in
+    [0, W) -> outs[r] (fp32, plan.shard_elems elements) for r in [0, W)."""
+    g, o = _rs_checked(plan, grads, outs)
+    plan.reduce_scatter_local_raw(g, o, alpha, int(bool(accumulate)), _stream_handle(stream))
+
+
+def _co_checked(plan, rank_major, params):
     import torch
 
     P = len(plan.shapes)
@@ -230,13 +255,24 @@ def allgather_copyout(plan, rank_major, params, stream=None):
         raise ValueError(f"params must hold {P} tensors")
     for p in range(P):
         _require(params[p], torch.bfloat16, plan.numel[p], f"params[{p}]")
-    plan.allgather_copyout_raw(rank_major.data_ptr(), [t.data_ptr() for t in params], _stream_handle(stream))
+    return rank_major.data_ptr(), [t.data_ptr() for t in params]
 
 
-def allgather_copyin(plan, shards, rank_major, stream=None):
-    """All-gather copy-in: shards[r][p] (rank r's local shard of parameter p,
-    n_real(p, r) elements, all float32 or all bfloat16) -> rank_major (bf16,
-    W*S elements; fp32 shards are cast by round to nearest even)."""
+def allgather_copyout_call(plan, rank_major, params):
+    """A registered copy-out (see allgather_copyout)."""
+    rm, ps = _co_checked(plan, rank_major, params)
+    return Call(lib.tide_allgather_copyout, (plan.handle, ctypes.c_void_p(rm or None), _ptr_array(ps)),
+                (plan, rank_major, params))
+
+
+def allgather_copyout(plan, rank_major, params, stream=None):
+    """All-gather copy-out: rank_major (bf16, W*S elements) -> params[p]
+    (bf16, plan.shapes[p])."""
+    rm, ps = _co_checked(plan, rank_major, params)
+    plan.allgather_copyout_raw(rm, ps, _stream_handle(stream))
+
+
+def _ci_checked(plan, shards, rank_major):
     import torch
 
     W, P = plan.world, len(plan.shapes)
@@ -252,5 +288,19 @@ def allgather_copyin(plan, shards, rank_major, stream=None):
             _require(shards[r][p], dtype, plan.n_real[r][p], f"shards[{r}][{p}]")
             ptrs.append(shards[r][p].data_ptr())
     _require(rank_major, torch.bfloat16, W * plan.shard_elems, "rank_major")
-    plan.allgather_copyin_raw(ptrs, DTYPE_F32 if dtype == torch.float32 else DTYPE_BF16, rank_major.data_ptr(),
-                              _stream_handle(stream))
+    return ptrs, DTYPE_F32 if dtype == torch.float32 else DTYPE_BF16, rank_major.data_ptr()
+
+
+def allgather_copyin_call(plan, shards, rank_major):
+    """A registered copy-in (see allgather_copyin)."""
+    ptrs, dt, rm = _ci_checked(plan, shards, rank_major)
+    return Call(lib.tide_allgather_copyin, (plan.handle, _ptr_array(ptrs), dt, ctypes.c_void_p(rm or None)),
+                (plan, shards, rank_major))
+
+
+def allgather_copyin(plan, shards, rank_major, stream=None):
+    """All-gather copy-in: shards[r][p] (rank r's local shard of parameter p,
+    n_real(p, r) elements, all float32 or all bfloat16) -> rank_major (bf16,
+    W*S elements; fp32 shards are cast by round to nearest even)."""
+    ptrs, dt, rm = _ci_checked(plan, shards, rank_major)
+    plan.allgather_copyin_raw(ptrs, dt, rm, _stream_handle(stream))

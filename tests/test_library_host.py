@@ -238,6 +238,7 @@ def test_options_round_trip_and_validation(tide):
     plan.set_options()
     assert plan.options(0) == {"cu_budget": 0, "wg_per_cu": 1, "chunk_elems": 1024, "flags": 0}
     assert plan.options(1) == {"cu_budget": 0, "wg_per_cu": 1, "chunk_elems": 4096, "flags": 0}
+    assert plan.options(2) == {"cu_budget": 0, "wg_per_cu": 2, "chunk_elems": 2048, "flags": 0}
 
 
 def test_too_many_chunks_is_a_range_error(tide):
