@@ -18,6 +18,12 @@ bytes read plus written by both kernels divided by the step time, with
   * a CU-budget sweep (grid-limited budgets, as the workgroup budget of the
     pages' short-lived sum kernels);
   * a plain device-to-device copy of the copy-out's byte count, for context;
+  * Equation 5's epilogue (alpha = 1/W, accumulate into the shards) and the
+    reduce-scatter from fp32 gradients, per kernel;
+  * the stock path A/B: W stock gradient packs (slice, zero-pad, widen, pack
+    rank-major into W*S fp32 per rank) followed by the fp32 reduce-scatter
+    of the packed buffers, against the layout-aware reduce-scatter that
+    replaces both (same shards, bit for bit, checked in the run);
   * the CPU oracle timed on the host's cores on the same workload.
 Algorithmic bytes: reduce-scatter 2*W*sum(D*K) read + 4*W*S written (padding
 is written, never read); copy-out 2*sum(D*K) read + 2*sum(D*K) written.
@@ -247,6 +253,59 @@ def main(argv=None):
     d2d = {"bytes": co_bytes, "avg_ms": round(d2d_ms, 5), "gbps": round(co_bytes / d2d_ms / 1e6, 1)}
     del src, dst
 
+    def timed(fn, n=10):
+        fn()
+        e = [(ev(), ev()) for _ in range(n)]
+        for a, b in e:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        stream.synchronize()
+        return [a.elapsed_time(b) for a, b in e]
+
+    # Equation 5's epilogue: alpha = 1/W, accumulating into separate shards
+    # (the timed outputs stay as they are for the parity check below); the
+    # shards are read as well: 4*W*S more bytes
+    with torch.cuda.stream(stream):
+        acc_outs = [torch.zeros(S, dtype=torch.float32, device="cuda") for _ in range(W)]
+    acc_call = tide.reduce_scatter_call(plan, grads, acc_outs, alpha=1.0 / W, accumulate=True)
+    kernels["rs_local_alpha_accumulate"] = kstats(timed(lambda: acc_call(stream)), rs_bytes + 4 * W * S)
+    del acc_outs, acc_call
+
+    # stock path A/B
+    pack_plan = tide.Plan(W, [(W, S)], **opts)
+    with torch.cuda.stream(stream):
+        packed = [torch.empty(W * S, dtype=torch.float32, device="cuda") for _ in range(W)]
+        stock_outs = [torch.empty(S, dtype=torch.float32, device="cuda") for _ in range(W)]
+    pack_calls = [tide.stock_chunk_cat_call(plan, grads[u], packed[u]) for u in range(W)]
+    red_call = tide.reduce_scatter_call(pack_plan, [[t.view(W, S)] for t in packed], stock_outs)
+    pack_bytes = W * (2 * sum_dk + 4 * W * S)  # every rank: its gradients read, W*S fp32 written
+    red_bytes = 4 * W * W * S + 4 * W * S      # W packed buffers read, W shards written
+    marks_ab = [(ev(), ev(), ev()) for _ in range(10)]
+    for c in pack_calls:
+        c(stream)
+    red_call(stream)
+    for a, b, c_ in marks_ab:
+        a.record(stream)
+        for c in pack_calls:
+            c(stream)
+        b.record(stream)
+        red_call(stream)
+        c_.record(stream)
+    stream.synchronize()
+    pk_ms = [a.elapsed_time(b) for a, b, _ in marks_ab]
+    rd_ms = [b.elapsed_time(c_) for _, b, c_ in marks_ab]
+    kernels["stock_pack_xW"] = kstats(pk_ms, pack_bytes)
+    kernels["rs_local_f32_packed"] = kstats(rd_ms, red_bytes)
+    same = all(torch.equal(stock_outs[r].view(torch.int32), outs[r].view(torch.int32)) for r in range(W))
+    stock_ms = kernels["stock_pack_xW"]["avg_ms"] + kernels["rs_local_f32_packed"]["avg_ms"]
+    stock_ab = {"stock_ms": round(stock_ms, 5), "layout_aware_ms": kernels["rs_local"]["avg_ms"],
+                "speedup": round(stock_ms / kernels["rs_local"]["avg_ms"], 3),
+                "stock_hbm_bytes": pack_bytes + red_bytes, "layout_aware_hbm_bytes": rs_bytes,
+                "extra_hbm_bytes": pack_bytes + red_bytes - rs_bytes, "extra_buffer_bytes": 4 * W * W * S,
+                "shards": "bit-identical" if same else "MISMATCH"}
+    del packed, stock_outs, pack_calls, red_call, pack_plan
+
     # CPU oracle on the same workload, and a bitwise check of this run's outputs
     cpu = None
     parity = None
@@ -308,9 +367,10 @@ def main(argv=None):
         "cu_sweep": sweep,
         "d2d_copy": d2d,
         "parity": parity,
+        "stock_ab": stock_ab,
     }
     print(json.dumps(line), flush=True)
-    if parity and "MISMATCH" in parity.values():
+    if (parity and "MISMATCH" in parity.values()) or stock_ab["shards"] != "bit-identical":
         return 3
     return 0
 

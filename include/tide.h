@@ -2,14 +2,15 @@
  * tide.h -- C ABI of the layout-aware FSDP2 collective local stages on one
  * MI355X (gfx950) GPU.
  *
- * Three operations, after "The Endgame of FSDP Communication: Layout-Aware
+ * Operations, after "The Endgame of FSDP Communication: Layout-Aware
  * Collectives on Copy Engines, RDMA, and NVSwitch" (Wang et al.):
  *
  *   reduce-scatter local stage (Section 4, Equation 5; Section 4.1): W ranks'
- *     per-parameter bf16 gradients, all resident in this GPU's memory, are
- *     summed into W packed per-rank fp32 shards.  The dimension-0 shard
- *     placement of Section 2.1 is folded into the addressing: no packed
- *     intermediate buffer (Equation 3) is formed.
+ *     per-parameter bf16 (or fp32) gradients, all resident in this GPU's
+ *     memory, are summed into W packed per-rank fp32 shards, then scaled and
+ *     optionally accumulated (Equation 5).  The dimension-0 shard placement
+ *     of Section 2.1 is folded into the addressing: no packed intermediate
+ *     buffer (Equation 3) is formed.
  *
  *   all-gather copy-out (Section 2.1): a flat rank-major bf16 buffer is
  *     scattered into per-parameter tensors.
@@ -17,6 +18,11 @@
  *   all-gather copy-in (Section 2.1, with the cast of Section 3.1): every
  *     rank's local fp32 (or bf16) shards are packed into the rank-major bf16
  *     buffer the all-gather would produce; the inverse of the copy-out.
+ *
+ *   stock gradient pack (Section 2.1, Equation 3): the step that the layout-
+ *     aware reduce-scatter removes, provided as the baseline: one rank's bf16
+ *     gradients are sliced, zero-padded, widened and packed rank-major into
+ *     the fp32 buffer a stock reduce-scatter reads.
  *
  * Shard geometry (Section 2.1), in ELEMENTS.  Parameter p has shape
  * (d_0, ..., d_{m-1}), m >= 1, viewed as D_p = d_0 rows of K_p = d_1*...*d_{m-1}
@@ -62,10 +68,10 @@ typedef enum {
     TIDE_ERR_ALIGN = -3,       /* a pointer is not aligned to its element size */
     TIDE_ERR_NOMEM = -4,       /* host, pinned or device allocation failed */
     TIDE_ERR_HIP = -5,         /* a HIP runtime call failed (its text is in tide_last_error) */
-    TIDE_ERR_UNSUPPORTED = -6  /* alpha != 1 or accumulate != 0: not provided */
+    TIDE_ERR_UNSUPPORTED = -6  /* reserved: no current call returns it */
 } tide_status;
 
-/* Element types of the copy-in's shards. */
+/* Element types (the copy-in's shard_dtype). */
 #define TIDE_DTYPE_BF16 0
 #define TIDE_DTYPE_F32 1
 
@@ -86,10 +92,11 @@ typedef enum {
  *               device's CU count.  Workgroups are dispatched round-robin over
  *               the 8 XCDs, so a budget is a grid size, not a CU mask.
  *   wg_per_cu   workgroups (256 threads, four waves) per budgeted CU;
- *               default 1 (reduce-scatter, copy-out), 2 (copy-in).
+ *               default 1 (reduce-scatter, copy-out), 2 (copy-in, stock
+ *               pack).
  *   chunk_elems elements per chunk (the unit a wave takes), a multiple of 8,
  *               at most 2^28; default 1024 (reduce-scatter), 4096 (copy-out),
- *               2048 (copy-in).
+ *               2048 (copy-in, stock pack).
  *               A plan may have at most 2^31 - 1 chunks per operation.
  *   flags       TIDE_FLAG_* bits.
  */
@@ -112,7 +119,7 @@ typedef struct tide_plan tide_plan; /* opaque, owned by the library */
  *   opt        launch knobs, or NULL for defaults
  *   out_plan   receives the plan
  * Host only: no device call is made.  The plan's device tables are allocated
- * and uploaded by the first reduce-scatter or copy-out call that uses it, on
+ * and uploaded by the first data-moving call that uses it, on
  * the device current at that time (that first call blocks the host for the
  * allocation); the plan is bound to that device afterwards.
  * Errors: TIDE_ERR_INVALID (bad counts, shapes, options, null pointers),
@@ -133,17 +140,18 @@ tide_status tide_plan_layout(const tide_plan* plan, int64_t* rows_per_rank, int6
 
 /*
  * The plan's work segments, for inspection and tests.  op 0 = reduce-scatter,
- * 1 = copy-out, 2 = copy-in.  Each segment is 6 int64 values:
+ * 1 = copy-out, 2 = copy-in, 3 = stock pack.  Each segment is 6 int64 values:
  *   kind     0 = sum of the W ranks' sources, 1 = zero fill (padding),
- *            2 = copy (the copy-in casts instead when its shards are fp32)
- *   src_idx  reduce-scatter: parameter p; copy-out: 0 (the rank-major buffer);
- *            copy-in: shard index r*P + p
+ *            2 = copy (the copy-in casts instead when its shards are fp32;
+ *            the stock pack widens bf16 to fp32)
+ *   src_idx  reduce-scatter, stock pack: parameter p; copy-out: 0 (the
+ *            rank-major buffer); copy-in: shard index r*P + p
  *   dst_idx  reduce-scatter: destination rank r; copy-out: parameter p;
- *            copy-in: 0 (the rank-major buffer)
+ *            copy-in, stock pack: 0 (the rank-major buffer)
  *   src_off  element offset in each source tensor (in the rank-major buffer
  *            for the copy-out)
  *   dst_off  element offset in the destination tensor (in the rank-major
- *            buffer for the copy-in)
+ *            buffer for the copy-in and the stock pack)
  *   len      elements (> 0)
  * Writes min(capacity, count) segments to `table` (may be NULL when
  * capacity is 0) and the total count to *count.
@@ -155,9 +163,9 @@ tide_status tide_plan_segments(const tide_plan* plan, int32_t op, int64_t* table
  * Errors: TIDE_ERR_INVALID, TIDE_ERR_RANGE (too many chunks). */
 tide_status tide_plan_set_options(tide_plan* plan, const tide_options* opt);
 
-/* The launch knobs in effect for op 0 (reduce-scatter), 1 (copy-out) or 2 (copy-in), with
- * defaults resolved (cu_budget is resolved once the plan is bound to a
- * device, 0 before). */
+/* The launch knobs in effect for op 0 (reduce-scatter), 1 (copy-out),
+ * 2 (copy-in) or 3 (stock pack), with defaults resolved (cu_budget is
+ * resolved once the plan is bound to a device, 0 before). */
 tide_status tide_plan_get_options(const tide_plan* plan, int32_t op, tide_options* out);
 
 /*
@@ -167,21 +175,39 @@ tide_status tide_plan_get_options(const tide_plan* plan, int32_t op, tide_option
  *           aligned.  May be NULL only where D_p*K_p = 0.
  *   out     [W] host array of device pointers; out[r] receives rank r's
  *           packed fp32 shard: S elements, 4-byte aligned, written in full.
- *   alpha, accumulate
- *           Equation 5's scale and accumulate flag.  Only alpha = 1.0f and
- *           accumulate = 0 are provided (else TIDE_ERR_UNSUPPORTED).
- * For r in [0, W), p in [0, P), e in [0, n_p):
- *   out[r][o_p + e] = g_0 + g_1 + ... + g_{W-1}   for e < n_real(p, r),
- *                     with g_u = grads[u*P+p][r R_p K_p + e] widened exactly
- *                     to fp32, added left to right (rank order 0..W-1) in
- *                     IEEE binary32, round to nearest even, subnormals kept;
- *   out[r][o_p + e] = +0.0f                        for padding (e >= n_real).
+ *   alpha   Equation 5's scale (any value; 1.0f leaves the sum unchanged).
+ *   accumulate
+ *           0: the shards are overwritten; 1: the result is added to the
+ *           values already in out[r] (which are then read), Equation 5's
+ *           accumulate.  Other values: TIDE_ERR_INVALID.
+ * For r in [0, W), p in [0, P), e in [0, n_p), with
+ *   s = g_0 + g_1 + ... + g_{W-1}   for e < n_real(p, r),
+ *       g_u = grads[u*P+p][r R_p K_p + e] widened exactly to fp32, added left
+ *       to right (rank order 0..W-1) in IEEE binary32, round to nearest even,
+ *       subnormals kept, no fused operations;
+ *   s = +0.0f                       for padding (e >= n_real: every rank's
+ *       padding rows are zeros);
+ *   out[r][o_p + e] = s                       (alpha = 1, accumulate = 0)
+ *   out[r][o_p + e] = alpha * s               (accumulate = 0)
+ *   out[r][o_p + e] = old + alpha * s         (accumulate = 1)
+ * each operation one binary32 rounding.  With alpha = 1 and accumulate = 0
+ * the product is skipped (it is exact anyway).
  * The result is bit-identical for every tide_options setting.
- * Errors: TIDE_ERR_INVALID (null plan/arrays/pointers), TIDE_ERR_ALIGN,
- * TIDE_ERR_UNSUPPORTED, TIDE_ERR_NOMEM, TIDE_ERR_HIP.
+ * Errors: TIDE_ERR_INVALID (null plan/arrays/pointers, accumulate not 0/1),
+ * TIDE_ERR_ALIGN, TIDE_ERR_NOMEM, TIDE_ERR_HIP.
  */
 tide_status tide_reduce_scatter_local(tide_plan* plan, const uint16_t* const* grads, float* const* out,
                                       float alpha, int32_t accumulate, void* stream);
+
+/*
+ * Reduce-scatter local stage from fp32 gradients (Section 4; the fp32
+ * reduce-scatter of Section 4.3): as tide_reduce_scatter_local with
+ * grads[u*P + p] fp32 (4-byte aligned) and g_u its value as it is.  With a
+ * plan of one parameter of shape (W, S) this is also the reduce-scatter of
+ * W ranks' pre-packed fp32 buffers (the stock path after its pack).
+ */
+tide_status tide_reduce_scatter_local_f32(tide_plan* plan, const float* const* grads, float* const* out,
+                                          float alpha, int32_t accumulate, void* stream);
 
 /*
  * All-gather copy-out (Section 2.1).
@@ -217,6 +243,24 @@ tide_status tide_allgather_copyout(tide_plan* plan, const uint16_t* rank_major, 
  */
 tide_status tide_allgather_copyin(tide_plan* plan, const void* const* shards, int32_t shard_dtype,
                                   uint16_t* rank_major, void* stream);
+
+/*
+ * Stock gradient pack of one rank (Section 2.1, Equation 3): what stock FSDP2
+ * does before its reduce-scatter, kept as the baseline of the layout-aware
+ * reduce-scatter above.
+ *   grads   [P] host array of device pointers: this rank's bf16 gradients,
+ *           grads[p] holding D_p*K_p elements, 2-byte aligned.  May be NULL
+ *           only where D_p*K_p = 0.
+ *   packed  device pointer to W*S fp32 elements, 4-byte aligned, written in
+ *           full: for every p, r and e < n_p,
+ *             packed[r S + o_p + e] = grads[p][r R_p K_p + e] widened exactly
+ *                                     (e < n_real(p, r)),  +0.0f otherwise.
+ * The W ranks' packed buffers, reduce-scattered with
+ * tide_reduce_scatter_local_f32 on a (W, S) plan, give exactly the shards
+ * tide_reduce_scatter_local gives (same additions in the same order).
+ * Errors: TIDE_ERR_INVALID, TIDE_ERR_ALIGN, TIDE_ERR_NOMEM, TIDE_ERR_HIP.
+ */
+tide_status tide_stock_chunk_cat(tide_plan* plan, const uint16_t* const* grads, float* packed, void* stream);
 
 /* Free a plan and its device tables (waits for the device to finish using
  * them).  NULL is accepted. */

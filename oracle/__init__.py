@@ -13,6 +13,10 @@ Collectives on Copy Engines, RDMA, and NVSwitch", Wang et al.):
   * ``copyout``  -- Section 2.1, rank-major all-gather output to per-parameter
                     storage;
   * ``pack``     -- Section 2.1, the inverse (FSDP2's copy-in), padding zero;
+  * ``rs_local_ex`` -- Section 4, Equation 5 in full: alpha, accumulate,
+                    bf16 or fp32 gradients;
+  * ``chunk_cat`` -- Section 2.1, Equation 3: stock FSDP2's packed fp32
+                    reduce-scatter input of one rank (the baseline);
   * ``copyin``   -- Sections 2.1 and 3.1: every rank's local shards (fp32 cast
                     to bf16 by round to nearest even, or bf16 as is) into the
                     rank-major buffer, padding zero.
@@ -47,6 +51,10 @@ def _bind(lib):
     lib.oracle_copyin.restype = ctypes.c_int
     lib.oracle_cast_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
     lib.oracle_cast_bf16.restype = ctypes.c_int
+    lib.oracle_rs_local_ex.argtypes = [i32, i32, i32p, i64p, vpp, i32, ctypes.c_float, i32, vpp, i32]
+    lib.oracle_rs_local_ex.restype = ctypes.c_int
+    lib.oracle_chunk_cat.argtypes = [i32, i32, i32p, i64p, vpp, ctypes.c_void_p, i32]
+    lib.oracle_chunk_cat.restype = ctypes.c_int
     return lib
 
 
@@ -182,6 +190,51 @@ class Oracle:
         _check(rc, "oracle_copyin")
         return rm[: world * geo["S"]]
 
+    def rs_local_ex(self, world, shapes, grads, alpha=1.0, accumulate=False, out=None, nthreads=1):
+        """Equation 5 in full: grads[u][p] all uint16 (bf16 bits) or all
+        float32; out (W float32 arrays of S, read when accumulating) is
+        updated in place and returned (new arrays when None)."""
+        geo = self.plan(world, shapes)
+        P = len(shapes)
+        if len(grads) != world or any(len(g) != P for g in grads):
+            raise ValueError("grads must be indexed [rank][parameter]")
+        dtypes = {np.asarray(a).dtype for row in grads for a in row}
+        if dtypes not in ({np.dtype(np.float32)}, {np.dtype(np.uint16)}):
+            raise TypeError(f"grads must be all float32 or all uint16, got {dtypes}")
+        f32 = dtypes == {np.dtype(np.float32)}
+        flat = []
+        for u in range(world):
+            for p in range(P):
+                a = np.ascontiguousarray(grads[u][p]).reshape(-1)
+                if a.size != geo["D"][p] * geo["K"][p]:
+                    raise ValueError(f"grads[{u}][{p}] has {a.size} elements")
+                flat.append(a if a.size else np.zeros(1, dtype=a.dtype))
+        if out is None:
+            out = [np.zeros(max(geo["S"], 1), dtype=np.float32) for _ in range(world)]
+        else:
+            out = [np.ascontiguousarray(o, dtype=np.float32).copy() if o.size else np.zeros(1, np.float32)
+                   for o in out]
+        ndims, dims = _shape_args(shapes)
+        rc = self.lib.oracle_rs_local_ex(world, P, _i32p(ndims), _i64p(dims), _ptrs(flat), 1 if f32 else 0,
+                                         float(alpha), int(bool(accumulate)), _ptrs(out), int(nthreads))
+        _check(rc, "oracle_rs_local_ex")
+        return [o[: geo["S"]] for o in out]
+
+    def chunk_cat(self, world, shapes, grads_u, nthreads=1):
+        """Stock FSDP2 packing of one rank's bf16 gradients grads_u[p] ->
+        float32 array of W*S."""
+        geo = self.plan(world, shapes)
+        flat = []
+        for p in range(len(shapes)):
+            a = _as_u16(grads_u[p], int(geo["D"][p] * geo["K"][p]), f"grads_u[{p}]")
+            flat.append(a if a.size else np.zeros(1, dtype=np.uint16))
+        packed = np.empty(max(world * geo["S"], 1), dtype=np.float32)
+        ndims, dims = _shape_args(shapes)
+        rc = self.lib.oracle_chunk_cat(world, len(shapes), _i32p(ndims), _i64p(dims), _ptrs(flat),
+                                       packed.ctypes.data, int(nthreads))
+        _check(rc, "oracle_chunk_cat")
+        return packed[: world * geo["S"]]
+
     def cast_bf16(self, x):
         """float32 array -> bf16 bits (uint16), the copy-in's cast."""
         x = np.ascontiguousarray(x, dtype=np.float32).reshape(-1)
@@ -222,3 +275,11 @@ def copyin(world, shapes, shards, nthreads=1):
 
 def cast_bf16(x):
     return _get().cast_bf16(x)
+
+
+def rs_local_ex(world, shapes, grads, alpha=1.0, accumulate=False, out=None, nthreads=1):
+    return _get().rs_local_ex(world, shapes, grads, alpha, accumulate, out, nthreads)
+
+
+def chunk_cat(world, shapes, grads_u, nthreads=1):
+    return _get().chunk_cat(world, shapes, grads_u, nthreads)

@@ -29,6 +29,10 @@
  *     subnormals kept, no fused operations;
  *   - alpha = 1 and accumulate = 0 (Equation 5's defaults): the finished sum
  *     is stored as is, with no added +0;
+ *   - otherwise alpha scales the finished fp32 sum once (one binary32
+ *     multiplication) and accumulate adds the scaled sum to the existing
+ *     output (one binary32 addition); padding rows count as rows of zeros;
+ *   - fp32 gradients are taken as is (no widening);
  *   - output elements of padding rows (rows at or past D_p) are +0.0f;
  *   - the copy-out writes the unpadded per-parameter tensor of D_p * K_p
  *     elements and never reads the padding of a shard;
@@ -224,6 +228,12 @@ typedef struct {
     const geometry* g;
     const void* const* shards;    /* [W*P], index r*P + p */
     int32_t shard_dtype;          /* 0 = bf16 bits, 1 = fp32 */
+    const void* const* grads_any; /* [W*P], index u*P + p, bf16 bits or fp32 */
+    int32_t grad_dtype;           /* 0 = bf16, 1 = fp32 */
+    float alpha;
+    int32_t accumulate;
+    const uint16_t* const* grads_one; /* [P]: one rank's gradients */
+    float* packed;                /* [W*S] */
     const uint16_t* const* grads; /* [W*P], index u*P + p */
     float* const* out;            /* [W] */
     const uint16_t* rank_major;   /* [W*S] */
@@ -255,6 +265,51 @@ static void rs_task(const job* j, int32_t r, int32_t p) {
             dst[e] = 0.0f;
         }
     }
+}
+
+/* Contribution of rank u to element i of parameter p, widened to fp32 (an
+ * fp32 gradient is taken as is). */
+static float grad_value(const job* j, int32_t u, int32_t p, int64_t i) {
+    const void* t = j->grads_any[(int64_t)u * j->g->P + p];
+    if (j->grad_dtype == 1) return ((const float*)t)[i];
+    return bf16_to_f32(((const uint16_t*)t)[i]);
+}
+
+/*
+ * Reduce-scatter in the general form of Equation 5, one task (r, p):
+ *   out_r[o_p + e] <- (accumulate ? out_r[o_p + e] : 0) + alpha * sum_u g_u
+ * with the sum taken in rank order as in rs_task, alpha applied once to the
+ * finished fp32 sum (one binary32 multiplication), and the accumulation one
+ * binary32 addition; with accumulate off the scaled sum is stored as is.
+ * Padding rows are rows of zeros in every rank (Section 2.1), so their sum
+ * is +0.  rs_task is the alpha = 1, accumulate off, bf16 case on its own.
+ */
+static void rs_general_task(const job* j, int32_t r, int32_t p) {
+    const geometry* g = j->g;
+    int64_t real = real_rows(g, p, r) * g->K[p];
+    int64_t first = (int64_t)r * g->R[p] * g->K[p];
+    float* dst = j->out[r] + g->o[p];
+    for (int64_t e = 0; e < g->n[p]; ++e) {
+        float sum = 0.0f;
+        if (e < real) {
+            sum = grad_value(j, 0, p, first + e);
+            for (int32_t u = 1; u < g->W; ++u) sum = sum + grad_value(j, u, p, first + e);
+        }
+        float v = j->alpha * sum;
+        dst[e] = j->accumulate ? dst[e] + v : v;
+    }
+}
+
+/* Stock FSDP2's gradient packing for one source rank (Section 2.1, Equation
+ * 3: slice, zero-pad, upcast, pack): rank u's bf16 gradient rows that
+ * destination r owns go, widened to fp32, to packed[r S + o_p + e]; padding
+ * rows are +0.0f. */
+static void chunk_cat_task(const job* j, int32_t r, int32_t p) {
+    const geometry* g = j->g;
+    int64_t real = real_rows(g, p, r) * g->K[p];
+    const uint16_t* src = j->grads_one[p] + (int64_t)r * g->R[p] * g->K[p];
+    float* dst = j->packed + (int64_t)r * g->S + g->o[p];
+    for (int64_t e = 0; e < g->n[p]; ++e) dst[e] = (e < real) ? bf16_to_f32(src[e]) : 0.0f;
 }
 
 /* Copy-out, one task: rank r's shard of parameter p lands in the parameter's
@@ -475,4 +530,59 @@ int oracle_cast_bf16(const float* x, int64_t n, uint16_t* out) {
     for (int64_t i = 0; i < n; ++i) out[i] = f32_to_bf16_rne(x[i]);
     ieee_mode_leave(saved);
     return ORACLE_OK;
+}
+
+/*
+ * oracle_rs_local_ex: Equation 5 in full.
+ *   grads       [W*P]  bf16 bits (grad_dtype 0) or fp32 (grad_dtype 1),
+ *                      grads[u*P + p] of D_p * K_p elements
+ *   alpha       scale of the finished sum
+ *   accumulate  0: out is written; 1: the scaled sum is added to out
+ *   out         [W]    S fp32 elements each (read when accumulating)
+ */
+int oracle_rs_local_ex(int32_t W, int32_t P, const int32_t* ndims, const int64_t* dims, const void* const* grads,
+                       int32_t grad_dtype, float alpha, int32_t accumulate, float* const* out, int32_t nthreads) {
+    geometry g;
+    int rc = geometry_build(W, P, ndims, dims, &g);
+    if (rc != ORACLE_OK) return rc;
+    if (grads == NULL || out == NULL || (grad_dtype != 0 && grad_dtype != 1)) {
+        geometry_free(&g);
+        return ORACLE_INVALID;
+    }
+    job j;
+    memset(&j, 0, sizeof j);
+    j.g = &g;
+    j.grads_any = grads;
+    j.grad_dtype = grad_dtype;
+    j.alpha = alpha;
+    j.accumulate = accumulate != 0;
+    j.out = out;
+    rc = run_tasks(j, rs_general_task, nthreads);
+    geometry_free(&g);
+    return rc;
+}
+
+/*
+ * oracle_chunk_cat: stock FSDP2's packed fp32 reduce-scatter input of one
+ * source rank.
+ *   grads   [P]    that rank's bf16 gradients, D_p * K_p elements each
+ *   packed  [W*S]  written in full
+ */
+int oracle_chunk_cat(int32_t W, int32_t P, const int32_t* ndims, const int64_t* dims, const uint16_t* const* grads,
+                     float* packed, int32_t nthreads) {
+    geometry g;
+    int rc = geometry_build(W, P, ndims, dims, &g);
+    if (rc != ORACLE_OK) return rc;
+    if (grads == NULL || packed == NULL) {
+        geometry_free(&g);
+        return ORACLE_INVALID;
+    }
+    job j;
+    memset(&j, 0, sizeof j);
+    j.g = &g;
+    j.grads_one = grads;
+    j.packed = packed;
+    rc = run_tasks(j, chunk_cat_task, nthreads);
+    geometry_free(&g);
+    return rc;
 }

@@ -1,9 +1,11 @@
 """Layout-aware FSDP2 collective local stages on MI355X (gfx950).
 
   Plan                   host shard-layout plan (dimension-0 shards, padding)
-  reduce_scatter_local   W ranks' bf16 gradients -> W packed fp32 shards
+  reduce_scatter_local   W ranks' bf16 (or fp32) gradients -> W packed fp32
+                         shards (with Equation 5's alpha and accumulate)
   allgather_copyout      rank-major bf16 buffer -> per-parameter tensors
   allgather_copyin       every rank's fp32/bf16 shards -> rank-major bf16 buffer
+  stock_chunk_cat        stock FSDP2's gradient pack of one rank (the baseline)
 
 The *_call variants check and marshal the tensors once and return a callable
 that launches with one library call (for buffers reused every step).
@@ -25,4 +27,6 @@ from .tide import (  # noqa: F401
     allgather_copyout_call,
     reduce_scatter_call,
     reduce_scatter_local,
+    stock_chunk_cat,
+    stock_chunk_cat_call,
 )

@@ -70,7 +70,7 @@ struct tide_plan {
   uint64_t magic = 0;
   tide::Geometry geo;
   tide_options given{};  // as passed (0 = default)
-  OpState rs, co, ci;
+  OpState rs, co, ci, pk;
   int device = -1;
   int cu_count = 0;
 };
@@ -89,20 +89,31 @@ bool live(const tide_plan* p) {
 
 int32_t nsrc_of(const tide_plan* p, tide::Op op) { return op == tide::kOpRs ? p->geo.world : 1; }
 
-OpState& op_state(tide_plan* p, tide::Op op) { return op == tide::kOpRs ? p->rs : op == tide::kOpCo ? p->co : p->ci; }
+OpState& op_state(tide_plan* p, tide::Op op) {
+  switch (op) {
+    case tide::kOpRs: return p->rs;
+    case tide::kOpCo: return p->co;
+    case tide::kOpCi: return p->ci;
+    default: return p->pk;
+  }
+}
+const OpState& op_state(const tide_plan* p, tide::Op op) { return op_state(const_cast<tide_plan*>(p), op); }
+
+const tide::Op kOps[tide::kNumOps] = {tide::kOpRs, tide::kOpCo, tide::kOpCi, tide::kOpPack};
+
+const char* const kOpNames = "0 (reduce-scatter), 1 (copy-out), 2 (copy-in) or 3 (stock pack)";
 
 tide_status rebuild_chunks(tide_plan* p, const tide_options& given) {
   std::string why;
-  std::vector<int32_t> cb[3];
-  const tide::Op ops[3] = {tide::kOpRs, tide::kOpCo, tide::kOpCi};
-  for (int i = 0; i < 3; ++i) {
-    const tide_options eff = tide::effective_options(given, ops[i], 0);
-    tide_status st = tide::chunk_table(op_state(p, ops[i]).segs, eff.chunk_elems, &cb[i], &why);
+  std::vector<int32_t> cb[tide::kNumOps];
+  for (int i = 0; i < tide::kNumOps; ++i) {
+    const tide_options eff = tide::effective_options(given, kOps[i], 0);
+    tide_status st = tide::chunk_table(op_state(p, kOps[i]).segs, eff.chunk_elems, &cb[i], &why);
     if (st != TIDE_OK) return fail(st, why);
   }
-  for (int i = 0; i < 3; ++i) {
-    op_state(p, ops[i]).chunk_begin.swap(cb[i]);
-    op_state(p, ops[i]).chunks_stale = true;
+  for (int i = 0; i < tide::kNumOps; ++i) {
+    op_state(p, kOps[i]).chunk_begin.swap(cb[i]);
+    op_state(p, kOps[i]).chunks_stale = true;
   }
   return TIDE_OK;
 }
@@ -173,9 +184,7 @@ void release_device(tide_plan* p) {
   int prev = -1;
   (void)hipGetDevice(&prev);
   (void)hipSetDevice(p->device);
-  release_op(&p->rs);
-  release_op(&p->co);
-  release_op(&p->ci);
+  for (tide::Op op : kOps) release_op(&op_state(p, op));
   p->device = -1;
   if (prev >= 0) (void)hipSetDevice(prev);
 }
@@ -206,9 +215,9 @@ tide_status bind_device(tide_plan* p) {
   if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
   p->device = dev;
   p->cu_count = cus;
-  tide_status st = alloc_op(&p->rs, p->geo.world);
-  if (st == TIDE_OK) st = alloc_op(&p->co, 1);
-  if (st == TIDE_OK) st = alloc_op(&p->ci, 1);
+  tide_status st = TIDE_OK;
+  for (tide::Op op : kOps)
+    if (st == TIDE_OK) st = alloc_op(&op_state(p, op), nsrc_of(p, op));
   if (st != TIDE_OK) {
     const std::string why = g_last_error;
     release_device(p);
@@ -217,10 +226,12 @@ tide_status bind_device(tide_plan* p) {
   return TIDE_OK;
 }
 
-// Upload what is stale, then launch.
+// Upload what is stale, then launch.  `f32`: the reduce-scatter's gradients
+// or the copy-in's shards are fp32.  `alpha`, `accumulate`: the
+// reduce-scatter's Equation 5 terms.
 template <typename BuildCall>
 tide_status run_op(tide_plan* p, tide::Op op, const std::vector<const void*>& key, BuildCall build,
-                   hipStream_t stream, bool f32 = false) {
+                   hipStream_t stream, bool f32 = false, float alpha = 1.0f, int32_t accumulate = 0) {
   OpState& s = op_state(p, op);
   const int32_t nchunks = s.chunk_begin.back();
   if (nchunks == 0) return TIDE_OK;  // nothing to write
@@ -259,14 +270,67 @@ tide_status run_op(tide_plan* p, tide::Op op, const std::vector<const void*>& ke
   a.nchunks = nchunks;
   a.chunk = int32_t(eff.chunk_elems);
   a.flags = eff.flags;
-  const int rc = op == tide::kOpRs   ? tide::launch_rs_local(a, grid, stream)
-                 : op == tide::kOpCo ? tide::launch_ag_copyout(a, grid, stream)
-                                     : tide::launch_ag_copyin(a, f32, grid, stream);
-  if (rc != 0)
-    return hip_fail(hipError_t(rc), op == tide::kOpRs   ? "rs_local_kernel launch"
-                                    : op == tide::kOpCo ? "ag_copyout_kernel launch"
-                                                        : "ag_copyin_kernel launch");
+  a.alpha = alpha;
+  a.accumulate = accumulate;
+  int rc = 0;
+  const char* what = "";
+  switch (op) {
+    case tide::kOpRs:
+      rc = tide::launch_rs_local(a, f32, grid, stream);
+      what = "rs_local_kernel launch";
+      break;
+    case tide::kOpCo:
+      rc = tide::launch_ag_copyout(a, grid, stream);
+      what = "ag_copyout_kernel launch";
+      break;
+    case tide::kOpCi:
+      rc = tide::launch_ag_copyin(a, f32, grid, stream);
+      what = "ag_copyin_kernel launch";
+      break;
+    case tide::kOpPack:
+      rc = tide::launch_stock_pack(a, grid, stream);
+      what = "stock_pack_kernel launch";
+      break;
+  }
+  if (rc != 0) return hip_fail(hipError_t(rc), what);
   return TIDE_OK;
+}
+
+// Both reduce-scatter entry points: `grads` holds uint16_t (bf16) or float
+// pointers, as `f32` says.
+tide_status reduce_scatter(tide_plan* plan, const void* const* grads, bool f32, float* const* out, float alpha,
+                           int32_t accumulate, void* stream) {
+  g_last_error.clear();
+  if (!live(plan)) return fail(TIDE_ERR_INVALID, "unknown or destroyed plan");
+  if (grads == nullptr || out == nullptr) return fail(TIDE_ERR_INVALID, "grads and out must not be NULL");
+  if (accumulate != 0 && accumulate != 1) return fail(TIDE_ERR_INVALID, "accumulate must be 0 or 1");
+  const tide::Geometry& g = plan->geo;
+  const int64_t W = g.world, P = g.nparams;
+  const uintptr_t align = f32 ? 4 : 2;
+  for (int64_t u = 0; u < W; ++u) {
+    for (int64_t p = 0; p < P; ++p) {
+      const void* ptr = grads[u * P + p];
+      if (g.D[p] * g.K[p] == 0) continue;
+      if (ptr == nullptr) return fail(TIDE_ERR_INVALID, "grads[" + std::to_string(u * P + p) + "] is NULL");
+      if (reinterpret_cast<uintptr_t>(ptr) & (align - 1))
+        return fail(TIDE_ERR_ALIGN, "grads[" + std::to_string(u * P + p) + "] is not aligned to its element size");
+    }
+  }
+  for (int64_t r = 0; r < W; ++r) {
+    if (g.S == 0) continue;
+    if (out[r] == nullptr) return fail(TIDE_ERR_INVALID, "out[" + std::to_string(r) + "] is NULL");
+    if (reinterpret_cast<uintptr_t>(out[r]) & 3)
+      return fail(TIDE_ERR_ALIGN, "out[" + std::to_string(r) + "] is not 4-byte aligned");
+  }
+  std::vector<const void*> key(grads, grads + W * P);
+  key.insert(key.end(), out, out + W);
+  key.push_back(reinterpret_cast<const void*>(uintptr_t(f32)));
+  return run_op(
+      plan, tide::kOpRs, key,
+      [&](std::vector<tide::CallHdr>* hdr, std::vector<const void*>* ptrs) {
+        tide::rs_call_table(g, plan->rs.segs, grads, f32, out, hdr, ptrs);
+      },
+      static_cast<hipStream_t>(stream), f32, alpha, accumulate);
 }
 
 }  // namespace
@@ -293,14 +357,16 @@ tide_status tide_plan_create(int32_t world, int32_t nparams, const int32_t* ndim
     p->rs.segs = tide::rs_segments(p->geo);
     p->co.segs = tide::copyout_segments(p->geo);
     p->ci.segs = tide::copyin_segments(p->geo);
+    p->pk.segs = tide::pack_segments(p->geo);
   } catch (...) {
     delete p;
     return fail(TIDE_ERR_NOMEM, "out of host memory");
   }
-  if (p->rs.segs.size() >= size_t(INT32_MAX) || p->co.segs.size() >= size_t(INT32_MAX) ||
-      p->ci.segs.size() >= size_t(INT32_MAX)) {
-    delete p;
-    return fail(TIDE_ERR_RANGE, "too many segments");
+  for (tide::Op op : kOps) {
+    if (op_state(p, op).segs.size() >= size_t(INT32_MAX)) {
+      delete p;
+      return fail(TIDE_ERR_RANGE, "too many segments");
+    }
   }
   p->given = given;
   st = rebuild_chunks(p, given);
@@ -334,10 +400,10 @@ tide_status tide_plan_segments(const tide_plan* plan, int32_t op, int64_t* table
                                int64_t* count) {
   g_last_error.clear();
   if (!live(plan)) return fail(TIDE_ERR_INVALID, "unknown or destroyed plan");
-  if (op < 0 || op > 2) return fail(TIDE_ERR_INVALID, "op must be 0 (reduce-scatter), 1 (copy-out) or 2 (copy-in)");
+  if (op < 0 || op >= tide::kNumOps) return fail(TIDE_ERR_INVALID, std::string("op must be ") + kOpNames);
   if (count == nullptr || capacity < 0 || (capacity > 0 && table == nullptr))
     return fail(TIDE_ERR_INVALID, "bad table/capacity/count");
-  const std::vector<tide::Seg>& segs = op == 0 ? plan->rs.segs : op == 1 ? plan->co.segs : plan->ci.segs;
+  const std::vector<tide::Seg>& segs = op_state(plan, tide::Op(op)).segs;
   *count = int64_t(segs.size());
   const int64_t n = capacity < *count ? capacity : *count;
   for (int64_t i = 0; i < n; ++i) {
@@ -369,7 +435,7 @@ tide_status tide_plan_set_options(tide_plan* plan, const tide_options* opt) {
 tide_status tide_plan_get_options(const tide_plan* plan, int32_t op, tide_options* out) {
   g_last_error.clear();
   if (!live(plan)) return fail(TIDE_ERR_INVALID, "unknown or destroyed plan");
-  if (op < 0 || op > 2) return fail(TIDE_ERR_INVALID, "op must be 0 (reduce-scatter), 1 (copy-out) or 2 (copy-in)");
+  if (op < 0 || op >= tide::kNumOps) return fail(TIDE_ERR_INVALID, std::string("op must be ") + kOpNames);
   if (out == nullptr) return fail(TIDE_ERR_INVALID, "out must not be NULL");
   *out = tide::effective_options(plan->given, tide::Op(op), plan->cu_count);
   return TIDE_OK;
@@ -377,36 +443,12 @@ tide_status tide_plan_get_options(const tide_plan* plan, int32_t op, tide_option
 
 tide_status tide_reduce_scatter_local(tide_plan* plan, const uint16_t* const* grads, float* const* out,
                                       float alpha, int32_t accumulate, void* stream) {
-  g_last_error.clear();
-  if (!live(plan)) return fail(TIDE_ERR_INVALID, "unknown or destroyed plan");
-  if (grads == nullptr || out == nullptr) return fail(TIDE_ERR_INVALID, "grads and out must not be NULL");
-  if (!(alpha == 1.0f) || accumulate != 0)
-    return fail(TIDE_ERR_UNSUPPORTED, "only alpha = 1 and accumulate = 0 are provided");
-  const tide::Geometry& g = plan->geo;
-  const int64_t W = g.world, P = g.nparams;
-  for (int64_t u = 0; u < W; ++u) {
-    for (int64_t p = 0; p < P; ++p) {
-      const uint16_t* ptr = grads[u * P + p];
-      if (g.D[p] * g.K[p] == 0) continue;
-      if (ptr == nullptr) return fail(TIDE_ERR_INVALID, "grads[" + std::to_string(u * P + p) + "] is NULL");
-      if (reinterpret_cast<uintptr_t>(ptr) & 1)
-        return fail(TIDE_ERR_ALIGN, "grads[" + std::to_string(u * P + p) + "] is not 2-byte aligned");
-    }
-  }
-  for (int64_t r = 0; r < W; ++r) {
-    if (g.S == 0) continue;
-    if (out[r] == nullptr) return fail(TIDE_ERR_INVALID, "out[" + std::to_string(r) + "] is NULL");
-    if (reinterpret_cast<uintptr_t>(out[r]) & 3)
-      return fail(TIDE_ERR_ALIGN, "out[" + std::to_string(r) + "] is not 4-byte aligned");
-  }
-  std::vector<const void*> key(grads, grads + W * P);
-  key.insert(key.end(), out, out + W);
-  return run_op(
-      plan, tide::kOpRs, key,
-      [&](std::vector<tide::CallHdr>* hdr, std::vector<const void*>* ptrs) {
-        tide::rs_call_table(g, plan->rs.segs, grads, out, hdr, ptrs);
-      },
-      static_cast<hipStream_t>(stream));
+  return reduce_scatter(plan, reinterpret_cast<const void* const*>(grads), false, out, alpha, accumulate, stream);
+}
+
+tide_status tide_reduce_scatter_local_f32(tide_plan* plan, const float* const* grads, float* const* out,
+                                          float alpha, int32_t accumulate, void* stream) {
+  return reduce_scatter(plan, reinterpret_cast<const void* const*>(grads), true, out, alpha, accumulate, stream);
 }
 
 tide_status tide_allgather_copyout(tide_plan* plan, const uint16_t* rank_major, uint16_t* const* params,
@@ -467,6 +509,31 @@ tide_status tide_allgather_copyin(tide_plan* plan, const void* const* shards, in
         tide::ci_call_table(g, plan->ci.segs, shards, f32, rank_major, hdr, ptrs);
       },
       static_cast<hipStream_t>(stream), f32);
+}
+
+tide_status tide_stock_chunk_cat(tide_plan* plan, const uint16_t* const* grads, float* packed, void* stream) {
+  g_last_error.clear();
+  if (!live(plan)) return fail(TIDE_ERR_INVALID, "unknown or destroyed plan");
+  if (grads == nullptr) return fail(TIDE_ERR_INVALID, "grads must not be NULL");
+  const tide::Geometry& g = plan->geo;
+  const int64_t P = g.nparams;
+  for (int64_t p = 0; p < P; ++p) {
+    if (g.D[p] * g.K[p] == 0) continue;
+    if (grads[p] == nullptr) return fail(TIDE_ERR_INVALID, "grads[" + std::to_string(p) + "] is NULL");
+    if (reinterpret_cast<uintptr_t>(grads[p]) & 1)
+      return fail(TIDE_ERR_ALIGN, "grads[" + std::to_string(p) + "] is not 2-byte aligned");
+  }
+  if (plan->pk.chunk_begin.back() == 0) return TIDE_OK;  // nothing to write
+  if (packed == nullptr) return fail(TIDE_ERR_INVALID, "packed must not be NULL");
+  if (reinterpret_cast<uintptr_t>(packed) & 3) return fail(TIDE_ERR_ALIGN, "packed is not 4-byte aligned");
+  std::vector<const void*> key(grads, grads + P);
+  key.push_back(packed);
+  return run_op(
+      plan, tide::kOpPack, key,
+      [&](std::vector<tide::CallHdr>* hdr, std::vector<const void*>* ptrs) {
+        tide::pk_call_table(g, plan->pk.segs, grads, packed, hdr, ptrs);
+      },
+      static_cast<hipStream_t>(stream));
 }
 
 void tide_plan_destroy(tide_plan* plan) {

@@ -4,15 +4,21 @@
 //
 //   rs_local_kernel    reduce-scatter local stage (Section 4, Equation 5;
 //                      Section 4.1 "Level 1: Node-Local Reduction"): W ranks'
-//                      bf16 gradients -> W packed fp32 shards, summed in rank
-//                      order in fp32 (Section 4.3), padding rows written +0.
+//                      bf16 (or fp32) gradients -> W packed fp32 shards,
+//                      summed in rank order in fp32 (Section 4.3), then
+//                      Equation 5's alpha and accumulate; padding rows are
+//                      rows of zeros.
 //   ag_copyout_kernel  all-gather copy-out (Section 2.1): rank-major bf16
 //                      buffer -> per-parameter tensors.
 //   ag_copyin_kernel   all-gather copy-in (Sections 2.1, 3.1): every rank's
 //                      local shards (fp32 cast to bf16, or bf16) -> the
 //                      rank-major bf16 buffer, padding +0.
+//   stock_pack_kernel  stock FSDP2's gradient pack of one rank (Section 2.1,
+//                      Equation 3): slice, zero-pad, widen to fp32 and place
+//                      rank-major; the baseline that the reduce-scatter above
+//                      makes unnecessary.
 //
-// Both are HBM-bandwidth bound: no MFMA, no atomics, no communication between
+// All are HBM-bandwidth bound: no MFMA, no atomics, no communication between
 // waves.  Structure (shared):
 //   * The plan's segments are cut into fixed-size chunks.  Every wave of the
 //     grid is an independent worker, and chunks are dealt to waves round
@@ -25,13 +31,13 @@
 //     with one 64-lane compare and ballot.  The segment's header and pointers
 //     are then fetched with scalar loads one chunk ahead, so the scalar
 //     fetch overlaps the vector loads of the current chunk.
-//   * Vector bodies use non-temporal 8-byte (reduce-scatter) or 16-byte
-//     (copy-out) loads and contiguous 16-byte stores; heads and tails of
-//     misaligned tensors take a scalar path.
+//   * Vector bodies use non-temporal loads and contiguous 8- or 16-byte
+//     stores; heads and tails of misaligned tensors take a scalar path.
 #include <hip/hip_runtime.h>
 
 #include <climits>
 #include <cstdint>
+#include <type_traits>
 
 #include "tide_internal.h"
 
@@ -70,6 +76,7 @@ __device__ __forceinline__ void store(void* p, T v) {
 
 __device__ __forceinline__ uint16_t load2(const uint16_t* p) { return *(const TIDE_GLOBAL uint16_t*)(p); }
 __device__ __forceinline__ void store2(uint16_t* p, uint16_t v) { *(TIDE_GLOBAL uint16_t*)(p) = v; }
+__device__ __forceinline__ float load4(const float* p) { return *(const TIDE_GLOBAL float*)(p); }
 __device__ __forceinline__ void store4(float* p, float v) { *(TIDE_GLOBAL float*)(p) = v; }
 
 // bf16 is the upper half of binary32, so widening is a shift (exact).
@@ -84,8 +91,18 @@ __device__ __forceinline__ int64_t min64(int64_t a, int64_t b) { return a < b ? 
 
 __device__ __forceinline__ int lane_id() { return int(threadIdx.x & 63); }
 
+// Groups each lane has in flight per step (measured on MI355X: two groups of
+// W loads for the reduce-scatter, four 16-byte loads for the copies).
+constexpr int kRsUnroll = 2;
+constexpr int kCoUnroll = 4;
+
+// Buffer-resource word 3 for raw (untyped) byte-addressed buffers on gfx9-class
+// GPUs, and the cache-policy operand bit that marks an access non-temporal.
+constexpr int kRawBuffer = 0x00020000;
+constexpr int kPolicyNT = 2;
+
 // ---------------------------------------------------------------------------
-// Chunk dealing and segment lookup
+// Chunk dealing and segment lookup (shared by every kernel)
 // ---------------------------------------------------------------------------
 
 // The chunk -> segment search table: first-chunk indices of all segments,
@@ -126,7 +143,6 @@ __device__ __forceinline__ int32_t seek(const int32_t* cb, int32_t nseg, int32_t
 // A wave's view of one chunk.
 struct Chunk {
   int64_t lo, vlo, vhi, hi;  // scalar [lo, vlo), vector groups [vlo, vhi), scalar [vhi, hi)
-  int32_t kind;
 };
 
 // Chunk j of a segment of `len` elements, `nch` chunks: chunk boundaries after
@@ -136,7 +152,6 @@ struct Chunk {
 __device__ __forceinline__ Chunk chunk_range(const CallHdr& h, int64_t j, int64_t nch, int64_t chunk, int group) {
   const int64_t head = h.head > 0 ? h.head : 0;
   Chunk r;
-  r.kind = h.kind;
   r.lo = (j == 0) ? 0 : min64(h.len, j * chunk + head);
   r.hi = (j == nch - 1) ? h.len : min64(h.len, (j + 1) * chunk + head);
   if (h.head < 0) {
@@ -162,130 +177,19 @@ __device__ __forceinline__ void wave_slot(int32_t* w, int32_t* nw) {
   *nw = int32_t(gridDim.x) * tide::kWavesPerGroup;
 }
 
-// ---------------------------------------------------------------------------
-// Reduce-scatter local stage
-// ---------------------------------------------------------------------------
-
-// Sum of the W sources at element e (scalar path), rank order 0..W-1.
-__device__ __forceinline__ float sum_one(const uint16_t* const* src, int32_t W, int64_t e) {
-  float acc = bf16_to_f32(load2(src[0] + e));
-  for (int32_t u = 1; u < W; ++u) acc = acc + bf16_to_f32(load2(src[u] + e));
-  return acc;
-}
-
-// acc = widen(v) and acc = acc + widen(v): one binary32 addition per element.
-__device__ __forceinline__ void widen4(u32x2 v, float a[4]) {
-  a[0] = bf16_lo(v.x);
-  a[1] = bf16_hi(v.x);
-  a[2] = bf16_lo(v.y);
-  a[3] = bf16_hi(v.y);
-}
-__device__ __forceinline__ void add4(u32x2 v, float a[4]) {
-  a[0] = a[0] + bf16_lo(v.x);
-  a[1] = a[1] + bf16_hi(v.x);
-  a[2] = a[2] + bf16_lo(v.y);
-  a[3] = a[3] + bf16_hi(v.y);
-}
-
-// Vector body of a sum chunk: groups of 4 elements in [vlo, vhi); sources
-// 8-byte aligned and the destination 16-byte aligned there.  Lane l handles
-// groups l, l + 64, ... (two per step: 2W independent loads in flight).
-// Groups each lane has in flight per step (measured on MI355X: two groups of
-// W 8-byte loads for the reduce-scatter, four 16-byte loads for the copy).
-constexpr int kRsUnroll = 2;
-
-// Buffer-resource word 3 for raw (untyped) byte-addressed buffers on gfx9-class
-// GPUs, and the cache-policy operand bit that marks an access non-temporal.
-constexpr int kRawBuffer = 0x00020000;
-constexpr int kPolicyNT = 2;
-constexpr int kCoUnroll = 4;
-
-template <int WT, bool CL, bool CS>
-__device__ __forceinline__ void sum_body(const uint16_t* const* src, int32_t W, float* dst, int64_t vlo, int64_t vhi) {
-  const int64_t ng = (vhi - vlo) >> 2;
-  int64_t g = lane_id();
-  if constexpr (WT > 0) {
-    constexpr int U = kRsUnroll;
-    const uint16_t* s[WT];
-#pragma unroll
-    for (int u = 0; u < WT; ++u) s[u] = src[u] + vlo;
-    float* d = dst + vlo;
-    // U groups per lane per step, U*WT independent loads in flight; the
-    // remainder of a partial chunk goes one group per lane per step.
-    int64_t base = 0;
-    // Source loads go through buffer resources covering exactly this chunk's
-    // body (scalar base, 32-bit lane offsets, hardware range check).
-    __amdgpu_buffer_rsrc_t rs[WT];
-#pragma unroll
-    for (int u = 0; u < WT; ++u)
-      rs[u] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(s[u]), 0, int((vhi - vlo) * 2), kRawBuffer);
-    for (; base + 64 * U <= ng; base += 64 * U) {
-      u32x2 v[U][WT];
-#pragma unroll
-      for (int k = 0; k < U; ++k) {
-#pragma unroll
-        for (int u = 0; u < WT; ++u)
-          v[k][u] = __builtin_amdgcn_raw_buffer_load_b64(rs[u], int((base + g + 64 * k) * 8), 0, CL ? 0 : kPolicyNT);
-      }
-#pragma unroll
-      for (int k = 0; k < U; ++k) {
-        float a[4];
-        widen4(v[k][0], a);
-#pragma unroll
-        for (int u = 1; u < WT; ++u) add4(v[k][u], a);
-        store<f32x4, CS>(d + (base + g + 64 * k) * 4, f32x4{a[0], a[1], a[2], a[3]});
-      }
-    }
-    for (int64_t gk = base + g; gk < ng; gk += 64) {
-      u32x2 v[WT];
-#pragma unroll
-      for (int u = 0; u < WT; ++u) v[u] = load<u32x2, CL>(s[u] + gk * 4);
-      float a[4];
-      widen4(v[0], a);
-#pragma unroll
-      for (int u = 1; u < WT; ++u) add4(v[u], a);
-      store<f32x4, CS>(d + gk * 4, f32x4{a[0], a[1], a[2], a[3]});
-    }
-  } else {
-    // Any W: sources in batches of 8, still added in rank order.
-    for (; g < ng; g += 64) {
-      const int64_t e = vlo + g * 4;
-      float acc[4];
-      widen4(load<u32x2, CL>(src[0] + e), acc);
-      for (int32_t u0 = 1; u0 < W; u0 += 8) {
-        const int32_t nb = (W - u0) < 8 ? (W - u0) : 8;
-        u32x2 v[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-          if (k < nb) v[k] = load<u32x2, CL>(src[u0 + k] + e);
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-          if (k < nb) add4(v[k], acc);
-      }
-      store<f32x4, CS>(dst + e, f32x4{acc[0], acc[1], acc[2], acc[3]});
-    }
-  }
-}
-
-template <bool CS>
-__device__ __forceinline__ void zero_chunk(float* dst, const Chunk& c) {
-  const int lane = lane_id();
-  for (int64_t e = c.lo + lane; e < c.vlo; e += 64) store4(dst + e, 0.0f);
-  for (int64_t e = c.vhi + lane; e < c.hi; e += 64) store4(dst + e, 0.0f);
-  for (int64_t e = c.vlo + int64_t(lane) * 4; e < c.vhi; e += 256) store<f32x4, CS>(dst + e, f32x4{0.0f, 0.0f, 0.0f, 0.0f});
-}
-
-// Segment descriptor of the chunk a wave is about to process (wave-uniform).
-template <int WT>
-struct RsDesc {
+// Segment descriptor of the chunk a wave is about to process (wave-uniform):
+// NS source pointers (none when the kernel reads them from the table as it
+// goes) and the destination.
+template <int NS>
+struct Desc {
   CallHdr h;
   int32_t seg, j, nch;
-  const uint16_t* src[WT > 0 ? WT : 1];
-  float* dst;
+  const void* src[NS > 0 ? NS : 1];
+  void* dst;
 };
 
-template <int WT>
-__device__ __forceinline__ void rs_fetch(const Tables& a, const int32_t* cb, int32_t* cur, int32_t c, RsDesc<WT>* d) {
+template <int NS>
+__device__ __forceinline__ void fetch(const Tables& a, const int32_t* cb, int32_t* cur, int32_t c, Desc<NS>* d) {
   *cur = seek(cb, a.nseg, *cur, c);
   const int32_t s = *cur;
   const int32_t first = sgpr(cb[s]);
@@ -294,73 +198,266 @@ __device__ __forceinline__ void rs_fetch(const Tables& a, const int32_t* cb, int
   d->nch = sgpr(cb[s + 1]) - first;
   d->h = a.hdr[s];
   const void* const* row = a.ptrs + int64_t(s) * (a.nsrc + 1);
-  if constexpr (WT > 0) {
 #pragma unroll
-    for (int u = 0; u < WT; ++u) d->src[u] = static_cast<const uint16_t*>(row[u]);
-  }
-  d->dst = static_cast<float*>(const_cast<void*>(row[a.nsrc]));
+  for (int u = 0; u < NS; ++u) d->src[u] = row[u];
+  d->dst = const_cast<void*>(row[a.nsrc]);
 }
 
-template <int WT, bool CL, bool CS, bool STAGED>
-__global__ __launch_bounds__(tide::kThreads) void rs_local_kernel(const CallHdr* __restrict__ hdr,
-                                                                  const void* const* __restrict__ ptrs,
-                                                                  const int32_t* __restrict__ chunk_begin,
-                                                                  int32_t nseg, int32_t nsrc, int32_t nchunks,
-                                                                  int32_t chunk) {
-  const Tables a{hdr, ptrs, nseg, nsrc, nchunks, chunk};
-  const int32_t* cb = chunk_table<STAGED>(chunk_begin, nseg);
+// The persistent loop of every kernel: deal chunks to this wave round robin,
+// fetch each chunk's descriptor one chunk ahead (the scalar loads overlap the
+// vector loads of the current chunk) and hand the chunk to `body`.
+template <int NS, bool STAGED, typename Body>
+__device__ __forceinline__ void for_each_chunk(const Tables& a, const int32_t* __restrict__ chunk_begin, Body body) {
+  const int32_t* cb = chunk_table<STAGED>(chunk_begin, a.nseg);
   int32_t w, nw;
   wave_slot(&w, &nw);
-  const int32_t W = WT > 0 ? WT : a.nsrc;
   int32_t cur = 0;
   int32_t c = w;
-  RsDesc<WT> next;
-  if (c < a.nchunks) rs_fetch<WT>(a, cb, &cur, c, &next);
+  Desc<NS> next;
+  if (c < a.nchunks) fetch<NS>(a, cb, &cur, c, &next);
   while (c < a.nchunks) {
-    const RsDesc<WT> d = next;
+    const Desc<NS> d = next;
     const int32_t cn = c + nw;
-    if (cn < a.nchunks) rs_fetch<WT>(a, cb, &cur, cn, &next);  // overlaps the loads below
-    if (d.h.kind == tide::kZero) {
-      zero_chunk<CS>(d.dst, chunk_range(d.h, d.j, d.nch, a.chunk, 4));
-    } else {
-      const Chunk r = chunk_range(d.h, d.j, d.nch, a.chunk, 4);
-      const uint16_t* const* src;
-      if constexpr (WT > 0) {
-        src = d.src;
-      } else {
-        // any W: the sources are read from the call table as needed
-        src = reinterpret_cast<const uint16_t* const*>(a.ptrs + int64_t(d.seg) * (a.nsrc + 1));
-      }
-      const int lane = lane_id();
-      for (int64_t e = r.lo + lane; e < r.vlo; e += 64) store4(d.dst + e, sum_one(src, W, e));
-      for (int64_t e = r.vhi + lane; e < r.hi; e += 64) store4(d.dst + e, sum_one(src, W, e));
-      if (r.vhi > r.vlo) sum_body<WT, CL, CS>(src, W, d.dst, r.vlo, r.vhi);
-    }
+    if (cn < a.nchunks) fetch<NS>(a, cb, &cur, cn, &next);
+    body(d);
     c = cn;
   }
 }
 
 // ---------------------------------------------------------------------------
-// All-gather copy-out
+// Reduce-scatter local stage
 // ---------------------------------------------------------------------------
 
-struct CoDesc {
-  CallHdr h;
-  int32_t j, nch;
-  const void* src;
-  uint16_t* dst;
+// Source types.  A vector group is 4 elements: 8 bytes of bf16 or 16 bytes of
+// fp32 per source.  first() starts the sum with rank 0's value, add() adds
+// the next rank's: one binary32 addition per element, no contraction.
+template <bool F32>
+struct Src;
+
+template <>
+struct Src<false> {
+  using T = uint16_t;
+  using V = u32x2;
+  template <int AUX>
+  static __device__ __forceinline__ V buffer_load(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, AUX);
+  }
+  static __device__ __forceinline__ void first(V v, float a[4]) {
+    a[0] = bf16_lo(v.x);
+    a[1] = bf16_hi(v.x);
+    a[2] = bf16_lo(v.y);
+    a[3] = bf16_hi(v.y);
+  }
+  static __device__ __forceinline__ void add(V v, float a[4]) {
+    a[0] = a[0] + bf16_lo(v.x);
+    a[1] = a[1] + bf16_hi(v.x);
+    a[2] = a[2] + bf16_lo(v.y);
+    a[3] = a[3] + bf16_hi(v.y);
+  }
+  static __device__ __forceinline__ float one(const void* p, int64_t e) {
+    return bf16_to_f32(load2(static_cast<const uint16_t*>(p) + e));
+  }
 };
 
-__device__ __forceinline__ void co_fetch(const Tables& a, const int32_t* cb, int32_t* cur, int32_t c, CoDesc* d) {
-  *cur = seek(cb, a.nseg, *cur, c);
-  const int32_t s = *cur;
-  const int32_t first = sgpr(cb[s]);
-  d->j = c - first;
-  d->nch = sgpr(cb[s + 1]) - first;
-  d->h = a.hdr[s];
-  d->src = a.ptrs[2 * int64_t(s)];
-  d->dst = static_cast<uint16_t*>(const_cast<void*>(a.ptrs[2 * int64_t(s) + 1]));
+template <>
+struct Src<true> {
+  using T = float;
+  using V = f32x4;
+  template <int AUX>
+  static __device__ __forceinline__ V buffer_load(__amdgpu_buffer_rsrc_t r, int off) {
+    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX);
+    return f32x4{__uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z), __uint_as_float(x.w)};
+  }
+  static __device__ __forceinline__ void first(V v, float a[4]) {
+    a[0] = v.x;
+    a[1] = v.y;
+    a[2] = v.z;
+    a[3] = v.w;
+  }
+  static __device__ __forceinline__ void add(V v, float a[4]) {
+    a[0] = a[0] + v.x;
+    a[1] = a[1] + v.y;
+    a[2] = a[2] + v.z;
+    a[3] = a[3] + v.w;
+  }
+  static __device__ __forceinline__ float one(const void* p, int64_t e) {
+    return load4(static_cast<const float*>(p) + e);
+  }
+};
+
+// Equation 5's scale and accumulate, applied to a finished sum: one binary32
+// product, then (accumulating) one binary32 addition of the value already in
+// the shard.  EPI = false (alpha = 1, no accumulation): the sum is stored as
+// it is.  The choice is uniform over the grid and made once per chunk, so the
+// default path's loop carries no trace of the epilogue.
+struct Epilogue {
+  float alpha;
+  bool accumulate;
+};
+
+template <bool CS, bool EPI>
+__device__ __forceinline__ void put4(float* d, const float a[4], const Epilogue& ep) {
+  if constexpr (!EPI) {
+    store<f32x4, CS>(d, f32x4{a[0], a[1], a[2], a[3]});
+    return;
+  }
+  float v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = ep.alpha * a[i];
+  if (ep.accumulate) {
+    const f32x4 o = load<f32x4, true>(d);
+    v[0] = o.x + v[0];
+    v[1] = o.y + v[1];
+    v[2] = o.z + v[2];
+    v[3] = o.w + v[3];
+  }
+  store<f32x4, CS>(d, f32x4{v[0], v[1], v[2], v[3]});
 }
+
+template <bool EPI>
+__device__ __forceinline__ void put1(float* d, float s, const Epilogue& ep) {
+  if constexpr (!EPI) {
+    store4(d, s);
+    return;
+  }
+  float v = ep.alpha * s;
+  if (ep.accumulate) v = load4(d) + v;
+  store4(d, v);
+}
+
+// Sum of the W sources at element e (scalar path), rank order 0..W-1.
+template <bool F32>
+__device__ __forceinline__ float sum_one(const void* const* src, int32_t W, int64_t e) {
+  float acc = Src<F32>::one(src[0], e);
+  for (int32_t u = 1; u < W; ++u) acc = acc + Src<F32>::one(src[u], e);
+  return acc;
+}
+
+// Vector body of a sum chunk: groups of 4 elements in [vlo, vhi), every
+// source and the destination group-aligned there.  Lane l handles groups
+// l, l + 64, ...; kRsUnroll groups per step keep kRsUnroll*W independent loads
+// in flight; the remainder of a partial chunk goes one group per step.
+template <int WT, bool F32, bool CL, bool CS, bool EPI>
+__device__ __forceinline__ void sum_body(const void* const* src, int32_t W, float* dst, int64_t vlo, int64_t vhi,
+                                         const Epilogue& ep) {
+  using S = Src<F32>;
+  using T = typename S::T;
+  using V = typename S::V;
+  constexpr int kGroupBytes = 4 * int(sizeof(T));
+  const int64_t ng = (vhi - vlo) >> 2;
+  const int64_t g = lane_id();
+  if constexpr (WT > 0) {
+    constexpr int U = kRsUnroll;
+    const T* s[WT];
+#pragma unroll
+    for (int u = 0; u < WT; ++u) s[u] = static_cast<const T*>(src[u]) + vlo;
+    float* d = dst + vlo;
+    // Source loads go through buffer resources covering exactly this chunk's
+    // body (scalar base, 32-bit lane offsets, hardware range check).
+    __amdgpu_buffer_rsrc_t rs[WT];
+#pragma unroll
+    for (int u = 0; u < WT; ++u)
+      rs[u] = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(s[u]), 0, int((vhi - vlo) * int64_t(sizeof(T))),
+                                                kRawBuffer);
+    int64_t base = 0;
+    for (; base + 64 * U <= ng; base += 64 * U) {
+      V v[U][WT];
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+#pragma unroll
+        for (int u = 0; u < WT; ++u)
+          v[k][u] = S::template buffer_load<CL ? 0 : kPolicyNT>(rs[u], int((base + g + 64 * k) * kGroupBytes));
+      }
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+        float a[4];
+        S::first(v[k][0], a);
+#pragma unroll
+        for (int u = 1; u < WT; ++u) S::add(v[k][u], a);
+        put4<CS, EPI>(d + (base + g + 64 * k) * 4, a, ep);
+      }
+    }
+    for (int64_t gk = base + g; gk < ng; gk += 64) {
+      V v[WT];
+#pragma unroll
+      for (int u = 0; u < WT; ++u) v[u] = load<V, CL>(s[u] + gk * 4);
+      float a[4];
+      S::first(v[0], a);
+#pragma unroll
+      for (int u = 1; u < WT; ++u) S::add(v[u], a);
+      put4<CS, EPI>(d + gk * 4, a, ep);
+    }
+  } else {
+    // Any W: sources in batches of 8, still added in rank order.
+    for (int64_t gk = g; gk < ng; gk += 64) {
+      const int64_t e = vlo + gk * 4;
+      float acc[4];
+      S::first(load<V, CL>(static_cast<const T*>(src[0]) + e), acc);
+      for (int32_t u0 = 1; u0 < W; u0 += 8) {
+        const int32_t nb = (W - u0) < 8 ? (W - u0) : 8;
+        V v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          if (k < nb) v[k] = load<V, CL>(static_cast<const T*>(src[u0 + k]) + e);
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          if (k < nb) S::add(v[k], acc);
+      }
+      put4<CS, EPI>(dst + e, acc, ep);
+    }
+  }
+}
+
+// Padding rows: every rank contributes zeros there, so the sum is +0.
+template <bool CS, bool EPI>
+__device__ __forceinline__ void zero_rows(float* dst, const Chunk& c, const Epilogue& ep) {
+  const int lane = lane_id();
+  const float z[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int64_t e = c.lo + lane; e < c.vlo; e += 64) put1<EPI>(dst + e, 0.0f, ep);
+  for (int64_t e = c.vhi + lane; e < c.hi; e += 64) put1<EPI>(dst + e, 0.0f, ep);
+  for (int64_t e = c.vlo + int64_t(lane) * 4; e < c.vhi; e += 256) put4<CS, EPI>(dst + e, z, ep);
+}
+
+// One chunk of the reduce-scatter: the sum of a kSum segment's piece, or the
+// zeros of a padding piece.
+template <int WT, bool F32, bool CL, bool CS, bool EPI>
+__device__ __forceinline__ void rs_chunk(const Tables& a, const Desc<WT>& d, int32_t W, const Epilogue& ep) {
+  float* dst = static_cast<float*>(d.dst);
+  const Chunk r = chunk_range(d.h, d.j, d.nch, a.chunk, 4);
+  if (d.h.kind == tide::kZero) {
+    zero_rows<CS, EPI>(dst, r, ep);
+    return;
+  }
+  // any W: the sources are read from the call table as needed
+  const void* const* src = WT > 0 ? d.src : a.ptrs + int64_t(d.seg) * (a.nsrc + 1);
+  const int lane = lane_id();
+  for (int64_t e = r.lo + lane; e < r.vlo; e += 64) put1<EPI>(dst + e, sum_one<F32>(src, W, e), ep);
+  for (int64_t e = r.vhi + lane; e < r.hi; e += 64) put1<EPI>(dst + e, sum_one<F32>(src, W, e), ep);
+  if (r.vhi > r.vlo) sum_body<WT, F32, CL, CS, EPI>(src, W, dst, r.vlo, r.vhi, ep);
+}
+
+template <int WT, bool F32, bool CL, bool CS, bool STAGED>
+__global__ __launch_bounds__(tide::kThreads) void rs_local_kernel(const CallHdr* __restrict__ hdr,
+                                                                  const void* const* __restrict__ ptrs,
+                                                                  const int32_t* __restrict__ chunk_begin,
+                                                                  int32_t nseg, int32_t nsrc, int32_t nchunks,
+                                                                  int32_t chunk, float alpha, int32_t accumulate) {
+  const Tables a{hdr, ptrs, nseg, nsrc, nchunks, chunk};
+  const Epilogue ep{alpha, accumulate != 0};
+  const bool epi = !(alpha == 1.0f) || accumulate != 0;
+  const int32_t W = WT > 0 ? WT : nsrc;
+  for_each_chunk<WT, STAGED>(a, chunk_begin, [&](const Desc<WT>& d) {
+    if (epi) {
+      rs_chunk<WT, F32, CL, CS, true>(a, d, W, ep);
+    } else {
+      rs_chunk<WT, F32, CL, CS, false>(a, d, W, ep);
+    }
+  });
+}
+
+// ---------------------------------------------------------------------------
+// Copies: all-gather copy-out and copy-in, stock gradient pack
+// ---------------------------------------------------------------------------
 
 // Full steps of U groups of 8 bf16 per lane (all loads issued before the
 // stores); returns where the steps stopped.
@@ -376,14 +473,18 @@ __device__ __forceinline__ int64_t copy_steps(const uint16_t* sv, uint16_t* dv, 
   return base;
 }
 
-// bf16 words of [vlo, vhi) (groups of 8, both sides 16-byte aligned).
+// bf16 [lo, hi): groups of 8 in [vlo, vhi) with both sides 16-byte aligned
+// (kCoUnroll 16-byte loads in flight per lane, then two, then one), the rest
+// element by element.
 template <bool CL, bool CS>
-__device__ __forceinline__ void copy_body(const uint16_t* src, uint16_t* dst, int64_t vlo, int64_t vhi) {
+__device__ __forceinline__ void copy_chunk(const uint16_t* src, uint16_t* dst, const Chunk& r) {
   const int lane = lane_id();
-  const uint16_t* sv = src + vlo;
-  uint16_t* dv = dst + vlo;
-  const int64_t ng = (vhi - vlo) >> 3;
-  // kCoUnroll 16-byte loads in flight per lane, then two, then one.
+  for (int64_t e = r.lo + lane; e < r.vlo; e += 64) store2(dst + e, load2(src + e));
+  for (int64_t e = r.vhi + lane; e < r.hi; e += 64) store2(dst + e, load2(src + e));
+  if (r.vhi <= r.vlo) return;
+  const uint16_t* sv = src + r.vlo;
+  uint16_t* dv = dst + r.vlo;
+  const int64_t ng = (r.vhi - r.vlo) >> 3;
   int64_t base = 0;
   base = copy_steps<kCoUnroll, CL, CS>(sv, dv, base, ng, lane);
   base = copy_steps<2, CL, CS>(sv, dv, base, ng, lane);
@@ -396,30 +497,11 @@ __global__ __launch_bounds__(tide::kThreads) void ag_copyout_kernel(const CallHd
                                                                     const int32_t* __restrict__ chunk_begin,
                                                                     int32_t nseg, int32_t nchunks, int32_t chunk) {
   const Tables a{hdr, ptrs, nseg, 1, nchunks, chunk};
-  const int32_t* cb = chunk_table<STAGED>(chunk_begin, nseg);
-  int32_t w, nw;
-  wave_slot(&w, &nw);
-  int32_t cur = 0;
-  int32_t c = w;
-  CoDesc next;
-  if (c < a.nchunks) co_fetch(a, cb, &cur, c, &next);
-  const int lane = lane_id();
-  while (c < a.nchunks) {
-    const CoDesc d = next;
-    const int32_t cn = c + nw;
-    if (cn < a.nchunks) co_fetch(a, cb, &cur, cn, &next);
-    const Chunk r = chunk_range(d.h, d.j, d.nch, a.chunk, 8);
-    const uint16_t* src = static_cast<const uint16_t*>(d.src);
-    for (int64_t e = r.lo + lane; e < r.vlo; e += 64) store2(d.dst + e, load2(src + e));
-    for (int64_t e = r.vhi + lane; e < r.hi; e += 64) store2(d.dst + e, load2(src + e));
-    if (r.vhi > r.vlo) copy_body<CL, CS>(src, d.dst, r.vlo, r.vhi);
-    c = cn;
-  }
+  for_each_chunk<1, STAGED>(a, chunk_begin, [&](const Desc<1>& d) {
+    copy_chunk<CL, CS>(static_cast<const uint16_t*>(d.src[0]), static_cast<uint16_t*>(d.dst),
+                       chunk_range(d.h, d.j, d.nch, a.chunk, 8));
+  });
 }
-
-// ---------------------------------------------------------------------------
-// All-gather copy-in
-// ---------------------------------------------------------------------------
 
 // fp32 -> bf16, round to nearest even, on the bit pattern; a NaN stays a NaN
 // of the same sign with its top payload bits and the quiet bit set.
@@ -445,19 +527,21 @@ __device__ __forceinline__ int64_t cast_steps(const float* sv, uint16_t* dv, int
   return base;
 }
 
-// fp32 [vlo, vhi) -> bf16 (groups of 4: 16-byte loads, 8-byte stores, each
-// contiguous across the wave).
+// fp32 [lo, hi) -> bf16: groups of 4 in [vlo, vhi) (16-byte loads, 8-byte
+// stores, each contiguous across the wave), the rest element by element.
 template <bool CL, bool CS>
-__device__ __forceinline__ void cast_body(const float* src, uint16_t* dst, int64_t vlo, int64_t vhi) {
+__device__ __forceinline__ void cast_chunk(const float* src, uint16_t* dst, const Chunk& r) {
   const int lane = lane_id();
-  const float* sv = src + vlo;
-  uint16_t* dv = dst + vlo;
-  const int64_t ng = (vhi - vlo) >> 2;
+  for (int64_t e = r.lo + lane; e < r.vlo; e += 64) store2(dst + e, uint16_t(f32_to_bf16(load4(src + e))));
+  for (int64_t e = r.vhi + lane; e < r.hi; e += 64) store2(dst + e, uint16_t(f32_to_bf16(load4(src + e))));
+  if (r.vhi <= r.vlo) return;
+  const float* sv = src + r.vlo;
+  uint16_t* dv = dst + r.vlo;
+  const int64_t ng = (r.vhi - r.vlo) >> 2;
   int64_t base = 0;
   base = cast_steps<kCoUnroll, CL, CS>(sv, dv, base, ng, lane);
   base = cast_steps<2, CL, CS>(sv, dv, base, ng, lane);
-  for (int64_t gk = base + lane; gk < ng; gk += 64)
-    store<u32x2, CS>(dv + gk * 4, cast4(load<f32x4, CL>(sv + gk * 4)));
+  for (int64_t gk = base + lane; gk < ng; gk += 64) store<u32x2, CS>(dv + gk * 4, cast4(load<f32x4, CL>(sv + gk * 4)));
 }
 
 template <bool F32, bool CL, bool CS, bool STAGED>
@@ -466,150 +550,148 @@ __global__ __launch_bounds__(tide::kThreads) void ag_copyin_kernel(const CallHdr
                                                                    const int32_t* __restrict__ chunk_begin,
                                                                    int32_t nseg, int32_t nchunks, int32_t chunk) {
   const Tables a{hdr, ptrs, nseg, 1, nchunks, chunk};
-  const int32_t* cb = chunk_table<STAGED>(chunk_begin, nseg);
-  int32_t w, nw;
-  wave_slot(&w, &nw);
-  int32_t cur = 0;
-  int32_t c = w;
-  CoDesc next;
-  if (c < a.nchunks) co_fetch(a, cb, &cur, c, &next);
-  const int lane = lane_id();
-  while (c < a.nchunks) {
-    const CoDesc d = next;
-    const int32_t cn = c + nw;
-    if (cn < a.nchunks) co_fetch(a, cb, &cur, cn, &next);
+  for_each_chunk<1, STAGED>(a, chunk_begin, [&](const Desc<1>& d) {
+    uint16_t* dst = static_cast<uint16_t*>(d.dst);
+    const int lane = lane_id();
     if (d.h.kind == tide::kZero) {
       // padding of the rank-major slot: bf16 +0
       const Chunk r = chunk_range(d.h, d.j, d.nch, a.chunk, 8);
-      for (int64_t e = r.lo + lane; e < r.vlo; e += 64) store2(d.dst + e, 0);
-      for (int64_t e = r.vhi + lane; e < r.hi; e += 64) store2(d.dst + e, 0);
-      for (int64_t e = r.vlo + int64_t(lane) * 8; e < r.vhi; e += 512) store<u32x4, CS>(d.dst + e, u32x4{0, 0, 0, 0});
+      for (int64_t e = r.lo + lane; e < r.vlo; e += 64) store2(dst + e, 0);
+      for (int64_t e = r.vhi + lane; e < r.hi; e += 64) store2(dst + e, 0);
+      for (int64_t e = r.vlo + int64_t(lane) * 8; e < r.vhi; e += 512) store<u32x4, CS>(dst + e, u32x4{0, 0, 0, 0});
     } else if constexpr (F32) {
-      const Chunk r = chunk_range(d.h, d.j, d.nch, a.chunk, 4);
-      const float* src = static_cast<const float*>(d.src);
-      for (int64_t e = r.lo + lane; e < r.vlo; e += 64) store2(d.dst + e, uint16_t(f32_to_bf16(load<float, true>(src + e))));
-      for (int64_t e = r.vhi + lane; e < r.hi; e += 64) store2(d.dst + e, uint16_t(f32_to_bf16(load<float, true>(src + e))));
-      if (r.vhi > r.vlo) cast_body<CL, CS>(src, d.dst, r.vlo, r.vhi);
+      cast_chunk<CL, CS>(static_cast<const float*>(d.src[0]), dst, chunk_range(d.h, d.j, d.nch, a.chunk, 4));
     } else {
-      const Chunk r = chunk_range(d.h, d.j, d.nch, a.chunk, 8);
-      const uint16_t* src = static_cast<const uint16_t*>(d.src);
-      for (int64_t e = r.lo + lane; e < r.vlo; e += 64) store2(d.dst + e, load2(src + e));
-      for (int64_t e = r.vhi + lane; e < r.hi; e += 64) store2(d.dst + e, load2(src + e));
-      if (r.vhi > r.vlo) copy_body<CL, CS>(src, d.dst, r.vlo, r.vhi);
+      copy_chunk<CL, CS>(static_cast<const uint16_t*>(d.src[0]), dst, chunk_range(d.h, d.j, d.nch, a.chunk, 8));
     }
-    c = cn;
-  }
+  });
 }
 
+// Stock gradient pack of one rank: its bf16 rows widened to fp32 (groups of
+// 4: 8-byte loads, 16-byte stores), padding rows +0.
+template <bool CL, bool CS, bool STAGED>
+__global__ __launch_bounds__(tide::kThreads) void stock_pack_kernel(const CallHdr* __restrict__ hdr,
+                                                                    const void* const* __restrict__ ptrs,
+                                                                    const int32_t* __restrict__ chunk_begin,
+                                                                    int32_t nseg, int32_t nchunks, int32_t chunk) {
+  const Tables a{hdr, ptrs, nseg, 1, nchunks, chunk};
+  for_each_chunk<1, STAGED>(a, chunk_begin, [&](const Desc<1>& d) {
+    float* dst = static_cast<float*>(d.dst);
+    const Chunk r = chunk_range(d.h, d.j, d.nch, a.chunk, 4);
+    const int lane = lane_id();
+    if (d.h.kind == tide::kZero) {
+      for (int64_t e = r.lo + lane; e < r.vlo; e += 64) store4(dst + e, 0.0f);
+      for (int64_t e = r.vhi + lane; e < r.hi; e += 64) store4(dst + e, 0.0f);
+      for (int64_t e = r.vlo + int64_t(lane) * 4; e < r.vhi; e += 256)
+        store<f32x4, CS>(dst + e, f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+      return;
+    }
+    const uint16_t* src = static_cast<const uint16_t*>(d.src[0]);
+    for (int64_t e = r.lo + lane; e < r.vlo; e += 64) store4(dst + e, bf16_to_f32(load2(src + e)));
+    for (int64_t e = r.vhi + lane; e < r.hi; e += 64) store4(dst + e, bf16_to_f32(load2(src + e)));
+    const int64_t ng = (r.vhi - r.vlo) >> 2;
+    for (int64_t gk = lane; gk < ng; gk += 64) {
+      float v[4];
+      Src<false>::first(load<u32x2, CL>(src + r.vlo + gk * 4), v);
+      store<f32x4, CS>(dst + r.vlo + gk * 4, f32x4{v[0], v[1], v[2], v[3]});
+    }
+  });
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+
+// LDS for the staged chunk table; large tables stay in global memory.
 size_t staged_bytes(const KernelArgs& a, bool* staged) {
   *staged = a.nseg <= tide::kMaxStagedSegs;
   return *staged ? size_t(a.nseg + 1) * sizeof(int32_t) : 0;
 }
 
-template <int WT>
-int launch_rs_w(const KernelArgs& a, int64_t grid, hipStream_t stream) {
+// Calls f(CL, CS, STAGED, lds_bytes) with the kernel instance's flags as
+// std::bool_constant values, chosen from the call's flags and table size.
+template <typename F>
+void by_instance(const KernelArgs& a, F f) {
   bool staged;
   const size_t lds = staged_bytes(a, &staged);
   const bool cl = a.flags & TIDE_FLAG_CACHED_LOADS, cs = a.flags & TIDE_FLAG_CACHED_STORES;
-  const dim3 g{unsigned(grid), 1, 1}, b{unsigned(tide::kThreads), 1, 1};
-#define TIDE_RS(CL, CS)                                                                   \
-  do {                                                                                     \
-    if (staged)                                                                            \
-      hipLaunchKernelGGL((rs_local_kernel<WT, CL, CS, true>), g, b, lds, stream, a.hdr, a.ptrs, \
-                         a.chunk_begin, a.nseg, a.nsrc, a.nchunks, a.chunk);                \
-    else                                                                                   \
-      hipLaunchKernelGGL((rs_local_kernel<WT, CL, CS, false>), g, b, 0, stream, a.hdr, a.ptrs, \
-                         a.chunk_begin, a.nseg, a.nsrc, a.nchunks, a.chunk);                \
-  } while (0)
+  auto go = [&](auto CL, auto CS) {
+    if (staged) {
+      f(CL, CS, std::true_type{}, lds);
+    } else {
+      f(CL, CS, std::false_type{}, size_t(0));
+    }
+  };
   if (cl && cs) {
-    TIDE_RS(true, true);
+    go(std::true_type{}, std::true_type{});
   } else if (cl) {
-    TIDE_RS(true, false);
+    go(std::true_type{}, std::false_type{});
   } else if (cs) {
-    TIDE_RS(false, true);
+    go(std::false_type{}, std::true_type{});
   } else {
-    TIDE_RS(false, false);
+    go(std::false_type{}, std::false_type{});
   }
-#undef TIDE_RS
+}
+
+#define TIDE_V(x) decltype(x)::value
+
+template <int WT, bool F32>
+int launch_rs_w(const KernelArgs& a, int64_t grid, hipStream_t s) {
+  by_instance(a, [&](auto CL, auto CS, auto ST, size_t lds) {
+    hipLaunchKernelGGL((rs_local_kernel<WT, F32, TIDE_V(CL), TIDE_V(CS), TIDE_V(ST)>), dim3(unsigned(grid)),
+                       dim3(unsigned(tide::kThreads)), lds, s, a.hdr, a.ptrs, a.chunk_begin, a.nseg, a.nsrc,
+                       a.nchunks, a.chunk, a.alpha, a.accumulate);
+  });
   return int(hipGetLastError());
+}
+
+template <bool F32>
+int launch_rs_t(const KernelArgs& a, int64_t grid, hipStream_t s) {
+  switch (a.nsrc) {
+    case 8: return launch_rs_w<8, F32>(a, grid, s);
+    case 4: return launch_rs_w<4, F32>(a, grid, s);
+    default: return launch_rs_w<0, F32>(a, grid, s);
+  }
 }
 
 }  // namespace
 
 namespace tide {
 
-int launch_rs_local(const KernelArgs& a, int64_t grid, void* stream) {
+int launch_rs_local(const KernelArgs& a, bool f32, int64_t grid, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  switch (a.nsrc) {
-    case 8: return launch_rs_w<8>(a, grid, s);
-    case 4: return launch_rs_w<4>(a, grid, s);
-    case 2: return launch_rs_w<2>(a, grid, s);
-    default: return launch_rs_w<0>(a, grid, s);
-  }
+  return f32 ? launch_rs_t<true>(a, grid, s) : launch_rs_t<false>(a, grid, s);
 }
 
 int launch_ag_copyout(const KernelArgs& a, int64_t grid, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  bool staged;
-  const size_t lds = staged_bytes(a, &staged);
-  const bool cl = a.flags & TIDE_FLAG_CACHED_LOADS, cs = a.flags & TIDE_FLAG_CACHED_STORES;
-  const dim3 g{unsigned(grid), 1, 1}, b{unsigned(kThreads), 1, 1};
-#define TIDE_CO(CL, CS)                                                                    \
-  do {                                                                                      \
-    if (staged)                                                                             \
-      hipLaunchKernelGGL((ag_copyout_kernel<CL, CS, true>), g, b, lds, s, a.hdr, a.ptrs,     \
-                         a.chunk_begin, a.nseg, a.nchunks, a.chunk);                        \
-    else                                                                                    \
-      hipLaunchKernelGGL((ag_copyout_kernel<CL, CS, false>), g, b, 0, s, a.hdr, a.ptrs,      \
-                         a.chunk_begin, a.nseg, a.nchunks, a.chunk);                        \
-  } while (0)
-  if (cl && cs) {
-    TIDE_CO(true, true);
-  } else if (cl) {
-    TIDE_CO(true, false);
-  } else if (cs) {
-    TIDE_CO(false, true);
-  } else {
-    TIDE_CO(false, false);
-  }
-#undef TIDE_CO
+  by_instance(a, [&](auto CL, auto CS, auto ST, size_t lds) {
+    hipLaunchKernelGGL((ag_copyout_kernel<TIDE_V(CL), TIDE_V(CS), TIDE_V(ST)>), dim3(unsigned(grid)),
+                       dim3(unsigned(kThreads)), lds, s, a.hdr, a.ptrs, a.chunk_begin, a.nseg, a.nchunks, a.chunk);
+  });
   return int(hipGetLastError());
 }
 
 int launch_ag_copyin(const KernelArgs& a, bool f32, int64_t grid, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  bool staged;
-  const size_t lds = staged_bytes(a, &staged);
-  const bool cl = a.flags & TIDE_FLAG_CACHED_LOADS, cs = a.flags & TIDE_FLAG_CACHED_STORES;
-  const dim3 g{unsigned(grid), 1, 1}, b{unsigned(kThreads), 1, 1};
-#define TIDE_CI(F, CL, CS)                                                                       \
-  do {                                                                                            \
-    if (staged)                                                                                   \
-      hipLaunchKernelGGL((ag_copyin_kernel<F, CL, CS, true>), g, b, lds, s, a.hdr, a.ptrs,        \
-                         a.chunk_begin, a.nseg, a.nchunks, a.chunk);                              \
-    else                                                                                          \
-      hipLaunchKernelGGL((ag_copyin_kernel<F, CL, CS, false>), g, b, 0, s, a.hdr, a.ptrs,         \
-                         a.chunk_begin, a.nseg, a.nchunks, a.chunk);                              \
-  } while (0)
-#define TIDE_CI_F(F)              \
-  do {                            \
-    if (cl && cs) {               \
-      TIDE_CI(F, true, true);     \
-    } else if (cl) {              \
-      TIDE_CI(F, true, false);    \
-    } else if (cs) {              \
-      TIDE_CI(F, false, true);    \
-    } else {                      \
-      TIDE_CI(F, false, false);   \
-    }                             \
-  } while (0)
-  if (f32) {
-    TIDE_CI_F(true);
-  } else {
-    TIDE_CI_F(false);
-  }
-#undef TIDE_CI_F
-#undef TIDE_CI
+  by_instance(a, [&](auto CL, auto CS, auto ST, size_t lds) {
+    if (f32) {
+      hipLaunchKernelGGL((ag_copyin_kernel<true, TIDE_V(CL), TIDE_V(CS), TIDE_V(ST)>), dim3(unsigned(grid)),
+                         dim3(unsigned(kThreads)), lds, s, a.hdr, a.ptrs, a.chunk_begin, a.nseg, a.nchunks, a.chunk);
+    } else {
+      hipLaunchKernelGGL((ag_copyin_kernel<false, TIDE_V(CL), TIDE_V(CS), TIDE_V(ST)>), dim3(unsigned(grid)),
+                         dim3(unsigned(kThreads)), lds, s, a.hdr, a.ptrs, a.chunk_begin, a.nseg, a.nchunks, a.chunk);
+    }
+  });
+  return int(hipGetLastError());
+}
+
+int launch_stock_pack(const KernelArgs& a, int64_t grid, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  by_instance(a, [&](auto CL, auto CS, auto ST, size_t lds) {
+    hipLaunchKernelGGL((stock_pack_kernel<TIDE_V(CL), TIDE_V(CS), TIDE_V(ST)>), dim3(unsigned(grid)),
+                       dim3(unsigned(kThreads)), lds, s, a.hdr, a.ptrs, a.chunk_begin, a.nseg, a.nchunks, a.chunk);
+  });
   return int(hipGetLastError());
 }
 

@@ -124,6 +124,19 @@ std::vector<Seg> copyin_segments(const Geometry& g) {
   return segs;
 }
 
+std::vector<Seg> pack_segments(const Geometry& g) {
+  std::vector<Seg> segs;
+  for (int32_t p = 0; p < g.nparams; ++p) {
+    for (int32_t r = 0; r < g.world; ++r) {
+      const int64_t real = real_elems(g, p, r);
+      const int64_t slot = int64_t(r) * g.S + g.o[p];
+      if (real > 0) segs.push_back(Seg{int64_t(r) * g.n[p], slot, real, p, 0, kCopy});
+      if (g.n[p] > real) segs.push_back(Seg{0, slot + real, g.n[p] - real, p, 0, kZero});
+    }
+  }
+  return segs;
+}
+
 tide_status chunk_table(const std::vector<Seg>& segs, int64_t chunk, std::vector<int32_t>* chunk_begin,
                         std::string* why) {
   chunk_begin->assign(segs.size() + 1, 0);
@@ -166,8 +179,10 @@ tide_status check_options(const tide_options* in, tide_options* out, std::string
 tide_options effective_options(const tide_options& given, Op op, int32_t cu_count) {
   tide_options o = given;
   if (o.cu_budget == 0) o.cu_budget = cu_count;
-  if (o.wg_per_cu == 0) o.wg_per_cu = op == kOpRs ? kRsWgPerCu : op == kOpCo ? kCoWgPerCu : kCiWgPerCu;
-  if (o.chunk_elems == 0) o.chunk_elems = op == kOpRs ? kRsChunk : op == kOpCo ? kCoChunk : kCiChunk;
+  const int32_t wg[kNumOps] = {kRsWgPerCu, kCoWgPerCu, kCiWgPerCu, kPkWgPerCu};
+  const int64_t chunk[kNumOps] = {kRsChunk, kCoChunk, kCiChunk, kPkChunk};
+  if (o.wg_per_cu == 0) o.wg_per_cu = wg[op];
+  if (o.chunk_elems == 0) o.chunk_elems = chunk[op];
   return o;
 }
 
@@ -181,9 +196,12 @@ int64_t skip_to(uintptr_t addr, int64_t esize, uintptr_t align) {
 
 }  // namespace
 
-void rs_call_table(const Geometry& g, const std::vector<Seg>& segs, const uint16_t* const* grads,
+void rs_call_table(const Geometry& g, const std::vector<Seg>& segs, const void* const* grads, bool f32,
                    float* const* out, std::vector<CallHdr>* hdr, std::vector<const void*>* ptrs) {
   const int32_t W = g.world, P = g.nparams;
+  // a vector group of 4 elements: 8-byte bf16 or 16-byte fp32 source loads
+  const int64_t esize = f32 ? 4 : 2;
+  const uintptr_t salign = uintptr_t(4 * esize);
   hdr->resize(segs.size());
   ptrs->assign(segs.size() * size_t(W + 1), nullptr);
   for (size_t s = 0; s < segs.size(); ++s) {
@@ -196,16 +214,17 @@ void rs_call_table(const Geometry& g, const std::vector<Seg>& segs, const uint16
     if (sg.kind == kZero) {
       head = int32_t(skip_to(d, 4, 16));  // 16-byte zero stores
     } else {
-      // 8-byte source loads and 16-byte destination stores, 4 elements each
-      const uint16_t* s0 = grads[int64_t(0) * P + sg.src_idx] + sg.src_off;
-      const uintptr_t phase = reinterpret_cast<uintptr_t>(s0) & 7;
+      // source loads of one group and 16-byte destination stores
+      const uintptr_t s0 = reinterpret_cast<uintptr_t>(grads[sg.src_idx]) + uintptr_t(sg.src_off * esize);
+      const uintptr_t phase = s0 & (salign - 1);
       bool same = true;
       for (int32_t u = 0; u < W; ++u) {
-        const uint16_t* su = grads[int64_t(u) * P + sg.src_idx] + sg.src_off;
-        row[u] = su;
-        same = same && (reinterpret_cast<uintptr_t>(su) & 7) == phase;
+        const uintptr_t su = reinterpret_cast<uintptr_t>(grads[int64_t(u) * P + sg.src_idx]) +
+                             uintptr_t(sg.src_off * esize);
+        row[u] = reinterpret_cast<const void*>(su);
+        same = same && (su & (salign - 1)) == phase;
       }
-      const int64_t h = skip_to(reinterpret_cast<uintptr_t>(s0), 2, 8);
+      const int64_t h = skip_to(s0, esize, salign);
       if (same && ((d + uintptr_t(4 * h)) & 15) == 0) head = int32_t(h);
     }
     (*hdr)[s] = CallHdr{sg.len, sg.kind, head};
@@ -256,6 +275,30 @@ void ci_call_table(const Geometry& g, const std::vector<Seg>& segs, const void* 
       if (ps == (d & 15)) head = int32_t(skip_to(reinterpret_cast<uintptr_t>(src), 2, 16));
     }
     (*hdr)[s] = CallHdr{sg.len, kind, head};
+  }
+}
+
+void pk_call_table(const Geometry& g, const std::vector<Seg>& segs, const uint16_t* const* grads, float* packed,
+                   std::vector<CallHdr>* hdr, std::vector<const void*>* ptrs) {
+  (void)g;
+  hdr->resize(segs.size());
+  ptrs->assign(segs.size() * 2, nullptr);
+  for (size_t s = 0; s < segs.size(); ++s) {
+    const Seg& sg = segs[s];
+    float* dst = packed + sg.dst_off;
+    const uintptr_t d = reinterpret_cast<uintptr_t>(dst);
+    (*ptrs)[2 * s + 1] = dst;
+    int32_t head = -1;
+    if (sg.kind == kZero) {
+      head = int32_t(skip_to(d, 4, 16));  // 16-byte zero stores
+    } else {
+      const uint16_t* src = grads[sg.src_idx] + sg.src_off;
+      (*ptrs)[2 * s] = src;
+      // 8-byte bf16 loads feeding 16-byte fp32 stores: 4 elements
+      const int64_t h = skip_to(reinterpret_cast<uintptr_t>(src), 2, 8);
+      if (((d + uintptr_t(4 * h)) & 15) == 0) head = int32_t(h);
+    }
+    (*hdr)[s] = CallHdr{sg.len, sg.kind, head};
   }
 }
 

@@ -26,17 +26,20 @@ constexpr int32_t kCoWgPerCu = 1;
 constexpr int64_t kCoChunk = 4096;
 constexpr int32_t kCiWgPerCu = 2;    // the copy-in's cast body wants more waves in flight
 constexpr int64_t kCiChunk = 2048;
+constexpr int32_t kPkWgPerCu = 2;    // the stock pack (bf16 -> fp32 widening copy)
+constexpr int64_t kPkChunk = 2048;
 
 enum SegKind : int32_t { kSum = 0, kZero = 1, kCopy = 2, kCast = 3 };
-enum Op : int32_t { kOpRs = 0, kOpCo = 1, kOpCi = 2 };
+enum Op : int32_t { kOpRs = 0, kOpCo = 1, kOpCi = 2, kOpPack = 3 };
+constexpr int kNumOps = 4;
 
 // One contiguous run of work, fixed by the plan (host only).
 struct Seg {
   int64_t src_off;  // element offset into each source tensor
   int64_t dst_off;  // element offset into the destination tensor
   int64_t len;      // elements, > 0
-  int32_t src_idx;  // reduce-scatter: parameter p; copy-out: 0
-  int32_t dst_idx;  // reduce-scatter: destination rank r; copy-out: parameter p
+  int32_t src_idx;  // reduce-scatter, pack: parameter p; copy-out: 0; copy-in: shard r*P + p
+  int32_t dst_idx;  // reduce-scatter: destination rank r; copy-out: parameter p; copy-in, pack: 0
   int32_t kind;     // SegKind
 };
 
@@ -73,9 +76,13 @@ int64_t real_elems(const Geometry& g, int32_t p, int32_t r);
 //  copy-in: a kCopy segment of the real elements of each (p, r) (the kind
 //    becomes kCast per call for fp32 shards) and a kZero segment of the
 //    slot's padding.
+//  stock pack (one rank's gradients into the rank-major fp32 buffer): a kCopy
+//    (widening) segment of the rows of each (p, r) and a kZero segment of the
+//    slot's padding.
 std::vector<Seg> rs_segments(const Geometry& g);
 std::vector<Seg> copyout_segments(const Geometry& g);
 std::vector<Seg> copyin_segments(const Geometry& g);
+std::vector<Seg> pack_segments(const Geometry& g);
 
 // chunk_begin[s] = index of segment s's first chunk, chunk_begin[nseg] = total;
 // segment s owns ceil(len / chunk) chunks.  Fails (TIDE_ERR_RANGE) when the
@@ -88,13 +95,15 @@ tide_status check_options(const tide_options* in, tide_options* out, std::string
 tide_options effective_options(const tide_options& given, Op op, int32_t cu_count);
 
 // Per-call tables.  Vector groups are 4 elements for the reduce-scatter
-// (8-byte bf16 loads, 16-byte fp32 stores) and 8 elements for the copy-out
-// (16-byte loads and stores).  A segment gets a vector body when every source
-// and the destination reach their group alignment at the same element.
+// (8-byte bf16 or 16-byte fp32 loads, 16-byte fp32 stores) and 8 elements for
+// the copy-out (16-byte loads and stores).  A segment gets a vector body when
+// every source and the destination reach their group alignment at the same
+// element.
 //  reduce-scatter: ptrs per segment = [W source pointers at the segment's
 //    first element, destination pointer]; zero segments have null sources.
+//    `grads` are uint16_t (bf16) or float pointers, as `f32` says.
 //  copy-out: ptrs per segment = [source, destination].
-void rs_call_table(const Geometry& g, const std::vector<Seg>& segs, const uint16_t* const* grads,
+void rs_call_table(const Geometry& g, const std::vector<Seg>& segs, const void* const* grads, bool f32,
                    float* const* out, std::vector<CallHdr>* hdr, std::vector<const void*>* ptrs);
 void co_call_table(const Geometry& g, const std::vector<Seg>& segs, const uint16_t* rank_major,
                    uint16_t* const* params, std::vector<CallHdr>* hdr, std::vector<const void*>* ptrs);
@@ -103,6 +112,10 @@ void co_call_table(const Geometry& g, const std::vector<Seg>& segs, const uint16
 //    for bf16 shards and for padding (16-byte accesses).
 void ci_call_table(const Geometry& g, const std::vector<Seg>& segs, const void* const* shards, bool f32,
                    uint16_t* rank_major, std::vector<CallHdr>* hdr, std::vector<const void*>* ptrs);
+//  stock pack: ptrs per segment = [gradient (null for padding), destination];
+//    groups of 4 elements (8-byte bf16 loads, 16-byte fp32 stores).
+void pk_call_table(const Geometry& g, const std::vector<Seg>& segs, const uint16_t* const* grads, float* packed,
+                   std::vector<CallHdr>* hdr, std::vector<const void*>* ptrs);
 
 // Device-side launch arguments (kernels.hip).
 struct KernelArgs {
@@ -110,16 +123,19 @@ struct KernelArgs {
   const void* const* ptrs;  // [nseg * (nsrc + 1)]
   const int32_t* chunk_begin;  // [nseg + 1]
   int32_t nseg;
-  int32_t nsrc;  // W (reduce-scatter) or 1 (copy-out)
+  int32_t nsrc;  // W (reduce-scatter) or 1 (the copies)
   int32_t nchunks;
   int32_t chunk;  // elements per chunk
   uint32_t flags;
+  float alpha;         // reduce-scatter only: Equation 5's scale
+  int32_t accumulate;  // reduce-scatter only: add into the shards' old values
 };
 
 // Launch with `grid` workgroups of kThreads on `stream`; returns the launch
 // status (hipError_t as int).
-int launch_rs_local(const KernelArgs& a, int64_t grid, void* stream);
+int launch_rs_local(const KernelArgs& a, bool f32, int64_t grid, void* stream);
 int launch_ag_copyout(const KernelArgs& a, int64_t grid, void* stream);
 int launch_ag_copyin(const KernelArgs& a, bool f32, int64_t grid, void* stream);
+int launch_stock_pack(const KernelArgs& a, int64_t grid, void* stream);
 
 }  // namespace tide

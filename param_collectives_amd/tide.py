@@ -1,7 +1,7 @@
 """Python binding of libtide (include/tide.h): argument marshalling only.
 
-Every step of the reduce-scatter local stage and the all-gather copy-out runs
-in the HIP library; this module turns torch tensors into device pointers and
+Every step of the reduce-scatter local stage, the all-gather copy-out and
+copy-in, and the stock gradient pack runs in the HIP library; this module turns torch tensors into device pointers and
 the current HIP stream, checks that each tensor has the size, dtype, device
 and contiguity the plan expects (so that no kernel is launched on a buffer
 smaller than the plan assumes), and raises on a non-zero status.  There is no
@@ -41,6 +41,8 @@ EXPORTS = (
     "tide_reduce_scatter_local",
     "tide_allgather_copyout",
     "tide_allgather_copyin",
+    "tide_reduce_scatter_local_f32",
+    "tide_stock_chunk_cat",
     "tide_plan_destroy",
     "tide_last_error",
 )
@@ -72,6 +74,8 @@ def _load():
     lib.tide_reduce_scatter_local.argtypes = [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.c_float, i32, vp]
     lib.tide_allgather_copyout.argtypes = [vp, vp, ctypes.POINTER(vp), vp]
     lib.tide_allgather_copyin.argtypes = [vp, ctypes.POINTER(vp), i32, vp, vp]
+    lib.tide_reduce_scatter_local_f32.argtypes = lib.tide_reduce_scatter_local.argtypes
+    lib.tide_stock_chunk_cat.argtypes = [vp, ctypes.POINTER(vp), vp, vp]
     lib.tide_plan_destroy.argtypes = [vp]
     lib.tide_plan_destroy.restype = None
     lib.tide_last_error.argtypes = []
@@ -125,8 +129,9 @@ class Plan:
                         for p, s in enumerate(self.shapes)] for r in range(self.world)]
 
     def segments(self, op):
-        """The work segments (op 0: reduce-scatter, 1: copy-out) as an int64
-        array of rows (kind, src_idx, dst_idx, src_off, dst_off, len)."""
+        """The work segments (op 0: reduce-scatter, 1: copy-out, 2: copy-in,
+        3: stock pack) as an int64 array of rows (kind, src_idx, dst_idx,
+        src_off, dst_off, len)."""
         count = ctypes.c_int64()
         _check(lib.tide_plan_segments(self.handle, int(op), None, 0, ctypes.byref(count)))
         table = np.zeros((max(count.value, 1), 6), dtype=np.int64)
@@ -139,7 +144,8 @@ class Plan:
         _check(lib.tide_plan_set_options(self.handle, ctypes.byref(opt)))
 
     def options(self, op=0):
-        """Effective launch knobs for op 0 (reduce-scatter) or 1 (copy-out)."""
+        """Effective launch knobs for op 0 (reduce-scatter), 1 (copy-out),
+        2 (copy-in) or 3 (stock pack)."""
         opt = Options()
         _check(lib.tide_plan_get_options(self.handle, int(op), ctypes.byref(opt)))
         return {"cu_budget": opt.cu_budget, "wg_per_cu": opt.wg_per_cu, "chunk_elems": opt.chunk_elems,
@@ -158,11 +164,19 @@ class Plan:
 
     # ------------------------------------------------------------ raw calls
 
-    def reduce_scatter_local_raw(self, grad_ptrs, out_ptrs, alpha=1.0, accumulate=0, stream=0):
-        """tide_reduce_scatter_local on raw device addresses: grad_ptrs[u*P+p],
+    def reduce_scatter_local_raw(self, grad_ptrs, out_ptrs, alpha=1.0, accumulate=0, stream=0, f32=False):
+        """tide_reduce_scatter_local (bf16 gradients) or, with f32=True,
+        tide_reduce_scatter_local_f32 on raw device addresses: grad_ptrs[u*P+p],
         out_ptrs[r] (ints), stream a hipStream_t handle (int)."""
-        _check(lib.tide_reduce_scatter_local(self.handle, _ptr_array(grad_ptrs), _ptr_array(out_ptrs),
-                                             float(alpha), int(accumulate), ctypes.c_void_p(int(stream) or None)))
+        fn = lib.tide_reduce_scatter_local_f32 if f32 else lib.tide_reduce_scatter_local
+        _check(fn(self.handle, _ptr_array(grad_ptrs), _ptr_array(out_ptrs), float(alpha), int(accumulate),
+                  ctypes.c_void_p(int(stream) or None)))
+
+    def stock_chunk_cat_raw(self, grad_ptrs, packed_ptr, stream=0):
+        """tide_stock_chunk_cat on raw device addresses (grad_ptrs[p] of one
+        rank, packed_ptr to W*S fp32 elements)."""
+        _check(lib.tide_stock_chunk_cat(self.handle, _ptr_array(grad_ptrs), ctypes.c_void_p(int(packed_ptr) or None),
+                                        ctypes.c_void_p(int(stream) or None)))
 
     def allgather_copyin_raw(self, shard_ptrs, shard_dtype, rank_major_ptr, stream=0):
         """tide_allgather_copyin on raw device addresses (shard_ptrs[r*P+p])."""
@@ -214,6 +228,8 @@ class Call:
 
 
 def _rs_checked(plan, grads, outs):
+    """Checks the tensors of a reduce-scatter; returns (gradient pointers,
+    output pointers, whether the gradients are fp32)."""
     import torch
 
     W, P = plan.world, len(plan.shapes)
@@ -221,29 +237,62 @@ def _rs_checked(plan, grads, outs):
         raise ValueError(f"grads must be {W} lists of {P} tensors")
     if len(outs) != W:
         raise ValueError(f"outs must hold {W} tensors")
+    dtypes = {t.dtype for row in grads for t in row}
+    if dtypes not in ({torch.float32}, {torch.bfloat16}):
+        raise TypeError(f"grads must be all torch.bfloat16 or all torch.float32, got {dtypes}")
+    dtype = dtypes.pop()
     ptrs = []
     for u in range(W):
         for p in range(P):
-            _require(grads[u][p], torch.bfloat16, plan.numel[p], f"grads[{u}][{p}]")
+            _require(grads[u][p], dtype, plan.numel[p], f"grads[{u}][{p}]")
             ptrs.append(grads[u][p].data_ptr())
     for r in range(W):
         _require(outs[r], torch.float32, plan.shard_elems, f"outs[{r}]")
-    return ptrs, [o.data_ptr() for o in outs]
+    return ptrs, [o.data_ptr() for o in outs], dtype == torch.float32
 
 
 def reduce_scatter_call(plan, grads, outs, alpha=1.0, accumulate=False):
     """A registered reduce-scatter (see reduce_scatter_local)."""
-    g, o = _rs_checked(plan, grads, outs)
-    return Call(lib.tide_reduce_scatter_local,
-                (plan.handle, _ptr_array(g), _ptr_array(o), ctypes.c_float(alpha), int(bool(accumulate))),
+    g, o, f32 = _rs_checked(plan, grads, outs)
+    fn = lib.tide_reduce_scatter_local_f32 if f32 else lib.tide_reduce_scatter_local
+    return Call(fn, (plan.handle, _ptr_array(g), _ptr_array(o), ctypes.c_float(alpha), int(bool(accumulate))),
                 (plan, grads, outs))
 
 
 def reduce_scatter_local(plan, grads, outs, alpha=1.0, accumulate=False, stream=None):
-    """Reduce-scatter local stage: grads[u][p] (bf16, plan.shapes[p]) for u in
-    [0, W) -> outs[r] (fp32, plan.shard_elems elements) for r in [0, W)."""
-    g, o = _rs_checked(plan, grads, outs)
-    plan.reduce_scatter_local_raw(g, o, alpha, int(bool(accumulate)), _stream_handle(stream))
+    """Reduce-scatter local stage: grads[u][p] (all bf16 or all fp32,
+    plan.shapes[p]) for u in [0, W) -> outs[r] (fp32, plan.shard_elems
+    elements) for r in [0, W): outs[r] = alpha * (sum over u in rank order),
+    added to the old outs[r] when accumulate is true."""
+    g, o, f32 = _rs_checked(plan, grads, outs)
+    plan.reduce_scatter_local_raw(g, o, alpha, int(bool(accumulate)), _stream_handle(stream), f32=f32)
+
+
+def _pk_checked(plan, grads, packed):
+    import torch
+
+    P = len(plan.shapes)
+    if len(grads) != P:
+        raise ValueError(f"grads must hold {P} tensors (one rank's gradients)")
+    for p in range(P):
+        _require(grads[p], torch.bfloat16, plan.numel[p], f"grads[{p}]")
+    _require(packed, torch.float32, plan.world * plan.shard_elems, "packed")
+    return [t.data_ptr() for t in grads], packed.data_ptr()
+
+
+def stock_chunk_cat_call(plan, grads, packed):
+    """A registered stock gradient pack (see stock_chunk_cat)."""
+    g, pk = _pk_checked(plan, grads, packed)
+    return Call(lib.tide_stock_chunk_cat, (plan.handle, _ptr_array(g), ctypes.c_void_p(pk or None)),
+                (plan, grads, packed))
+
+
+def stock_chunk_cat(plan, grads, packed, stream=None):
+    """Stock gradient pack of one rank: grads[p] (bf16, plan.shapes[p]) ->
+    packed (fp32, W*S elements: rank r's rows of p at r*S + o_p, widened,
+    padding +0)."""
+    g, pk = _pk_checked(plan, grads, packed)
+    plan.stock_chunk_cat_raw(g, pk, _stream_handle(stream))
 
 
 def _co_checked(plan, rank_major, params):

@@ -20,7 +20,8 @@ Device (torch on the GPU; full-size workloads):
   * rank u uses a ``torch.Generator`` on the device seeded with
     ``device_seed(c, u)``; values are float32 ``randn * sigma`` (times 100
     where ``rand < 0.01`` with ``outliers``), rounded once to bf16 by torch's
-    float32 -> bfloat16 conversion (round to nearest even).
+    float32 -> bfloat16 conversion (round to nearest even); fp32 gradients
+    are the same float32 values, not rounded.
 Both recipes give N(0, sigma^2) bf16 values; the GPU path and the oracle
 always receive the same bytes, whichever recipe made them.
 """

@@ -53,9 +53,13 @@ def device_seed(c: int, u: int) -> int:
                & np.uint64(0x7FFFFFFFFFFFFFFF))
 
 
-def grads_device(w: Workload, device, seed_index=None):
-    """grads[u][p]: torch bf16 tensors on ``device``, generated there."""
+def grads_device(w: Workload, device, seed_index=None, dtype=None):
+    """grads[u][p]: torch tensors on ``device``, generated there: bf16 (the
+    default) or, with ``dtype=torch.float32``, the float32 values before the
+    bf16 rounding."""
     import torch
+
+    dtype = torch.bfloat16 if dtype is None else dtype
 
     c = w.index if seed_index is None else seed_index
     out = []
@@ -69,7 +73,7 @@ def grads_device(w: Workload, device, seed_index=None):
             if w.outliers:
                 m = torch.rand(n, generator=g, device=device, dtype=torch.float32) < 0.01
                 v = torch.where(m, v * 100.0, v)
-            row.append(v.to(torch.bfloat16).reshape(w.shapes[p]))
+            row.append(v.to(dtype).reshape(w.shapes[p]))
             del v
         out.append(row)
     return out

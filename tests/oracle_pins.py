@@ -124,23 +124,28 @@ def check_landing_is_padded_parameter(orc, seed=2):
 # --------------------------------------------------------- reduce-scatter
 
 
+def stock_fsdp2_pack(W, shapes, grads_u):
+    """Stock FSDP2's packed fp32 input of one source rank: every parameter
+    zero-padded to W*R_p rows and widened (fp32 taken as is), then rank r's
+    rows of every parameter concatenated, ranks one after the other."""
+    pieces_by_dest = [[] for _ in range(W)]
+    for p, shape in enumerate(shapes):
+        D = shape[0]
+        K = int(np.prod(shape[1:], dtype=np.int64))
+        R = -(-D // W)
+        a = np.asarray(grads_u[p])
+        g = (a.astype(np.float32) if a.dtype == np.float32 else f32_from_bf16(a)).reshape(D, K)
+        padded = np.zeros((W * R, K), dtype=np.float32)
+        padded[:D] = g
+        for r in range(W):
+            pieces_by_dest[r].append(padded[r * R:(r + 1) * R].reshape(-1))
+    return np.concatenate([np.concatenate(pc) if pc else np.zeros(0, np.float32) for pc in pieces_by_dest])
+
+
 def stock_fsdp2_reduce_scatter(W, shapes, grads):
     """Brute force by the stock path: pad, widen, pack rank-major, then sum
     the W packed buffers in rank order and give rank r its S-element slice."""
-    packed = []
-    for u in range(W):
-        pieces_by_dest = [[] for _ in range(W)]
-        for p, shape in enumerate(shapes):
-            D = shape[0]
-            K = int(np.prod(shape[1:], dtype=np.int64))
-            R = -(-D // W)
-            g = f32_from_bf16(grads[u][p]).reshape(D, K)
-            padded = np.zeros((W * R, K), dtype=np.float32)
-            padded[:D] = g
-            for r in range(W):
-                pieces_by_dest[r].append(padded[r * R:(r + 1) * R].reshape(-1))
-        packed.append(np.concatenate([np.concatenate(pc) if pc else np.zeros(0, np.float32)
-                                      for pc in pieces_by_dest]))
+    packed = [stock_fsdp2_pack(W, shapes, grads[u]) for u in range(W)]
     total = packed[0].copy()
     for u in range(1, W):
         total = total + packed[u]
@@ -519,6 +524,95 @@ def check_copyin_f32_is_cast_then_stock_pack(orc, seed=16):
         assert np.array_equal(rm, want), (W, shapes)
 
 
+# ------------------------------------------ Equation 5 in full, stock pack
+
+
+def rand_f32(rng, shape, scale=1.0):
+    return (rng.standard_normal(int(np.prod(shape, dtype=np.int64))) * scale).astype(np.float32).reshape(shape)
+
+
+def check_rs_ex_defaults_are_the_base_case(orc, seed=17):
+    rng = np.random.default_rng(seed)
+    for W in (1, 3, 4, 8):
+        shapes = random_case(rng, W, 4)
+        grads = [[rand_bf16(rng, s) for s in shapes] for _ in range(W)]
+        base = orc.rs_local(W, shapes, grads)
+        ex = orc.rs_local_ex(W, shapes, grads)
+        for r in range(W):
+            assert same_bits(base[r], ex[r])
+
+
+def check_rs_ex_fp32_grads(orc, seed=18):
+    """fp32 gradients: the stock path's sum, and the bf16 path's result when
+    every value is a bf16 value."""
+    rng = np.random.default_rng(seed)
+    for W in (2, 4, 8):
+        shapes = random_case(rng, W, 4)
+        grads = [[rand_f32(rng, s, scale=float(rng.choice([1e-3, 1.0, 1e3]))) for s in shapes] for _ in range(W)]
+        got = orc.rs_local_ex(W, shapes, grads)
+        want = stock_fsdp2_reduce_scatter(W, shapes, grads)
+        for r in range(W):
+            assert same_bits(got[r], want[r])
+        bgrads = [[rand_bf16(rng, s) for s in shapes] for _ in range(W)]
+        as_f32 = [[f32_from_bf16(g).reshape(g.shape) for g in row] for row in bgrads]
+        a, b = orc.rs_local(W, shapes, bgrads), orc.rs_local_ex(W, shapes, as_f32)
+        for r in range(W):
+            assert same_bits(a[r], b[r])
+
+
+def check_rs_ex_alpha(orc, seed=19):
+    """alpha = 2^k scales exactly; alpha = -1 flips every sign (padding
+    becomes -0); any alpha is one binary32 product of the sum."""
+    rng = np.random.default_rng(seed)
+    W = 4
+    shapes = [(2 * W + 1, 5), (7,), (1, 3)]
+    grads = [[rand_bf16(rng, s) for s in shapes] for _ in range(W)]
+    base = orc.rs_local(W, shapes, grads)
+    for k in (-3, 1, 5):
+        got = orc.rs_local_ex(W, shapes, grads, alpha=2.0 ** k)
+        for r in range(W):
+            assert same_bits(got[r], base[r] * np.float32(2.0 ** k))
+    neg = orc.rs_local_ex(W, shapes, grads, alpha=-1.0)
+    for r in range(W):
+        assert np.array_equal(neg[r].view(np.uint32), base[r].view(np.uint32) ^ np.uint32(0x80000000))
+    tenth = orc.rs_local_ex(W, shapes, grads, alpha=0.1)
+    for r in range(W):
+        assert same_bits(tenth[r], np.float32(0.1) * base[r])
+
+
+def check_rs_ex_accumulate(orc, seed=20):
+    rng = np.random.default_rng(seed)
+    for W in (2, 8):
+        shapes = random_case(rng, W, 4)
+        # integer values: the accumulated result is the exact integer sum
+        ints = [[rng.integers(-64, 65, size=s) for s in shapes] for _ in range(W)]
+        grads = [[(np.asarray(v, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16) for v in row]
+                 for row in ints]
+        geo = orc.plan(W, shapes)
+        old = [rng.integers(-1000, 1001, size=geo["S"]).astype(np.float32) for _ in range(W)]
+        base = orc.rs_local(W, shapes, grads)
+        got = orc.rs_local_ex(W, shapes, grads, alpha=1.0, accumulate=True, out=old)
+        for r in range(W):
+            assert np.array_equal(got[r].astype(np.int64), old[r].astype(np.int64) + base[r].astype(np.int64))
+        # general values: one product, then one sum, each rounded
+        fgrads = [[rand_bf16(rng, s) for s in shapes] for _ in range(W)]
+        fold = [rand_f32(rng, (geo["S"],)) for _ in range(W)]
+        fbase = orc.rs_local(W, shapes, fgrads)
+        got = orc.rs_local_ex(W, shapes, fgrads, alpha=0.25, accumulate=True, out=fold)
+        for r in range(W):
+            assert same_bits(got[r], fold[r] + np.float32(0.25) * fbase[r])
+
+
+def check_chunk_cat_matches_stock_pack(orc, seed=21):
+    rng = np.random.default_rng(seed)
+    for W in (1, 3, 4, 8):
+        shapes = random_case(rng, W, int(rng.integers(1, 6)))
+        g = [rand_bf16(rng, s) for s in shapes]
+        got = orc.chunk_cat(W, shapes, g)
+        want = stock_fsdp2_pack(W, shapes, g)
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
 ALL_CHECKS = [
     check_tiny_plan_golden,
     check_plan_invariants,
@@ -542,4 +636,9 @@ ALL_CHECKS = [
     check_cast_matches_torch_rne,
     check_copyin_bf16_equals_pack_and_round_trips,
     check_copyin_f32_is_cast_then_stock_pack,
+    check_rs_ex_defaults_are_the_base_case,
+    check_rs_ex_fp32_grads,
+    check_rs_ex_alpha,
+    check_rs_ex_accumulate,
+    check_chunk_cat_matches_stock_pack,
 ]

@@ -24,7 +24,7 @@ def tide():
 def header_functions():
     text = open(os.path.join(ROOT, "include", "tide.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(tide_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(tide_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_symbol(tide):
@@ -111,6 +111,51 @@ def _emulate_rs(plan, grads_f32):
     return outs
 
 
+def _emulate_pack(plan, grads_u):
+    """Walk the library's stock-pack segment table on the CPU."""
+    out = np.full(plan.world * plan.shard_elems, np.nan, dtype=np.float32)
+    for kind, p, _, so, do, n in plan.segments(3):
+        if kind == 1:
+            out[do:do + n] = 0.0
+        else:
+            out[do:do + n] = oracle_pins.f32_from_bf16(grads_u[p]).reshape(-1)[so:so + n]
+    return out
+
+
+@pytest.mark.parametrize("world,shapes", CASES)
+def test_pack_segments_describe_the_oracle_layout(tide, oracle_mod, world, shapes):
+    """The stock pack writes each (rank, parameter) slot of the rank-major fp32
+    buffer: the rank's rows of the parameter, then zeros for its padding."""
+    plan = tide.Plan(world, shapes)
+    geo = oracle_mod.plan(world, shapes)
+    pk = plan.segments(3)
+    assert np.all(pk[:, 5] > 0)
+    for p in range(len(shapes)):
+        for r in range(world):
+            real = geo["n_real"][p, r]
+            pad = geo["n"][p] - real
+            slot = geo["rank_major_offset"][p, r]
+            mine = pk[(pk[:, 1] == p) & (pk[:, 4] >= slot) & (pk[:, 4] < slot + geo["n"][p])]
+            copies, zeros = mine[mine[:, 0] == 2], mine[mine[:, 0] == 1]
+            assert len(copies) == (1 if real else 0) and len(zeros) == (1 if pad else 0)
+            if real:
+                assert tuple(copies[0, 3:]) == (r * geo["R"][p] * geo["K"][p], slot, real)
+            if pad:
+                assert tuple(zeros[0, 4:]) == (slot + real, pad)
+    assert pk[:, 5].sum() == world * geo["S"]  # the whole packed buffer is written
+
+
+def test_pack_table_walk_reproduces_oracle(tide, oracle_mod):
+    rng = np.random.default_rng(6)
+    for world, shapes in CASES[:5]:
+        if sum(int(np.prod(s)) for s in shapes) > 10**6:
+            continue
+        plan = tide.Plan(world, shapes)
+        grads_u = [oracle_pins.rand_bf16(rng, s) for s in shapes]
+        want = oracle_mod.chunk_cat(world, shapes, grads_u)
+        assert oracle_pins.same_bits(_emulate_pack(plan, grads_u), want)
+
+
 def test_segment_table_walk_reproduces_oracle(tide, oracle_mod):
     rng = np.random.default_rng(5)
     for world, shapes in CASES[:5]:
@@ -173,20 +218,42 @@ def test_reduce_scatter_argument_errors(tide):
     good_g = [FAKE + 0x1000 * i for i in range(W * P)]
     good_o = [FAKE + 0x100000 + 0x1000 * r for r in range(W)]
     cases = [
-        (dict(alpha=2.0), -6),
-        (dict(accumulate=1), -6),
+        (dict(accumulate=2), -1),
+        (dict(accumulate=-1), -1),
         (dict(grad_ptrs=good_g[:5] + [0] + good_g[6:]), -1),
         (dict(grad_ptrs=good_g[:5] + [FAKE + 1] + good_g[6:]), -3),
+        (dict(grad_ptrs=good_g[:5] + [FAKE + 2] + good_g[6:], f32=True), -3),
         (dict(out_ptrs=good_o[:2] + [0] + good_o[3:]), -1),
         (dict(out_ptrs=good_o[:2] + [FAKE + 2] + good_o[3:]), -3),
+        (dict(out_ptrs=good_o[:2] + [FAKE + 2] + good_o[3:], f32=True, alpha=-3.0), -3),
     ]
     for kw, status in cases:
-        args = dict(grad_ptrs=good_g, out_ptrs=good_o, alpha=1.0, accumulate=0)
+        args = dict(grad_ptrs=good_g, out_ptrs=good_o, alpha=1.0, accumulate=0, f32=False)
         args.update(kw)
         with pytest.raises(tide.TideError) as e:
-            plan.reduce_scatter_local_raw(args["grad_ptrs"], args["out_ptrs"], args["alpha"], args["accumulate"])
+            plan.reduce_scatter_local_raw(args["grad_ptrs"], args["out_ptrs"], args["alpha"], args["accumulate"],
+                                          f32=args["f32"])
         assert _status(e) == status, kw
         assert tide.lib.tide_last_error()
+
+
+def test_stock_pack_argument_errors(tide):
+    plan = tide.Plan(4, oracle_pins.TINY_SHAPES)
+    good = [FAKE + 0x1000 * i for i in range(4)]
+    for grads, packed, status in [
+        (good[:2] + [0] + good[3:], FAKE, -1),
+        (good[:2] + [FAKE + 1] + good[3:], FAKE, -3),
+        (good, 0, -1),
+        (good, FAKE + 2, -3),
+    ]:
+        with pytest.raises(tide.TideError) as e:
+            plan.stock_chunk_cat_raw(grads, packed)
+        assert _status(e) == status
+    # a parameter with no elements may be NULL; the call still fails on `packed`
+    plan = tide.Plan(2, [(0, 4), (3,)])
+    with pytest.raises(tide.TideError) as e:
+        plan.stock_chunk_cat_raw([0, FAKE], FAKE + 1)
+    assert _status(e) == -3
 
 
 def test_copyout_argument_errors(tide):
@@ -239,6 +306,14 @@ def test_options_round_trip_and_validation(tide):
     assert plan.options(0) == {"cu_budget": 0, "wg_per_cu": 1, "chunk_elems": 1024, "flags": 0}
     assert plan.options(1) == {"cu_budget": 0, "wg_per_cu": 1, "chunk_elems": 4096, "flags": 0}
     assert plan.options(2) == {"cu_budget": 0, "wg_per_cu": 2, "chunk_elems": 2048, "flags": 0}
+    assert plan.options(3) == {"cu_budget": 0, "wg_per_cu": 2, "chunk_elems": 2048, "flags": 0}
+    for bad in (-1, 4):
+        with pytest.raises(tide.TideError) as e:
+            plan.options(bad)
+        assert _status(e) == -1
+        with pytest.raises(tide.TideError) as e:
+            plan.segments(bad)
+        assert _status(e) == -1
 
 
 def test_too_many_chunks_is_a_range_error(tide):

@@ -62,9 +62,27 @@ MUTANTS = [
     ("copyin_wrong_destination_rank",
      "uint16_t* dst = j->rank_major_out + (int64_t)r * g->S + g->o[p];\n    const void* src = j->shards",
      "uint16_t* dst = j->rank_major_out + (int64_t)(g->W - 1 - r) * g->S + g->o[p];\n    const void* src = j->shards"),
+    ("alpha_dropped",
+     "float v = j->alpha * sum;", "float v = sum;"),
+    ("accumulate_ignored",
+     "dst[e] = j->accumulate ? dst[e] + v : v;", "dst[e] = v;"),
+    ("fp32_grads_read_as_bf16",
+     "if (j->grad_dtype == 1) return ((const float*)t)[i];", "if (j->grad_dtype == 2) return ((const float*)t)[i];"),
+    ("chunk_cat_padding_not_zero",
+     "dst[e] = (e < real) ? bf16_to_f32(src[e]) : 0.0f;", "dst[e] = (e < real) ? bf16_to_f32(src[e]) : 1.0f;"),
+    ("chunk_cat_rows_of_wrong_rank",
+     "const uint16_t* src = j->grads_one[p] + (int64_t)r * g->R[p] * g->K[p];",
+     "const uint16_t* src = j->grads_one[p] + (int64_t)(r > 0 ? r - 1 : 0) * g->R[p] * g->K[p];"),
     ("rs_source_row_offset_uses_real_count",
-     "int64_t first = (int64_t)r * g->R[p] * g->K[p];\n    float* dst",
-     "int64_t first = (int64_t)r * real;\n    float* dst"),
+     "int64_t first = (int64_t)r * g->R[p] * g->K[p];\n    float* dst = j->out[r] + g->o[p];\n"
+     "    for (int64_t e = 0; e < g->n[p]; ++e) {\n        if (e < real) {",
+     "int64_t first = (int64_t)r * real;\n    float* dst = j->out[r] + g->o[p];\n"
+     "    for (int64_t e = 0; e < g->n[p]; ++e) {\n        if (e < real) {"),
+    ("general_source_row_offset_uses_real_count",
+     "int64_t first = (int64_t)r * g->R[p] * g->K[p];\n    float* dst = j->out[r] + g->o[p];\n"
+     "    for (int64_t e = 0; e < g->n[p]; ++e) {\n        float sum",
+     "int64_t first = (int64_t)r * real;\n    float* dst = j->out[r] + g->o[p];\n"
+     "    for (int64_t e = 0; e < g->n[p]; ++e) {\n        float sum"),
 ]
 
 
