@@ -59,8 +59,12 @@ def parse_args(argv=None):
     ap.add_argument("--flags", type=int, default=0)
     ap.add_argument("--no-sweep", action="store_true", help="skip the CU-budget sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
-    ap.add_argument("--only", choices=["rs", "co", "ci", "calib"],
-                    help="launch just one kernel --launches times (for counter collection) and exit")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the Equation 5 epilogue and stock-path A/B sections (their reduce-scatter launches "
+                         "share the kernel name of the timed one)")
+    ap.add_argument("--only", choices=["rs", "co", "ci", "calib", "stock"],
+                    help="launch just one kernel (stock: the W packs and the fp32 reduce-scatter of the stock "
+                         "path) --launches times, for profiling, and exit")
     ap.add_argument("--launches", type=int, default=5)
     return ap.parse_args(argv)
 
@@ -131,8 +135,33 @@ def main(argv=None):
     def co():
         co_call(stream)
 
+    def stock_setup():
+        """The stock path's buffers and registered calls: W packs of W*S fp32
+        and the fp32 reduce-scatter of a (W, S) plan."""
+        pack_plan = tide.Plan(W, [(W, S)], **opts)
+        with torch.cuda.stream(stream):
+            packed = [torch.empty(W * S, dtype=torch.float32, device="cuda") for _ in range(W)]
+            stock_outs = [torch.empty(S, dtype=torch.float32, device="cuda") for _ in range(W)]
+        pack_calls = [tide.stock_chunk_cat_call(plan, grads[u], packed[u]) for u in range(W)]
+        red_call = tide.reduce_scatter_call(pack_plan, [[t.view(W, S)] for t in packed], stock_outs)
+        return pack_calls, red_call, stock_outs
+
+    # every rank: its gradients read, W*S fp32 written; then W packed buffers
+    # read and W shards written
+    pack_bytes = W * (2 * sum_dk + 4 * W * S)
+    red_bytes = 4 * W * W * S + 4 * W * S
+
     if args.only:
-        if args.only == "calib":
+        if args.only == "stock":
+            pack_calls, red_call, _ = stock_setup()
+            for _ in range(args.launches):
+                for c in pack_calls:
+                    c(stream)
+                red_call(stream)
+            stream.synchronize()
+            print(json.dumps({"only": "stock", "workload": w.name, "launches": args.launches,
+                              "pack_bytes_per_rank": pack_bytes // W, "reduce_bytes": red_bytes}))
+        elif args.only == "calib":
             n = W * S
             cplan = tide.Plan(1, [(n,)], **opts)
             dst = torch.empty(n, dtype=torch.bfloat16, device="cuda")
@@ -263,49 +292,48 @@ def main(argv=None):
         stream.synchronize()
         return [a.elapsed_time(b) for a, b in e]
 
-    # Equation 5's epilogue: alpha = 1/W, accumulating into separate shards
-    # (the timed outputs stay as they are for the parity check below); the
-    # shards are read as well: 4*W*S more bytes
-    with torch.cuda.stream(stream):
-        acc_outs = [torch.zeros(S, dtype=torch.float32, device="cuda") for _ in range(W)]
-    acc_call = tide.reduce_scatter_call(plan, grads, acc_outs, alpha=1.0 / W, accumulate=True)
-    kernels["rs_local_alpha_accumulate"] = kstats(timed(lambda: acc_call(stream)), rs_bytes + 4 * W * S)
-    del acc_outs, acc_call
-
-    # stock path A/B
-    pack_plan = tide.Plan(W, [(W, S)], **opts)
-    with torch.cuda.stream(stream):
-        packed = [torch.empty(W * S, dtype=torch.float32, device="cuda") for _ in range(W)]
-        stock_outs = [torch.empty(S, dtype=torch.float32, device="cuda") for _ in range(W)]
-    pack_calls = [tide.stock_chunk_cat_call(plan, grads[u], packed[u]) for u in range(W)]
-    red_call = tide.reduce_scatter_call(pack_plan, [[t.view(W, S)] for t in packed], stock_outs)
-    pack_bytes = W * (2 * sum_dk + 4 * W * S)  # every rank: its gradients read, W*S fp32 written
-    red_bytes = 4 * W * W * S + 4 * W * S      # W packed buffers read, W shards written
-    marks_ab = [(ev(), ev(), ev()) for _ in range(10)]
-    for c in pack_calls:
-        c(stream)
-    red_call(stream)
-    for a, b, c_ in marks_ab:
-        a.record(stream)
+    def stock_a_b(kstats, kernels):
+        """Stock path A/B: W packs then the fp32 reduce-scatter, against the
+        layout-aware reduce-scatter (same shards, checked bit for bit)."""
+        pack_calls, red_call, stock_outs = stock_setup()
+        marks_ab = [(ev(), ev(), ev()) for _ in range(10)]
         for c in pack_calls:
             c(stream)
-        b.record(stream)
         red_call(stream)
-        c_.record(stream)
-    stream.synchronize()
-    pk_ms = [a.elapsed_time(b) for a, b, _ in marks_ab]
-    rd_ms = [b.elapsed_time(c_) for _, b, c_ in marks_ab]
-    kernels["stock_pack_xW"] = kstats(pk_ms, pack_bytes)
-    kernels["rs_local_f32_packed"] = kstats(rd_ms, red_bytes)
-    same = all(torch.equal(stock_outs[r].view(torch.int32), outs[r].view(torch.int32)) for r in range(W))
-    stock_ms = kernels["stock_pack_xW"]["avg_ms"] + kernels["rs_local_f32_packed"]["avg_ms"]
-    stock_ab = {"stock_ms": round(stock_ms, 5), "layout_aware_ms": kernels["rs_local"]["avg_ms"],
-                "speedup": round(stock_ms / kernels["rs_local"]["avg_ms"], 3),
-                "stock_hbm_bytes": pack_bytes + red_bytes, "layout_aware_hbm_bytes": rs_bytes,
-                "extra_hbm_bytes": pack_bytes + red_bytes - rs_bytes, "extra_buffer_bytes": 4 * W * W * S,
-                "shards": "bit-identical" if same else "MISMATCH"}
-    del packed, stock_outs, pack_calls, red_call, pack_plan
+        for a, b, c_ in marks_ab:
+            a.record(stream)
+            for c in pack_calls:
+                c(stream)
+            b.record(stream)
+            red_call(stream)
+            c_.record(stream)
+        stream.synchronize()
+        pk_ms = [a.elapsed_time(b) for a, b, _ in marks_ab]
+        rd_ms = [b.elapsed_time(c_) for _, b, c_ in marks_ab]
+        kernels["stock_pack_xW"] = kstats(pk_ms, pack_bytes)
+        kernels["rs_local_f32_packed"] = kstats(rd_ms, red_bytes)
+        same = all(torch.equal(stock_outs[r].view(torch.int32), outs[r].view(torch.int32)) for r in range(W))
+        stock_ms = kernels["stock_pack_xW"]["avg_ms"] + kernels["rs_local_f32_packed"]["avg_ms"]
+        stock_ab = {"stock_ms": round(stock_ms, 5), "layout_aware_ms": kernels["rs_local"]["avg_ms"],
+                    "speedup": round(stock_ms / kernels["rs_local"]["avg_ms"], 3),
+                    "stock_hbm_bytes": pack_bytes + red_bytes, "layout_aware_hbm_bytes": rs_bytes,
+                    "extra_hbm_bytes": pack_bytes + red_bytes - rs_bytes, "extra_buffer_bytes": 4 * W * W * S,
+                    "shards": "bit-identical" if same else "MISMATCH"}
+        return stock_ab
 
+    stock_ab = None
+    if not args.no_extras:
+        # Equation 5's epilogue: alpha = 1/W, accumulating into separate shards
+        # (the timed outputs stay as they are for the parity check below); the
+        # shards are read as well: 4*W*S more bytes
+        with torch.cuda.stream(stream):
+            acc_outs = [torch.zeros(S, dtype=torch.float32, device="cuda") for _ in range(W)]
+        acc_call = tide.reduce_scatter_call(plan, grads, acc_outs, alpha=1.0 / W, accumulate=True)
+        kernels["rs_local_alpha_accumulate"] = kstats(timed(lambda: acc_call(stream)), rs_bytes + 4 * W * S)
+        del acc_outs, acc_call
+        stock_ab = stock_a_b(kstats, kernels)
+
+    # CPU oracle
     # CPU oracle on the same workload, and a bitwise check of this run's outputs
     cpu = None
     parity = None
@@ -370,7 +398,7 @@ def main(argv=None):
         "stock_ab": stock_ab,
     }
     print(json.dumps(line), flush=True)
-    if (parity and "MISMATCH" in parity.values()) or stock_ab["shards"] != "bit-identical":
+    if (parity and "MISMATCH" in parity.values()) or (stock_ab and stock_ab["shards"] != "bit-identical"):
         return 3
     return 0
 

@@ -287,42 +287,49 @@ struct Src<true> {
 
 // Equation 5's scale and accumulate, applied to a finished sum: one binary32
 // product, then (accumulating) one binary32 addition of the value already in
-// the shard.  EPI = false (alpha = 1, no accumulation): the sum is stored as
-// it is.  The choice is uniform over the grid and made once per chunk, so the
-// default path's loop carries no trace of the epilogue.
-struct Epilogue {
-  float alpha;
-  bool accumulate;
-};
+// the shard.  kPlain (alpha = 1, no accumulation) stores the sum as it is.
+// The mode is uniform over the grid and chosen once per chunk, so the default
+// path's loop carries no trace of the epilogue.  When accumulating, the old
+// shard values are loaded together with the sources, so their latency hides
+// behind the same wait.
+enum Epi : int { kPlain = 0, kScale = 1, kScaleAcc = 2 };
 
-template <bool CS, bool EPI>
-__device__ __forceinline__ void put4(float* d, const float a[4], const Epilogue& ep) {
-  if constexpr (!EPI) {
-    store<f32x4, CS>(d, f32x4{a[0], a[1], a[2], a[3]});
-    return;
+template <int EPI>
+__device__ __forceinline__ f32x4 old4(const float* d) {
+  if constexpr (EPI == kScaleAcc) {
+    return load<f32x4, true>(d);
+  } else {
+    return f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   }
-  float v[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) v[i] = ep.alpha * a[i];
-  if (ep.accumulate) {
-    const f32x4 o = load<f32x4, true>(d);
-    v[0] = o.x + v[0];
-    v[1] = o.y + v[1];
-    v[2] = o.z + v[2];
-    v[3] = o.w + v[3];
-  }
-  store<f32x4, CS>(d, f32x4{v[0], v[1], v[2], v[3]});
 }
 
-template <bool EPI>
-__device__ __forceinline__ void put1(float* d, float s, const Epilogue& ep) {
-  if constexpr (!EPI) {
-    store4(d, s);
-    return;
+template <bool CS, int EPI>
+__device__ __forceinline__ void put4(float* d, const float a[4], float alpha, f32x4 old) {
+  if constexpr (EPI == kPlain) {
+    store<f32x4, CS>(d, f32x4{a[0], a[1], a[2], a[3]});
+  } else {
+    float v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = alpha * a[i];
+    if constexpr (EPI == kScaleAcc) {
+      v[0] = old.x + v[0];
+      v[1] = old.y + v[1];
+      v[2] = old.z + v[2];
+      v[3] = old.w + v[3];
+    }
+    store<f32x4, CS>(d, f32x4{v[0], v[1], v[2], v[3]});
   }
-  float v = ep.alpha * s;
-  if (ep.accumulate) v = load4(d) + v;
-  store4(d, v);
+}
+
+template <int EPI>
+__device__ __forceinline__ void put1(float* d, float s, float alpha) {
+  if constexpr (EPI == kPlain) {
+    store4(d, s);
+  } else {
+    float v = alpha * s;
+    if constexpr (EPI == kScaleAcc) v = load4(d) + v;
+    store4(d, v);
+  }
 }
 
 // Sum of the W sources at element e (scalar path), rank order 0..W-1.
@@ -337,9 +344,9 @@ __device__ __forceinline__ float sum_one(const void* const* src, int32_t W, int6
 // source and the destination group-aligned there.  Lane l handles groups
 // l, l + 64, ...; kRsUnroll groups per step keep kRsUnroll*W independent loads
 // in flight; the remainder of a partial chunk goes one group per step.
-template <int WT, bool F32, bool CL, bool CS, bool EPI>
+template <int WT, bool F32, bool CL, bool CS, int EPI>
 __device__ __forceinline__ void sum_body(const void* const* src, int32_t W, float* dst, int64_t vlo, int64_t vhi,
-                                         const Epilogue& ep) {
+                                         float alpha) {
   using S = Src<F32>;
   using T = typename S::T;
   using V = typename S::V;
@@ -362,11 +369,13 @@ __device__ __forceinline__ void sum_body(const void* const* src, int32_t W, floa
     int64_t base = 0;
     for (; base + 64 * U <= ng; base += 64 * U) {
       V v[U][WT];
+      f32x4 o[U];
 #pragma unroll
       for (int k = 0; k < U; ++k) {
 #pragma unroll
         for (int u = 0; u < WT; ++u)
           v[k][u] = S::template buffer_load<CL ? 0 : kPolicyNT>(rs[u], int((base + g + 64 * k) * kGroupBytes));
+        o[k] = old4<EPI>(d + (base + g + 64 * k) * 4);
       }
 #pragma unroll
       for (int k = 0; k < U; ++k) {
@@ -374,18 +383,19 @@ __device__ __forceinline__ void sum_body(const void* const* src, int32_t W, floa
         S::first(v[k][0], a);
 #pragma unroll
         for (int u = 1; u < WT; ++u) S::add(v[k][u], a);
-        put4<CS, EPI>(d + (base + g + 64 * k) * 4, a, ep);
+        put4<CS, EPI>(d + (base + g + 64 * k) * 4, a, alpha, o[k]);
       }
     }
     for (int64_t gk = base + g; gk < ng; gk += 64) {
       V v[WT];
 #pragma unroll
       for (int u = 0; u < WT; ++u) v[u] = load<V, CL>(s[u] + gk * 4);
+      const f32x4 o = old4<EPI>(d + gk * 4);
       float a[4];
       S::first(v[0], a);
 #pragma unroll
       for (int u = 1; u < WT; ++u) S::add(v[u], a);
-      put4<CS, EPI>(d + gk * 4, a, ep);
+      put4<CS, EPI>(d + gk * 4, a, alpha, o);
     }
   } else {
     // Any W: sources in batches of 8, still added in rank order.
@@ -403,37 +413,37 @@ __device__ __forceinline__ void sum_body(const void* const* src, int32_t W, floa
         for (int k = 0; k < 8; ++k)
           if (k < nb) S::add(v[k], acc);
       }
-      put4<CS, EPI>(dst + e, acc, ep);
+      put4<CS, EPI>(dst + e, acc, alpha, old4<EPI>(dst + e));
     }
   }
 }
 
 // Padding rows: every rank contributes zeros there, so the sum is +0.
-template <bool CS, bool EPI>
-__device__ __forceinline__ void zero_rows(float* dst, const Chunk& c, const Epilogue& ep) {
+template <bool CS, int EPI>
+__device__ __forceinline__ void zero_rows(float* dst, const Chunk& c, float alpha) {
   const int lane = lane_id();
   const float z[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int64_t e = c.lo + lane; e < c.vlo; e += 64) put1<EPI>(dst + e, 0.0f, ep);
-  for (int64_t e = c.vhi + lane; e < c.hi; e += 64) put1<EPI>(dst + e, 0.0f, ep);
-  for (int64_t e = c.vlo + int64_t(lane) * 4; e < c.vhi; e += 256) put4<CS, EPI>(dst + e, z, ep);
+  for (int64_t e = c.lo + lane; e < c.vlo; e += 64) put1<EPI>(dst + e, 0.0f, alpha);
+  for (int64_t e = c.vhi + lane; e < c.hi; e += 64) put1<EPI>(dst + e, 0.0f, alpha);
+  for (int64_t e = c.vlo + int64_t(lane) * 4; e < c.vhi; e += 256) put4<CS, EPI>(dst + e, z, alpha, old4<EPI>(dst + e));
 }
 
 // One chunk of the reduce-scatter: the sum of a kSum segment's piece, or the
 // zeros of a padding piece.
-template <int WT, bool F32, bool CL, bool CS, bool EPI>
-__device__ __forceinline__ void rs_chunk(const Tables& a, const Desc<WT>& d, int32_t W, const Epilogue& ep) {
+template <int WT, bool F32, bool CL, bool CS, int EPI>
+__device__ __forceinline__ void rs_chunk(const Tables& a, const Desc<WT>& d, int32_t W, float alpha) {
   float* dst = static_cast<float*>(d.dst);
   const Chunk r = chunk_range(d.h, d.j, d.nch, a.chunk, 4);
   if (d.h.kind == tide::kZero) {
-    zero_rows<CS, EPI>(dst, r, ep);
+    zero_rows<CS, EPI>(dst, r, alpha);
     return;
   }
   // any W: the sources are read from the call table as needed
   const void* const* src = WT > 0 ? d.src : a.ptrs + int64_t(d.seg) * (a.nsrc + 1);
   const int lane = lane_id();
-  for (int64_t e = r.lo + lane; e < r.vlo; e += 64) put1<EPI>(dst + e, sum_one<F32>(src, W, e), ep);
-  for (int64_t e = r.vhi + lane; e < r.hi; e += 64) put1<EPI>(dst + e, sum_one<F32>(src, W, e), ep);
-  if (r.vhi > r.vlo) sum_body<WT, F32, CL, CS, EPI>(src, W, dst, r.vlo, r.vhi, ep);
+  for (int64_t e = r.lo + lane; e < r.vlo; e += 64) put1<EPI>(dst + e, sum_one<F32>(src, W, e), alpha);
+  for (int64_t e = r.vhi + lane; e < r.hi; e += 64) put1<EPI>(dst + e, sum_one<F32>(src, W, e), alpha);
+  if (r.vhi > r.vlo) sum_body<WT, F32, CL, CS, EPI>(src, W, dst, r.vlo, r.vhi, alpha);
 }
 
 template <int WT, bool F32, bool CL, bool CS, bool STAGED>
@@ -443,14 +453,13 @@ __global__ __launch_bounds__(tide::kThreads) void rs_local_kernel(const CallHdr*
                                                                   int32_t nseg, int32_t nsrc, int32_t nchunks,
                                                                   int32_t chunk, float alpha, int32_t accumulate) {
   const Tables a{hdr, ptrs, nseg, nsrc, nchunks, chunk};
-  const Epilogue ep{alpha, accumulate != 0};
-  const bool epi = !(alpha == 1.0f) || accumulate != 0;
+  const int epi = accumulate != 0 ? kScaleAcc : !(alpha == 1.0f) ? kScale : kPlain;
   const int32_t W = WT > 0 ? WT : nsrc;
   for_each_chunk<WT, STAGED>(a, chunk_begin, [&](const Desc<WT>& d) {
-    if (epi) {
-      rs_chunk<WT, F32, CL, CS, true>(a, d, W, ep);
-    } else {
-      rs_chunk<WT, F32, CL, CS, false>(a, d, W, ep);
+    switch (epi) {
+      case kPlain: rs_chunk<WT, F32, CL, CS, kPlain>(a, d, W, alpha); break;
+      case kScale: rs_chunk<WT, F32, CL, CS, kScale>(a, d, W, alpha); break;
+      default: rs_chunk<WT, F32, CL, CS, kScaleAcc>(a, d, W, alpha); break;
     }
   });
 }
@@ -567,8 +576,34 @@ __global__ __launch_bounds__(tide::kThreads) void ag_copyin_kernel(const CallHdr
   });
 }
 
+template <bool CL, bool CS>
+__device__ __forceinline__ void widen_group(const uint16_t* s, float* d) {
+  float v[4];
+  Src<false>::first(load<u32x2, CL>(s), v);
+  store<f32x4, CS>(d, f32x4{v[0], v[1], v[2], v[3]});
+}
+
+// Full steps of U groups of 4 bf16 per lane widened to fp32 (all loads
+// issued before the stores); returns where the steps stopped.
+template <int U, bool CL, bool CS>
+__device__ __forceinline__ int64_t widen_steps(const uint16_t* sv, float* dv, int64_t base, int64_t ng, int lane) {
+  for (; base + 64 * U <= ng; base += 64 * U) {
+    u32x2 v[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) v[k] = load<u32x2, CL>(sv + (base + lane + 64 * k) * 4);
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      float a[4];
+      Src<false>::first(v[k], a);
+      store<f32x4, CS>(dv + (base + lane + 64 * k) * 4, f32x4{a[0], a[1], a[2], a[3]});
+    }
+  }
+  return base;
+}
+
 // Stock gradient pack of one rank: its bf16 rows widened to fp32 (groups of
-// 4: 8-byte loads, 16-byte stores), padding rows +0.
+// 4: 8-byte loads, 16-byte stores; kCoUnroll groups in flight per lane, then
+// two, then one), padding rows +0.
 template <bool CL, bool CS, bool STAGED>
 __global__ __launch_bounds__(tide::kThreads) void stock_pack_kernel(const CallHdr* __restrict__ hdr,
                                                                     const void* const* __restrict__ ptrs,
@@ -589,12 +624,14 @@ __global__ __launch_bounds__(tide::kThreads) void stock_pack_kernel(const CallHd
     const uint16_t* src = static_cast<const uint16_t*>(d.src[0]);
     for (int64_t e = r.lo + lane; e < r.vlo; e += 64) store4(dst + e, bf16_to_f32(load2(src + e)));
     for (int64_t e = r.vhi + lane; e < r.hi; e += 64) store4(dst + e, bf16_to_f32(load2(src + e)));
+    if (r.vhi <= r.vlo) return;
+    const uint16_t* sv = src + r.vlo;
+    float* dv = dst + r.vlo;
     const int64_t ng = (r.vhi - r.vlo) >> 2;
-    for (int64_t gk = lane; gk < ng; gk += 64) {
-      float v[4];
-      Src<false>::first(load<u32x2, CL>(src + r.vlo + gk * 4), v);
-      store<f32x4, CS>(dst + r.vlo + gk * 4, f32x4{v[0], v[1], v[2], v[3]});
-    }
+    int64_t base = 0;
+    base = widen_steps<kCoUnroll, CL, CS>(sv, dv, base, ng, lane);
+    base = widen_steps<2, CL, CS>(sv, dv, base, ng, lane);
+    for (int64_t gk = base + lane; gk < ng; gk += 64) widen_group<CL, CS>(sv + gk * 4, dv + gk * 4);
   });
 }
 

@@ -1,11 +1,13 @@
-"""Collect and summarize rocprofv3 measurements of the two kernels.
+"""Collect and summarize rocprofv3 measurements of the kernels.
 
     python -m param_collectives_amd.profiling trace    --workload W --out DIR
     python -m param_collectives_amd.profiling counters --workload W --out DIR
     python -m param_collectives_amd.profiling summarize --workload W --out DIR --profiles profiles/
 
-`trace` runs bench.py under `rocprofv3 --kernel-trace --stats` (one
-process); `counters` runs one `rocprofv3 --pmc` pass per counter group (a
+`trace` runs bench.py under `rocprofv3 --kernel-trace --stats` twice: the
+timed step and the copy-in (with the sections whose reduce-scatter launches
+share the timed kernel's name left out), then the stock path alone (W stock
+packs and the fp32 reduce-scatter of the packed buffers); `counters` runs one `rocprofv3 --pmc` pass per counter group (a
 group never exceeds one hardware block's counter slots) on single-kernel
 launches of bench.py, including a calibration copy of known size;
 `summarize` reads those outputs and writes short text summaries and
@@ -33,7 +35,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 KERNEL_SOURCE = os.path.join(HERE, "csrc", "kernels.hip")
-KERNEL_REGEX = "rs_local_kernel|ag_copyout_kernel|ag_copyin_kernel"
+KERNEL_REGEX = "rs_local_kernel|ag_copyout_kernel|ag_copyin_kernel|stock_pack_kernel"
+KERNELS = ("rs_local_kernel", "ag_copyout_kernel", "ag_copyin_kernel", "stock_pack_kernel")
 COUNTER_PASSES = {
     "fetch": ["FETCH_SIZE"],
     "write": ["WRITE_SIZE"],
@@ -71,17 +74,20 @@ def bench_cmd(workload, extra):
 
 def collect_trace(workload, out, steps=10):
     os.makedirs(out, exist_ok=True)
-    cmd = ["rocprofv3", "--kernel-trace", "--stats", "-f", "csv", "-d", os.path.join(out, "trace"), "-o", "trace",
-           "--", *bench_cmd(workload, ["--steps", str(steps), "--warmup", "2", "--no-cpu-baseline", "--no-sweep"])]
-    _run(cmd, os.path.join(out, "trace.log"))
-    with open(os.path.join(out, "trace.cmd"), "w") as f:
-        f.write(_portable(" ".join(shlex.quote(c) for c in cmd), out) + "\n")
+    runs = {"trace": ["--steps", str(steps), "--warmup", "2", "--no-cpu-baseline", "--no-sweep", "--no-extras"],
+            "trace_stock": ["--only", "stock", "--launches", str(steps)]}
+    for name, extra in runs.items():
+        cmd = ["rocprofv3", "--kernel-trace", "--stats", "-f", "csv", "-d", os.path.join(out, name), "-o", name,
+               "--", *bench_cmd(workload, extra)]
+        _run(cmd, os.path.join(out, name + ".log"))
+        with open(os.path.join(out, name + ".cmd"), "w") as f:
+            f.write(_portable(" ".join(shlex.quote(c) for c in cmd), out) + "\n")
 
 
 def collect_counters(workload, out, launches=3):
     os.makedirs(out, exist_ok=True)
     cmds = {}
-    for only in ("rs", "co", "ci", "calib"):
+    for only in ("rs", "co", "ci", "calib", "stock"):
         for name, counters in COUNTER_PASSES.items():
             d = os.path.join(out, f"pmc_{only}_{name}")
             cmd = ["rocprofv3", "--pmc", *counters, "--kernel-include-regex", KERNEL_REGEX, "-f", "csv", "-d", d,
@@ -119,21 +125,21 @@ def _read_counter(d, counter):
 
 
 def _short(name):
-    for k in ("rs_local_kernel", "ag_copyout_kernel", "ag_copyin_kernel"):
+    for k in KERNELS:
         if k in name:
             return k
     return name[:60]
 
 
-def _kernel_stats(out):
-    files = glob.glob(os.path.join(out, "trace", "**", "*kernel_stats.csv"), recursive=True)
+def _kernel_stats(out, run="trace"):
+    files = glob.glob(os.path.join(out, run, "**", "*kernel_stats.csv"), recursive=True)
     rows = []
     for fn in files:
         with open(fn) as f:
             rows += list(csv.DictReader(f))
     if rows:
         return rows
-    dbs = glob.glob(os.path.join(out, "trace", "**", "*.db"), recursive=True)
+    dbs = glob.glob(os.path.join(out, run, "**", "*.db"), recursive=True)
     for db in dbs:
         con = sqlite3.connect(db)
         for name, calls, total, avg, pct in con.execute("select name, total_calls, total_duration, average, percentage "
@@ -145,26 +151,33 @@ def _kernel_stats(out):
 def summarize(workload, out, profiles):
     os.makedirs(profiles, exist_ok=True)
     digest = source_digest()
-    # kernel trace
-    stats = _kernel_stats(out)
-    lines = [f"# rocprofv3 kernel trace: {workload}", ""]
-    try:
-        lines.append("command (run in /tmp): " + _normalise(open(os.path.join(out, "trace.cmd")).read().strip()))
-    except OSError:
-        pass
-    lines.append(f"kernel source sha256: {digest}")
-    lines.append("")
-    lines.append(f"{'kernel':<22} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}")
-    for r in stats:
-        name = _short(r.get("Name", r.get("KernelName", "")))
-        if name not in ("rs_local_kernel", "ag_copyout_kernel", "ag_copyin_kernel"):
+    # kernel traces: the timed step (+ copy-in), then the stock path alone,
+    # whose reduce-scatter is the fp32 instance of rs_local_kernel
+    lines = [f"# rocprofv3 kernel trace: {workload}", "", f"kernel source sha256: {digest}"]
+    any_stats = False
+    for run, title in (("trace", "timed step (reduce-scatter from bf16 gradients, copy-out) and copy-in"),
+                       ("trace_stock", "stock path: W stock packs, then the reduce-scatter of the W packed fp32 "
+                                       "buffers (rs_local_kernel here is its fp32-source instance)")):
+        stats = _kernel_stats(out, run)
+        if not stats:
             continue
-        avg = float(r.get("AverageNs", 0)) / 1e3
-        mn = float(r.get("MinNs", 0) or 0) / 1e3
-        mx = float(r.get("MaxNs", 0) or 0) / 1e3
-        lines.append(f"{name:<22} {r.get('Calls', ''):>6} {avg:>10.2f} {mn:>10.2f} {mx:>10.2f} "
-                     f"{float(r.get('Percentage', 0)):>6.1f}")
-    if stats:
+        any_stats = True
+        lines += ["", f"## {title}"]
+        try:
+            lines.append("command (run in /tmp): " + _normalise(open(os.path.join(out, run + ".cmd")).read().strip()))
+        except OSError:
+            pass
+        lines.append(f"{'kernel':<22} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}")
+        for r in stats:
+            name = _short(r.get("Name", r.get("KernelName", "")))
+            if name not in KERNELS:
+                continue
+            avg = float(r.get("AverageNs", 0)) / 1e3
+            mn = float(r.get("MinNs", 0) or 0) / 1e3
+            mx = float(r.get("MaxNs", 0) or 0) / 1e3
+            lines.append(f"{name:<22} {r.get('Calls', ''):>6} {avg:>10.2f} {mn:>10.2f} {mx:>10.2f} "
+                         f"{float(r.get('Percentage', 0)):>6.1f}")
+    if any_stats:
         with open(os.path.join(profiles, f"kernel_trace_{workload}.txt"), "w") as f:
             f.write("\n".join(lines) + "\n")
     # counters
@@ -191,16 +204,22 @@ def summarize(workload, out, profiles):
            "bytes_written": calib_bytes, "fetch_kib": cf, "write_kib": cw,
            "fetch_factor": calib_bytes / (cf * 1024.0), "write_factor": calib_bytes / (cw * 1024.0)}
     kernels = {}
-    for only, kname, alg_r, alg_w in (("rs", "rs_local", 2 * w.world * sum_dk, 4 * w.world * S),
-                                      ("co", "ag_copyout", 2 * sum_dk, 2 * sum_dk),
-                                      ("ci", "ag_copyin", 4 * sum_dk, 2 * w.world * S)):
+    W = w.world
+    for only, kname, key, alg_r, alg_w in (("rs", "rs_local", "rs_local", 2 * W * sum_dk, 4 * W * S),
+                                           ("co", "ag_copyout", "ag_copyout", 2 * sum_dk, 2 * sum_dk),
+                                           ("ci", "ag_copyin", "ag_copyin", 4 * sum_dk, 2 * W * S),
+                                           ("stock", "stock_pack", "stock_pack", 2 * sum_dk, 4 * W * S),
+                                           ("stock", "rs_local", "rs_local_f32_packed", 4 * W * W * S, 4 * W * S)):
+        kname = kname + "_kernel"
+        if not os.path.isdir(os.path.join(cdir, f"pmc_{only}_fetch")):
+            continue
         f = med(only, "fetch", "FETCH_SIZE", kname)
         wr = med(only, "write", "WRITE_SIZE", kname)
         if f is None or wr is None:
             continue
         traffic_r = f * 1024.0 * cal["fetch_factor"]
         traffic_w = wr * 1024.0 * cal["write_factor"]
-        kernels[f"{kname}/{workload}"] = {
+        kernels[f"{key}/{workload}"] = {
             "fetch_kib": f, "write_kib": wr, "hbm_read_bytes": traffic_r, "hbm_write_bytes": traffic_w,
             "algorithmic_read_bytes": alg_r, "algorithmic_write_bytes": alg_w,
             "read_ratio": traffic_r / alg_r, "write_ratio": traffic_w / alg_w}
