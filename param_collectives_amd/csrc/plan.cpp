@@ -88,8 +88,8 @@ int64_t real_elems(const Geometry& g, int32_t p, int32_t r) {
 
 std::vector<Seg> rs_segments(const Geometry& g) {
   std::vector<Seg> segs;
-  for (int32_t p = 0; p < g.nparams; ++p) {
-    for (int32_t r = 0; r < g.world; ++r) {
+  for (int32_t r = 0; r < g.world; ++r) {
+    for (int32_t p = 0; p < g.nparams; ++p) {
       const int64_t real = real_elems(g, p, r);
       const int64_t src = int64_t(r) * g.n[p];  // first element of rows [r R_p, ...) in G_p
       if (real > 0) segs.push_back(Seg{src, g.o[p], real, p, r, kSum});
@@ -112,8 +112,8 @@ std::vector<Seg> copyout_segments(const Geometry& g) {
 
 std::vector<Seg> copyin_segments(const Geometry& g) {
   std::vector<Seg> segs;
-  for (int32_t p = 0; p < g.nparams; ++p) {
-    for (int32_t r = 0; r < g.world; ++r) {
+  for (int32_t r = 0; r < g.world; ++r) {
+    for (int32_t p = 0; p < g.nparams; ++p) {
       const int64_t real = real_elems(g, p, r);
       const int64_t slot = int64_t(r) * g.S + g.o[p];
       const int32_t shard = r * g.nparams + p;
@@ -126,8 +126,8 @@ std::vector<Seg> copyin_segments(const Geometry& g) {
 
 std::vector<Seg> pack_segments(const Geometry& g) {
   std::vector<Seg> segs;
-  for (int32_t p = 0; p < g.nparams; ++p) {
-    for (int32_t r = 0; r < g.world; ++r) {
+  for (int32_t r = 0; r < g.world; ++r) {
+    for (int32_t p = 0; p < g.nparams; ++p) {
       const int64_t real = real_elems(g, p, r);
       const int64_t slot = int64_t(r) * g.S + g.o[p];
       if (real > 0) segs.push_back(Seg{int64_t(r) * g.n[p], slot, real, p, 0, kCopy});

@@ -67,9 +67,13 @@ tide_status build_geometry(int32_t world, int32_t nparams, const int32_t* ndims,
 // Real (non-padding) elements of parameter p in rank r's shard.
 int64_t real_elems(const Geometry& g, int32_t p, int32_t r);
 
-// Segments are ordered parameter-major (p, then r), so that the chunks the
-// grid works on at any moment read consecutive row blocks of the same W
-// gradient tensors.
+// Segment order decides which tensors the grid streams through at any moment
+// (it works on a window of consecutive chunks).  Every operation is ordered so
+// that its destination is written front to back: the reduce-scatter, copy-in
+// and stock pack rank-major (r, then p: the slots of one destination rank are
+// contiguous), the copy-out parameter-major (p, then r: the row blocks of one
+// parameter are contiguous).  Measured on MI355X: one write stream per window
+// beats one read stream per window by 3-5% on layers of many small tensors.
 //  reduce-scatter: a kSum segment of the real elements and a kZero segment of
 //    the padding elements of each (p, r) (each only when non-empty);
 //  copy-out: a kCopy segment of the real elements of each (p, r).
