@@ -55,6 +55,8 @@ def _bind(lib):
     lib.oracle_rs_local_ex.restype = ctypes.c_int
     lib.oracle_chunk_cat.argtypes = [i32, i32, i32p, i64p, vpp, ctypes.c_void_p, i32]
     lib.oracle_chunk_cat.restype = ctypes.c_int
+    lib.oracle_axpb.argtypes = [ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_float, ctypes.c_void_p]
+    lib.oracle_axpb.restype = ctypes.c_int
     return lib
 
 
@@ -243,6 +245,14 @@ class Oracle:
         return out[: x.size]
 
 
+    def axpb(self, x, a, b):
+        """The elementwise victim: float32 y = a * x + b, two roundings."""
+        x = np.ascontiguousarray(x, dtype=np.float32).reshape(-1)
+        y = np.empty(max(x.size, 1), dtype=np.float32)
+        _check(self.lib.oracle_axpb(x.size, x.ctypes.data, float(a), float(b), y.ctypes.data), "oracle_axpb")
+        return y[: x.size]
+
+
 _default = None
 
 
@@ -283,3 +293,7 @@ def rs_local_ex(world, shapes, grads, alpha=1.0, accumulate=False, out=None, nth
 
 def chunk_cat(world, shapes, grads_u, nthreads=1):
     return _get().chunk_cat(world, shapes, grads_u, nthreads)
+
+
+def axpb(x, a, b):
+    return _get().axpb(x, a, b)

@@ -17,7 +17,9 @@
  *     - Section 4.3 "Numerical Semantics and Determinism": fp32 accumulation
  *       that never narrows a partial;
  *     - Section 3.1 "In-Place Shards and Paced Doubling": mixed-precision
- *       groups cast their fp32 shards to bf16 on the way into the all-gather.
+ *       groups cast their fp32 shards to bf16 on the way into the all-gather;
+ *     - Section 2.2 and Table 4: the memory-bound elementwise victim of the
+ *       interference measurements.
  *
  * Readings taken where the pages leave a step open (each is also listed with
  * the design notes of this repository):
@@ -41,12 +43,16 @@
  *     stays a quiet NaN of the same sign and top payload bits), and writes
  *     bf16 +0 into the padding;
  *   - a parameter must have at least one dimension; a 1-D parameter has
- *     K_p = 1; zero-sized dimensions are allowed.
+ *     K_p = 1; zero-sized dimensions are allowed;
+ *   - the pages name their elementwise victim without its operation; here it
+ *     is y = a * x + b over fp32 arrays, the product and the sum each rounded
+ *     to binary32 (no fused multiply-add).
  *
  * Pins: every function here is checked against hand-derived values, closed
  * forms, invariants and brute force by the CPU tests of this repository.
  */
 #include <float.h>
+#include <math.h>
 #include <pthread.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -585,4 +591,21 @@ int oracle_chunk_cat(int32_t W, int32_t P, const int32_t* ndims, const int64_t* 
     rc = run_tasks(j, chunk_cat_task, nthreads);
     geometry_free(&g);
     return rc;
+}
+
+/*
+ * oracle_axpb: the elementwise victim of the interference measurements
+ * (Section 2.2; Table 4's 256 MiB elementwise kernel), y[i] = a * x[i] + b,
+ * the product rounded to binary32 and then the sum rounded to binary32.
+ *   n  elements (>= 0); x, y  [n] (may be NULL only when n = 0)
+ */
+int oracle_axpb(int64_t n, const float* x, float a, float b, float* y) {
+    if (n < 0 || (n > 0 && (x == NULL || y == NULL))) return ORACLE_INVALID;
+    unsigned saved = ieee_mode_enter();
+    for (int64_t i = 0; i < n; ++i) {
+        volatile float prod = a * x[i]; /* one rounding, kept apart from the sum */
+        y[i] = prod + b;
+    }
+    ieee_mode_leave(saved);
+    return ORACLE_OK;
 }

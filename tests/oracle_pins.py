@@ -613,6 +613,46 @@ def check_chunk_cat_matches_stock_pack(orc, seed=21):
         assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
 
 
+# ---------------------------------------------------- interference victim
+
+
+def check_axpb_worked_golden(orc):
+    g = goldens.read("axpb_worked.txt")
+    cols = [np.array([int(r[i], 16) for r in g["axpb"]], dtype=np.uint32) for i in range(4)]
+    x, a, b, want = cols
+    for i in range(len(x)):
+        got = orc.axpb(x[i:i + 1].view(np.float32), a[i:i + 1].view(np.float32)[0], b[i:i + 1].view(np.float32)[0])
+        gb, wb = got.view(np.uint32)[0], want[i]
+        if np.isnan(want[i:i + 1].view(np.float32)[0]):
+            assert np.isnan(got[0]), (i, hex(gb))
+        else:
+            assert gb == wb, (i, hex(gb), hex(wb))
+
+
+def check_axpb_integers_are_exact(orc, seed=22):
+    """Small integers: every product and sum is exact, so the result is
+    integer arithmetic's."""
+    rng = np.random.default_rng(seed)
+    xi = rng.integers(-2**10, 2**10, size=10000)
+    for a, b in ((3, -7), (-1, 0), (0, 5), (1024, 1)):
+        got = orc.axpb(xi.astype(np.float32), a, b)
+        assert np.array_equal(got, (a * xi + b).astype(np.float32)), (a, b)
+
+
+def check_axpb_is_two_numpy_float32_operations(orc, seed=23):
+    """numpy's float32 multiply then float32 add (each one IEEE rounding) give
+    the same bits on random and special inputs."""
+    rng = np.random.default_rng(seed)
+    x = np.concatenate([(rng.standard_normal(100000) * 10.0 ** rng.integers(-44, 37, 100000)).astype(np.float32),
+                        np.array([0x00000001, 0x807FFFFF, 0x7F7FFFFF], dtype=np.uint32).view(np.float32)])
+    for a, b in ((np.float32(0.1), np.float32(0.7)), (np.float32(-3.5e38), np.float32(1e-30)),
+                 (np.float32(1.0 + 2 ** -12), np.float32(-1.0))):
+        with np.errstate(all="ignore"):
+            want = (x * a) + b
+        got = orc.axpb(x, a, b)
+        assert same_bits(got, want), (a, b)
+
+
 ALL_CHECKS = [
     check_tiny_plan_golden,
     check_plan_invariants,
@@ -641,4 +681,7 @@ ALL_CHECKS = [
     check_rs_ex_alpha,
     check_rs_ex_accumulate,
     check_chunk_cat_matches_stock_pack,
+    check_axpb_worked_golden,
+    check_axpb_integers_are_exact,
+    check_axpb_is_two_numpy_float32_operations,
 ]

@@ -83,6 +83,13 @@ MUTANTS = [
      "    for (int64_t e = 0; e < g->n[p]; ++e) {\n        float sum",
      "int64_t first = (int64_t)r * real;\n    float* dst = j->out[r] + g->o[p];\n"
      "    for (int64_t e = 0; e < g->n[p]; ++e) {\n        float sum"),
+    ("axpb_fused",
+     "volatile float prod = a * x[i]; /* one rounding, kept apart from the sum */\n        y[i] = prod + b;",
+     "y[i] = fmaf(a, x[i], b);"),
+    ("axpb_flushes_subnormals",
+     "unsigned saved = ieee_mode_enter();\n    for (int64_t i = 0; i < n; ++i) {\n        volatile float prod",
+     "unsigned saved = _mm_getcsr();\n    _mm_setcsr(saved | 0x8040u);\n    for (int64_t i = 0; i < n; ++i) {\n"
+     "        volatile float prod"),
 ]
 
 
