@@ -645,7 +645,7 @@ def check_axpb_is_two_numpy_float32_operations(orc, seed=23):
     rng = np.random.default_rng(seed)
     x = np.concatenate([(rng.standard_normal(100000) * 10.0 ** rng.integers(-44, 37, 100000)).astype(np.float32),
                         np.array([0x00000001, 0x807FFFFF, 0x7F7FFFFF], dtype=np.uint32).view(np.float32)])
-    for a, b in ((np.float32(0.1), np.float32(0.7)), (np.float32(-3.5e38), np.float32(1e-30)),
+    for a, b in ((np.float32(0.1), np.float32(0.7)), (np.float32(-3.0e38), np.float32(1e-30)),
                  (np.float32(1.0 + 2 ** -12), np.float32(-1.0))):
         with np.errstate(all="ignore"):
             want = (x * a) + b
