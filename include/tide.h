@@ -262,6 +262,69 @@ tide_status tide_allgather_copyin(tide_plan* plan, const void* const* shards, in
  */
 tide_status tide_stock_chunk_cat(tide_plan* plan, const uint16_t* const* grads, float* packed, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Interference instruments (Section 2.2 "SM Wave Quantization", Equation 4,
+ * Figure 3, Table 4 and Table 5): what one GPU can show of the cost a
+ * collective's kernels impose on the compute they overlap.  None of these
+ * touches a plan.
+ * ------------------------------------------------------------------------ */
+
+/*
+ * Properties of the current device: its CU count, the largest LDS allocation
+ * one workgroup may make and the LDS of one CU (bytes), and the rate of the
+ * constant wall clock the probe records (kHz).  Any output pointer may be
+ * NULL.
+ * Errors: TIDE_ERR_HIP.
+ */
+tide_status tide_device_info(int32_t* cu_count, int32_t* max_lds_per_workgroup, int32_t* lds_per_cu,
+                             int32_t* wall_clock_khz);
+
+/*
+ * Hardware-ID probe, the analog of the pages' SM-id probe (Table 5, Figure 3):
+ * `grid` workgroups of 256 threads, each allocating `lds_bytes` of LDS (so
+ * that at most floor(LDS per CU / lds_bytes) probe workgroups, and nothing
+ * else that needs the rest, share a CU), each holding its CU for `hold_ns`
+ * nanoseconds of wall-clock time and then writing one record of 8 uint32
+ * words to records[8*b .. 8*b+7]:
+ *   [0] b (the workgroup index)
+ *   [1] the wave's HW_ID hardware register (CDNA ISA: wave id bits 3:0, SIMD
+ *       id 5:4, pipe id 7:6, CU id 11:8, shader-array id 12, shader-engine
+ *       id 15:13, ...)
+ *   [2] the XCC_ID hardware register (accelerator-complex die id in bits 3:0)
+ *   [3] 0 when the workgroup's LDS read back what it wrote (or lds_bytes < 4)
+ *   [4],[5] entry time, [6],[7] exit time: wall-clock ticks (low, high word)
+ *   records    device pointer to grid*8 uint32, 4-byte aligned
+ *   grid       1 <= grid <= 65536
+ *   lds_bytes  0 <= lds_bytes <= max_lds_per_workgroup
+ *   hold_ns    0 <= hold_ns <= 1e9
+ * Errors: TIDE_ERR_INVALID, TIDE_ERR_ALIGN, TIDE_ERR_HIP.
+ */
+tide_status tide_probe_launch(uint32_t* records, int32_t grid, int32_t lds_bytes, int64_t hold_ns, void* stream);
+
+/*
+ * The memory-bound elementwise victim (Table 4's 256 MiB elementwise
+ * kernel; the pages do not give its operation): y[i] = a * x[i] + b for i in
+ * [0, n), the product rounded to binary32 and then the sum (no fused
+ * multiply-add), one thread per element or per group of four (16-byte
+ * accesses when x and y are 16-byte aligned and n is a multiple of 4).
+ *   x, y  device pointers to n fp32 elements, 4-byte aligned (may be NULL
+ *         when n = 0); y may equal x, other overlaps are not allowed.
+ * Errors: TIDE_ERR_INVALID, TIDE_ERR_ALIGN, TIDE_ERR_RANGE, TIDE_ERR_HIP.
+ */
+tide_status tide_victim_axpb(const float* x, float* y, int64_t n, float a, float b, void* stream);
+
+/*
+ * A stream of default priority for the current device.  cu_mask NULL: an
+ * ordinary non-blocking stream.  Otherwise the stream's kernels may only use
+ * the CUs whose bits are set (bit i of cu_mask[i / 32] is the runtime's CU i;
+ * mask_words >= ceil(cu_count / 32), at least one bit set): a hard CU budget,
+ * where tide_options.cu_budget only limits the grid.  *out_stream receives a
+ * hipStream_t, to be freed with tide_stream_destroy.
+ * Errors: TIDE_ERR_INVALID, TIDE_ERR_HIP.
+ */
+tide_status tide_stream_create(const uint32_t* cu_mask, int32_t mask_words, void** out_stream);
+tide_status tide_stream_destroy(void* stream); /* NULL is accepted */
+
 /* Free a plan and its device tables (waits for the device to finish using
  * them).  NULL is accepted. */
 void tide_plan_destroy(tide_plan* plan);

@@ -6,6 +6,9 @@
   allgather_copyout      rank-major bf16 buffer -> per-parameter tensors
   allgather_copyin       every rank's fp32/bf16 shards -> rank-major bf16 buffer
   stock_chunk_cat        stock FSDP2's gradient pack of one rank (the baseline)
+  probe, victim_axpb, Stream
+                         interference instruments: hardware-ID probe,
+                         elementwise victim, CU-masked streams
 
 The *_call variants check and marshal the tensors once and return a callable
 that launches with one library call (for buffers reused every step).
@@ -29,4 +32,9 @@ from .tide import (  # noqa: F401
     reduce_scatter_local,
     stock_chunk_cat,
     stock_chunk_cat_call,
+    Stream,
+    decode_probe,
+    device_info,
+    probe,
+    victim_axpb,
 )

@@ -39,6 +39,18 @@ tide_status hip_fail(hipError_t e, const char* what) {
   return fail(TIDE_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
+}  // namespace
+
+namespace tide {
+
+tide_status set_error(tide_status st, const std::string& msg) { return fail(st, msg); }
+
+void clear_error() { g_last_error.clear(); }
+
+}  // namespace tide
+
+namespace {
+
 // One host->device upload channel: a pinned staging buffer whose previous
 // copy must have finished before it is rewritten.
 struct Upload {

@@ -135,6 +135,11 @@ struct KernelArgs {
   int32_t accumulate;  // reduce-scatter only: add into the shards' old values
 };
 
+// The calling thread's error message (tide_last_error), shared by every
+// source file of the C ABI.  set_error stores `msg` and returns `st`.
+tide_status set_error(tide_status st, const std::string& msg);
+void clear_error();
+
 // Launch with `grid` workgroups of kThreads on `stream`; returns the launch
 // status (hipError_t as int).
 int launch_rs_local(const KernelArgs& a, bool f32, int64_t grid, void* stream);

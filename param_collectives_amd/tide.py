@@ -43,6 +43,11 @@ EXPORTS = (
     "tide_allgather_copyin",
     "tide_reduce_scatter_local_f32",
     "tide_stock_chunk_cat",
+    "tide_device_info",
+    "tide_probe_launch",
+    "tide_victim_axpb",
+    "tide_stream_create",
+    "tide_stream_destroy",
     "tide_plan_destroy",
     "tide_last_error",
 )
@@ -76,6 +81,12 @@ def _load():
     lib.tide_allgather_copyin.argtypes = [vp, ctypes.POINTER(vp), i32, vp, vp]
     lib.tide_reduce_scatter_local_f32.argtypes = lib.tide_reduce_scatter_local.argtypes
     lib.tide_stock_chunk_cat.argtypes = [vp, ctypes.POINTER(vp), vp, vp]
+    i32p = ctypes.POINTER(i32)
+    lib.tide_device_info.argtypes = [i32p, i32p, i32p, i32p]
+    lib.tide_probe_launch.argtypes = [vp, i32, i32, i64, vp]
+    lib.tide_victim_axpb.argtypes = [vp, vp, i64, ctypes.c_float, ctypes.c_float, vp]
+    lib.tide_stream_create.argtypes = [ctypes.POINTER(ctypes.c_uint32), i32, ctypes.POINTER(vp)]
+    lib.tide_stream_destroy.argtypes = [vp]
     lib.tide_plan_destroy.argtypes = [vp]
     lib.tide_plan_destroy.restype = None
     lib.tide_last_error.argtypes = []
@@ -353,3 +364,97 @@ def allgather_copyin(plan, shards, rank_major, stream=None):
     W*S elements; fp32 shards are cast by round to nearest even)."""
     ptrs, dt, rm = _ci_checked(plan, shards, rank_major)
     plan.allgather_copyin_raw(ptrs, dt, rm, _stream_handle(stream))
+
+
+# ------------------------------------------------------------ instruments
+
+
+def device_info():
+    """CU count, largest LDS allocation per workgroup and LDS per CU (bytes),
+    and wall-clock rate (kHz) of the current device (tide_device_info)."""
+    cu, lds, lds_cu, khz = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    _check(lib.tide_device_info(ctypes.byref(cu), ctypes.byref(lds), ctypes.byref(lds_cu), ctypes.byref(khz)))
+    return {"cu_count": cu.value, "max_lds_per_workgroup": lds.value, "lds_per_cu": lds_cu.value,
+            "wall_clock_khz": khz.value}
+
+
+PROBE_WORDS = 8
+
+
+def probe(records, grid, lds_bytes, hold_ns, stream=None):
+    """Launch the hardware-ID probe (tide_probe_launch): `records` is a GPU
+    int32 tensor of at least grid*8 elements; decode it with decode_probe."""
+    import torch
+
+    if not isinstance(records, torch.Tensor) or records.device.type != "cuda" or records.dtype != torch.int32:
+        raise TypeError("records: expected a GPU torch.int32 tensor")
+    if not records.is_contiguous() or records.numel() < int(grid) * PROBE_WORDS:
+        raise ValueError(f"records: expected a contiguous tensor of at least {int(grid) * PROBE_WORDS} elements")
+    _check(lib.tide_probe_launch(ctypes.c_void_p(records.data_ptr()), int(grid), int(lds_bytes), int(hold_ns),
+                                 ctypes.c_void_p(_stream_handle(stream) or None)))
+
+
+def decode_probe(records):
+    """Probe records (any int32/uint32 array of grid*8 words) -> dict of numpy
+    arrays: block, wave, simd, cu, sh, se, xcc, ok (LDS read back intact),
+    entry, exit (wall-clock ticks)."""
+    r = np.asarray(records).reshape(-1, PROBE_WORDS).view(np.uint32).astype(np.int64)
+    hw = r[:, 1]
+    return {
+        "block": r[:, 0], "wave": hw & 0xF, "simd": (hw >> 4) & 0x3, "cu": (hw >> 8) & 0xF, "sh": (hw >> 12) & 0x1,
+        "se": (hw >> 13) & 0x7, "xcc": r[:, 2] & 0xF, "ok": r[:, 3] == 0,
+        "entry": r[:, 4] | (r[:, 5] << 32), "exit": r[:, 6] | (r[:, 7] << 32),
+    }
+
+
+def victim_axpb(x, y, a, b, stream=None):
+    """The elementwise victim y = a * x + b on fp32 GPU tensors of equal size
+    (tide_victim_axpb)."""
+    import torch
+
+    for t, what in ((x, "x"), (y, "y")):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or t.dtype != torch.float32:
+            raise TypeError(f"{what}: expected a GPU torch.float32 tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{what}: expected a contiguous tensor")
+    if x.numel() != y.numel():
+        raise ValueError("x and y must have the same number of elements")
+    _check(lib.tide_victim_axpb(ctypes.c_void_p(x.data_ptr() or None), ctypes.c_void_p(y.data_ptr() or None),
+                                x.numel(), ctypes.c_float(a), ctypes.c_float(b),
+                                ctypes.c_void_p(_stream_handle(stream) or None)))
+
+
+class Stream:
+    """A library-created stream (tide_stream_create), optionally restricted to
+    the CUs in `cu_mask` (a sequence of CU indices).  `.torch` is the same
+    stream as a torch.cuda.ExternalStream, for events and torch work."""
+
+    def __init__(self, cus=None):
+        import torch
+
+        handle = ctypes.c_void_p()
+        if cus is None:
+            _check(lib.tide_stream_create(None, 0, ctypes.byref(handle)))
+        else:
+            n = device_info()["cu_count"]
+            words = [0] * ((n + 31) // 32)
+            for c in cus:
+                if not 0 <= int(c) < n:
+                    raise ValueError(f"CU index {c} out of range [0, {n})")
+                words[int(c) // 32] |= 1 << (int(c) % 32)
+            arr = (ctypes.c_uint32 * len(words))(*words)
+            _check(lib.tide_stream_create(arr, len(words), ctypes.byref(handle)))
+        self.handle = handle.value
+        self.torch = torch.cuda.ExternalStream(self.handle)
+
+    def destroy(self):
+        if getattr(self, "handle", None):
+            self.torch.synchronize()
+            _check(lib.tide_stream_destroy(ctypes.c_void_p(self.handle)))
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass

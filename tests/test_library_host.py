@@ -374,3 +374,36 @@ def test_copyin_argument_errors(tide):
     with pytest.raises(tide.TideError) as e:
         plan.allgather_copyin_raw(good[:15] + [0], tide.DTYPE_BF16, FAKE + 1)
     assert _status(e) == -3
+
+
+def test_instrument_argument_errors(tide):
+    """Checks of the interference instruments that fail before any device
+    call (no GPU is touched)."""
+    import ctypes
+
+    lib = tide.lib
+    vp = ctypes.c_void_p
+    assert lib.tide_probe_launch(None, 1, 0, 0, None) == -1
+    assert lib.tide_probe_launch(vp(FAKE + 2), 1, 0, 0, None) == -3
+    assert lib.tide_probe_launch(vp(FAKE), 0, 0, 0, None) == -1
+    assert lib.tide_probe_launch(vp(FAKE), 65537, 0, 0, None) == -1
+    assert lib.tide_probe_launch(vp(FAKE), 4, 0, -1, None) == -1
+    assert lib.tide_probe_launch(vp(FAKE), 4, 0, 10**9 + 1, None) == -1
+    assert b"hold_ns" in lib.tide_last_error()
+    f = ctypes.c_float
+    assert lib.tide_victim_axpb(vp(FAKE), vp(FAKE), -1, f(1), f(0), None) == -1
+    assert lib.tide_victim_axpb(None, vp(FAKE), 5, f(1), f(0), None) == -1
+    assert lib.tide_victim_axpb(vp(FAKE + 2), vp(FAKE), 5, f(1), f(0), None) == -3
+    assert lib.tide_victim_axpb(None, None, 0, f(1), f(0), None) == 0  # nothing to do
+    assert lib.tide_stream_create(None, 0, None) == -1
+    assert lib.tide_stream_destroy(None) == 0
+
+
+def test_probe_record_decoding(tide):
+    """The probe's register fields, decoded from hand-built records."""
+    hw = (5 << 0) | (2 << 4) | (1 << 6) | (11 << 8) | (1 << 12) | (3 << 13)
+    rec = np.array([7, hw, 6, 0, 0xFFFFFFFF, 1, 5, 2], dtype=np.uint32)
+    d = tide.decode_probe(rec)
+    assert (d["block"][0], d["wave"][0], d["simd"][0], d["cu"][0], d["sh"][0], d["se"][0], d["xcc"][0]) == \
+        (7, 5, 2, 11, 1, 3, 6)
+    assert d["ok"][0] and d["entry"][0] == 2**33 - 1 and d["exit"][0] == 2**33 + 5
