@@ -82,6 +82,11 @@ typedef enum {
  * carry the non-temporal hint (the data is touched once). */
 #define TIDE_FLAG_CACHED_LOADS 0x1u  /* plain (temporal) loads instead */
 #define TIDE_FLAG_CACHED_STORES 0x2u /* plain (temporal) stores instead */
+/* Keep the chunk -> segment table in global memory instead of staging it in
+ * LDS: the kernels then allocate no LDS, so a co-running kernel that claims a
+ * whole CU's LDS (a large GEMM tile, the probe below) is never kept off a CU
+ * by them (Section 2.2: placement decides which kernels are displaced). */
+#define TIDE_FLAG_NO_LDS 0x4u
 
 /*
  * Launch knobs.  A numeric field of 0 selects the default of the operation

@@ -19,6 +19,7 @@ package fails if that library has not been built.
 from .tide import (  # noqa: F401
     FLAG_CACHED_LOADS,
     FLAG_CACHED_STORES,
+    FLAG_NO_LDS,
     MAX_WORLD,
     Plan,
     DTYPE_BF16,

@@ -639,9 +639,10 @@ __global__ __launch_bounds__(tide::kThreads) void stock_pack_kernel(const CallHd
 // Launchers
 // ---------------------------------------------------------------------------
 
-// LDS for the staged chunk table; large tables stay in global memory.
+// LDS for the staged chunk table; large tables, and calls with
+// TIDE_FLAG_NO_LDS, keep it in global memory.
 size_t staged_bytes(const KernelArgs& a, bool* staged) {
-  *staged = a.nseg <= tide::kMaxStagedSegs;
+  *staged = a.nseg <= tide::kMaxStagedSegs && !(a.flags & TIDE_FLAG_NO_LDS);
   return *staged ? size_t(a.nseg + 1) * sizeof(int32_t) : 0;
 }
 

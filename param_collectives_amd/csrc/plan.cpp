@@ -168,7 +168,7 @@ tide_status check_options(const tide_options* in, tide_options* out, std::string
     *why = "wg_per_cu must be at most 64";
     return TIDE_ERR_RANGE;
   }
-  if (o.flags & ~(TIDE_FLAG_CACHED_LOADS | TIDE_FLAG_CACHED_STORES)) {
+  if (o.flags & ~(TIDE_FLAG_CACHED_LOADS | TIDE_FLAG_CACHED_STORES | TIDE_FLAG_NO_LDS)) {
     *why = "unknown bits in tide_options.flags";
     return TIDE_ERR_INVALID;
   }

@@ -12,6 +12,12 @@ import os
 
 import numpy as np
 
+# PyTorch ships its own HIP runtime under the same soname as the system's, and
+# whichever copy a process loads first serves every library in it.  torch is
+# imported before the library is loaded, so that torch and this library share
+# one runtime (its devices, memory and streams).
+import torch  # noqa: F401
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(_HERE, "libtide.so")
 
@@ -27,6 +33,7 @@ STATUS_NAMES = {
 }
 FLAG_CACHED_LOADS = 0x1
 FLAG_CACHED_STORES = 0x2
+FLAG_NO_LDS = 0x4
 DTYPE_BF16 = 0
 DTYPE_F32 = 1
 MAX_WORLD = 256
