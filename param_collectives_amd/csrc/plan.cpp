@@ -1,8 +1,9 @@
 // Host shard-layout planner: the dimension-0 shard geometry of "The Endgame of
 // FSDP Communication" (Wang et al.), Section 2.1, turned into the segment
 // table the kernels walk.  The placement is decided here once per plan, so a
-// call only passes tensor pointers (Section 6: gradient pointers as kernel
-// parameters, a segment table uploaded at registration).
+// call only passes tensor pointers (as in Section 6, where the kernels take
+// the gradient pointers as arguments and the segment table is uploaded once,
+// when the buffers are registered).
 #include <string>
 #include <vector>
 
