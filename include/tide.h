@@ -104,12 +104,18 @@ typedef enum {
  *               2048 (copy-in, stock pack).
  *               A plan may have at most 2^31 - 1 chunks per operation.
  *   flags       TIDE_FLAG_* bits.
+ *   wave_chunks at most this many chunks per wave in one kernel launch; an
+ *               operation with more chunks than waves * wave_chunks is run as
+ *               several launches, back to back on the stream (waves of one
+ *               long launch drift apart and spread their memory traffic).
+ *               At most 2^30 (one launch for any plan); default 64.
  */
 typedef struct {
     int32_t cu_budget;
     int32_t wg_per_cu;
     int64_t chunk_elems;
     uint32_t flags;
+    int32_t wave_chunks;
 } tide_options;
 
 typedef struct tide_plan tide_plan; /* opaque, owned by the library */

@@ -17,6 +17,7 @@
 // caller's stream, so they are ordered before the launch that reads them.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <cstring>
 #include <mutex>
@@ -284,27 +285,37 @@ tide_status run_op(tide_plan* p, tide::Op op, const std::vector<const void*>& ke
   a.flags = eff.flags;
   a.alpha = alpha;
   a.accumulate = accumulate;
-  int rc = 0;
-  const char* what = "";
-  switch (op) {
-    case tide::kOpRs:
-      rc = tide::launch_rs_local(a, f32, grid, stream);
-      what = "rs_local_kernel launch";
-      break;
-    case tide::kOpCo:
-      rc = tide::launch_ag_copyout(a, grid, stream);
-      what = "ag_copyout_kernel launch";
-      break;
-    case tide::kOpCi:
-      rc = tide::launch_ag_copyin(a, f32, grid, stream);
-      what = "ag_copyin_kernel launch";
-      break;
-    case tide::kOpPack:
-      rc = tide::launch_stock_pack(a, grid, stream);
-      what = "stock_pack_kernel launch";
-      break;
+  // At most wave_chunks chunks per wave per launch: longer work runs as
+  // several launches of consecutive chunk ranges.
+  const int64_t waves = grid * tide::kWavesPerGroup;
+  const int64_t per_launch = std::max<int64_t>(1, std::min<int64_t>(int64_t(eff.wave_chunks) * waves, nchunks));
+  for (int64_t c0 = 0; c0 < nchunks; c0 += per_launch) {
+    const int64_t c1 = std::min<int64_t>(nchunks, c0 + per_launch);
+    const auto it = std::upper_bound(s.chunk_begin.begin(), s.chunk_begin.end(), int32_t(c0));
+    a.span = tide::ChunkSpan{int32_t(c0), int32_t(c1), int32_t(it - s.chunk_begin.begin()) - 1};
+    const int64_t g = std::min<int64_t>(grid, (c1 - c0 + tide::kWavesPerGroup - 1) / tide::kWavesPerGroup);
+    int rc = 0;
+    const char* what = "";
+    switch (op) {
+      case tide::kOpRs:
+        rc = tide::launch_rs_local(a, f32, g, stream);
+        what = "rs_local_kernel launch";
+        break;
+      case tide::kOpCo:
+        rc = tide::launch_ag_copyout(a, g, stream);
+        what = "ag_copyout_kernel launch";
+        break;
+      case tide::kOpCi:
+        rc = tide::launch_ag_copyin(a, f32, g, stream);
+        what = "ag_copyin_kernel launch";
+        break;
+      case tide::kOpPack:
+        rc = tide::launch_stock_pack(a, g, stream);
+        what = "stock_pack_kernel launch";
+        break;
+    }
+    if (rc != 0) return hip_fail(hipError_t(rc), what);
   }
-  if (rc != 0) return hip_fail(hipError_t(rc), what);
   return TIDE_OK;
 }
 

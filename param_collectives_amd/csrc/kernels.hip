@@ -44,6 +44,7 @@
 namespace {
 
 using tide::CallHdr;
+using tide::ChunkSpan;
 using tide::KernelArgs;
 
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
@@ -125,7 +126,8 @@ __device__ __forceinline__ const int32_t* chunk_table(const int32_t* __restrict_
 struct Tables {
   const CallHdr* __restrict__ hdr;
   const void* const* __restrict__ ptrs;
-  int32_t nseg, nsrc, nchunks, chunk;
+  int32_t nseg, nsrc, chunk;
+  ChunkSpan span;  // the chunks of this launch
 };
 
 // Advance `cur` (wave-uniform, non-decreasing) to the segment holding chunk
@@ -203,22 +205,23 @@ __device__ __forceinline__ void fetch(const Tables& a, const int32_t* cb, int32_
   d->dst = const_cast<void*>(row[a.nsrc]);
 }
 
-// The persistent loop of every kernel: deal chunks to this wave round robin,
-// fetch each chunk's descriptor one chunk ahead (the scalar loads overlap the
-// vector loads of the current chunk) and hand the chunk to `body`.
+// The persistent loop of every kernel: deal the launch's chunks to this wave
+// round robin, fetch each chunk's descriptor one chunk ahead (the scalar loads
+// overlap the vector loads of the current chunk) and hand the chunk to `body`.
 template <int NS, bool STAGED, typename Body>
 __device__ __forceinline__ void for_each_chunk(const Tables& a, const int32_t* __restrict__ chunk_begin, Body body) {
   const int32_t* cb = chunk_table<STAGED>(chunk_begin, a.nseg);
   int32_t w, nw;
   wave_slot(&w, &nw);
-  int32_t cur = 0;
-  int32_t c = w;
+  const int32_t end = a.span.end;
+  int32_t cur = a.span.seg;
+  int32_t c = a.span.first + w;
   Desc<NS> next;
-  if (c < a.nchunks) fetch<NS>(a, cb, &cur, c, &next);
-  while (c < a.nchunks) {
+  if (c < end) fetch<NS>(a, cb, &cur, c, &next);
+  while (c < end) {
     const Desc<NS> d = next;
     const int32_t cn = c + nw;
-    if (cn < a.nchunks) fetch<NS>(a, cb, &cur, cn, &next);
+    if (cn < end) fetch<NS>(a, cb, &cur, cn, &next);
     body(d);
     c = cn;
   }
@@ -450,9 +453,9 @@ template <int WT, bool F32, bool CL, bool CS, bool STAGED>
 __global__ __launch_bounds__(tide::kThreads) void rs_local_kernel(const CallHdr* __restrict__ hdr,
                                                                   const void* const* __restrict__ ptrs,
                                                                   const int32_t* __restrict__ chunk_begin,
-                                                                  int32_t nseg, int32_t nsrc, int32_t nchunks,
+                                                                  int32_t nseg, int32_t nsrc, ChunkSpan span,
                                                                   int32_t chunk, float alpha, int32_t accumulate) {
-  const Tables a{hdr, ptrs, nseg, nsrc, nchunks, chunk};
+  const Tables a{hdr, ptrs, nseg, nsrc, chunk, span};
   const int epi = accumulate != 0 ? kScaleAcc : !(alpha == 1.0f) ? kScale : kPlain;
   const int32_t W = WT > 0 ? WT : nsrc;
   for_each_chunk<WT, STAGED>(a, chunk_begin, [&](const Desc<WT>& d) {
@@ -504,8 +507,8 @@ template <bool CL, bool CS, bool STAGED>
 __global__ __launch_bounds__(tide::kThreads) void ag_copyout_kernel(const CallHdr* __restrict__ hdr,
                                                                     const void* const* __restrict__ ptrs,
                                                                     const int32_t* __restrict__ chunk_begin,
-                                                                    int32_t nseg, int32_t nchunks, int32_t chunk) {
-  const Tables a{hdr, ptrs, nseg, 1, nchunks, chunk};
+                                                                    int32_t nseg, ChunkSpan span, int32_t chunk) {
+  const Tables a{hdr, ptrs, nseg, 1, chunk, span};
   for_each_chunk<1, STAGED>(a, chunk_begin, [&](const Desc<1>& d) {
     copy_chunk<CL, CS>(static_cast<const uint16_t*>(d.src[0]), static_cast<uint16_t*>(d.dst),
                        chunk_range(d.h, d.j, d.nch, a.chunk, 8));
@@ -557,8 +560,8 @@ template <bool F32, bool CL, bool CS, bool STAGED>
 __global__ __launch_bounds__(tide::kThreads) void ag_copyin_kernel(const CallHdr* __restrict__ hdr,
                                                                    const void* const* __restrict__ ptrs,
                                                                    const int32_t* __restrict__ chunk_begin,
-                                                                   int32_t nseg, int32_t nchunks, int32_t chunk) {
-  const Tables a{hdr, ptrs, nseg, 1, nchunks, chunk};
+                                                                   int32_t nseg, ChunkSpan span, int32_t chunk) {
+  const Tables a{hdr, ptrs, nseg, 1, chunk, span};
   for_each_chunk<1, STAGED>(a, chunk_begin, [&](const Desc<1>& d) {
     uint16_t* dst = static_cast<uint16_t*>(d.dst);
     const int lane = lane_id();
@@ -608,8 +611,8 @@ template <bool CL, bool CS, bool STAGED>
 __global__ __launch_bounds__(tide::kThreads) void stock_pack_kernel(const CallHdr* __restrict__ hdr,
                                                                     const void* const* __restrict__ ptrs,
                                                                     const int32_t* __restrict__ chunk_begin,
-                                                                    int32_t nseg, int32_t nchunks, int32_t chunk) {
-  const Tables a{hdr, ptrs, nseg, 1, nchunks, chunk};
+                                                                    int32_t nseg, ChunkSpan span, int32_t chunk) {
+  const Tables a{hdr, ptrs, nseg, 1, chunk, span};
   for_each_chunk<1, STAGED>(a, chunk_begin, [&](const Desc<1>& d) {
     float* dst = static_cast<float*>(d.dst);
     const Chunk r = chunk_range(d.h, d.j, d.nch, a.chunk, 4);
@@ -678,7 +681,7 @@ int launch_rs_w(const KernelArgs& a, int64_t grid, hipStream_t s) {
   by_instance(a, [&](auto CL, auto CS, auto ST, size_t lds) {
     hipLaunchKernelGGL((rs_local_kernel<WT, F32, TIDE_V(CL), TIDE_V(CS), TIDE_V(ST)>), dim3(unsigned(grid)),
                        dim3(unsigned(tide::kThreads)), lds, s, a.hdr, a.ptrs, a.chunk_begin, a.nseg, a.nsrc,
-                       a.nchunks, a.chunk, a.alpha, a.accumulate);
+                       a.span, a.chunk, a.alpha, a.accumulate);
   });
   return int(hipGetLastError());
 }
@@ -705,7 +708,7 @@ int launch_ag_copyout(const KernelArgs& a, int64_t grid, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   by_instance(a, [&](auto CL, auto CS, auto ST, size_t lds) {
     hipLaunchKernelGGL((ag_copyout_kernel<TIDE_V(CL), TIDE_V(CS), TIDE_V(ST)>), dim3(unsigned(grid)),
-                       dim3(unsigned(kThreads)), lds, s, a.hdr, a.ptrs, a.chunk_begin, a.nseg, a.nchunks, a.chunk);
+                       dim3(unsigned(kThreads)), lds, s, a.hdr, a.ptrs, a.chunk_begin, a.nseg, a.span, a.chunk);
   });
   return int(hipGetLastError());
 }
@@ -715,10 +718,10 @@ int launch_ag_copyin(const KernelArgs& a, bool f32, int64_t grid, void* stream) 
   by_instance(a, [&](auto CL, auto CS, auto ST, size_t lds) {
     if (f32) {
       hipLaunchKernelGGL((ag_copyin_kernel<true, TIDE_V(CL), TIDE_V(CS), TIDE_V(ST)>), dim3(unsigned(grid)),
-                         dim3(unsigned(kThreads)), lds, s, a.hdr, a.ptrs, a.chunk_begin, a.nseg, a.nchunks, a.chunk);
+                         dim3(unsigned(kThreads)), lds, s, a.hdr, a.ptrs, a.chunk_begin, a.nseg, a.span, a.chunk);
     } else {
       hipLaunchKernelGGL((ag_copyin_kernel<false, TIDE_V(CL), TIDE_V(CS), TIDE_V(ST)>), dim3(unsigned(grid)),
-                         dim3(unsigned(kThreads)), lds, s, a.hdr, a.ptrs, a.chunk_begin, a.nseg, a.nchunks, a.chunk);
+                         dim3(unsigned(kThreads)), lds, s, a.hdr, a.ptrs, a.chunk_begin, a.nseg, a.span, a.chunk);
     }
   });
   return int(hipGetLastError());
@@ -728,7 +731,7 @@ int launch_stock_pack(const KernelArgs& a, int64_t grid, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   by_instance(a, [&](auto CL, auto CS, auto ST, size_t lds) {
     hipLaunchKernelGGL((stock_pack_kernel<TIDE_V(CL), TIDE_V(CS), TIDE_V(ST)>), dim3(unsigned(grid)),
-                       dim3(unsigned(kThreads)), lds, s, a.hdr, a.ptrs, a.chunk_begin, a.nseg, a.nchunks, a.chunk);
+                       dim3(unsigned(kThreads)), lds, s, a.hdr, a.ptrs, a.chunk_begin, a.nseg, a.span, a.chunk);
   });
   return int(hipGetLastError());
 }

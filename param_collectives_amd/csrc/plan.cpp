@@ -155,10 +155,14 @@ tide_status chunk_table(const std::vector<Seg>& segs, int64_t chunk, std::vector
 }
 
 tide_status check_options(const tide_options* in, tide_options* out, std::string* why) {
-  tide_options o{0, 0, 0, 0};
+  tide_options o{0, 0, 0, 0, 0};
   if (in) o = *in;
-  if (o.cu_budget < 0 || o.wg_per_cu < 0 || o.chunk_elems < 0) {
+  if (o.cu_budget < 0 || o.wg_per_cu < 0 || o.chunk_elems < 0 || o.wave_chunks < 0) {
     *why = "tide_options fields must be >= 0";
+    return TIDE_ERR_INVALID;
+  }
+  if (o.wave_chunks > kMaxWaveChunks) {
+    *why = "wave_chunks must be at most 2^30";
     return TIDE_ERR_INVALID;
   }
   if (o.chunk_elems % 8 != 0 || o.chunk_elems > kMaxChunk) {
@@ -184,6 +188,7 @@ tide_options effective_options(const tide_options& given, Op op, int32_t cu_coun
   const int64_t chunk[kNumOps] = {kRsChunk, kCoChunk, kCiChunk, kPkChunk};
   if (o.wg_per_cu == 0) o.wg_per_cu = wg[op];
   if (o.chunk_elems == 0) o.chunk_elems = chunk[op];
+  if (o.wave_chunks == 0) o.wave_chunks = kWaveChunks;
   return o;
 }
 

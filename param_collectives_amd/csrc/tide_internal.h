@@ -28,6 +28,8 @@ constexpr int32_t kCiWgPerCu = 2;    // the copy-in's cast body wants more waves
 constexpr int64_t kCiChunk = 2048;
 constexpr int32_t kPkWgPerCu = 2;    // the stock pack (bf16 -> fp32 widening copy)
 constexpr int64_t kPkChunk = 2048;
+constexpr int32_t kMaxWaveChunks = 1 << 30;  // chunks per wave per launch: no split
+constexpr int32_t kWaveChunks = 64;  // measured on MI355X: 48-128 are equally good, 8 and no split 5-9% worse
 
 enum SegKind : int32_t { kSum = 0, kZero = 1, kCopy = 2, kCast = 3 };
 enum Op : int32_t { kOpRs = 0, kOpCo = 1, kOpCi = 2, kOpPack = 3 };
@@ -121,6 +123,15 @@ void ci_call_table(const Geometry& g, const std::vector<Seg>& segs, const void* 
 void pk_call_table(const Geometry& g, const std::vector<Seg>& segs, const uint16_t* const* grads, float* packed,
                    std::vector<CallHdr>* hdr, std::vector<const void*>* ptrs);
 
+// The chunks one launch covers, [first, end), and the segment holding chunk
+// `first`.  Long work is split into several launches: within one persistent
+// launch the waves drift apart over time, widening the window of HBM they
+// touch at once (measured on MI355X: one 17 GB reduce-scatter launch 5.85
+// TB/s, the same work in four launches 6.28 TB/s).
+struct ChunkSpan {
+  int32_t first, end, seg;
+};
+
 // Device-side launch arguments (kernels.hip).
 struct KernelArgs {
   const CallHdr* hdr;       // [nseg]
@@ -128,8 +139,9 @@ struct KernelArgs {
   const int32_t* chunk_begin;  // [nseg + 1]
   int32_t nseg;
   int32_t nsrc;  // W (reduce-scatter) or 1 (the copies)
-  int32_t nchunks;
-  int32_t chunk;  // elements per chunk
+  int32_t nchunks;  // of the whole operation
+  ChunkSpan span;   // of this launch
+  int32_t chunk;    // elements per chunk
   uint32_t flags;
   float alpha;         // reduce-scatter only: Equation 5's scale
   int32_t accumulate;  // reduce-scatter only: add into the shards' old values

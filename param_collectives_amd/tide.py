@@ -68,7 +68,7 @@ class TideError(RuntimeError):
 
 class Options(ctypes.Structure):
     _fields_ = [("cu_budget", ctypes.c_int32), ("wg_per_cu", ctypes.c_int32),
-                ("chunk_elems", ctypes.c_int64), ("flags", ctypes.c_uint32)]
+                ("chunk_elems", ctypes.c_int64), ("flags", ctypes.c_uint32), ("wave_chunks", ctypes.c_int32)]
 
 
 def _load():
@@ -111,8 +111,8 @@ def _check(status):
         raise TideError(status, lib.tide_last_error().decode(errors="replace"))
 
 
-def _options(cu_budget=0, wg_per_cu=0, chunk_elems=0, flags=0):
-    return Options(int(cu_budget), int(wg_per_cu), int(chunk_elems), int(flags))
+def _options(cu_budget=0, wg_per_cu=0, chunk_elems=0, flags=0, wave_chunks=0):
+    return Options(int(cu_budget), int(wg_per_cu), int(chunk_elems), int(flags), int(wave_chunks))
 
 
 def _ptr_array(values):
@@ -123,14 +123,14 @@ class Plan:
     """A shard-layout plan for `world` simulated ranks and the given parameter
     shapes (tide_plan_create)."""
 
-    def __init__(self, world, shapes, cu_budget=0, wg_per_cu=0, chunk_elems=0, flags=0):
+    def __init__(self, world, shapes, cu_budget=0, wg_per_cu=0, chunk_elems=0, flags=0, wave_chunks=0):
         self.world = int(world)
         self.shapes = [tuple(int(d) for d in s) for s in shapes]
         ndims = (ctypes.c_int32 * max(len(self.shapes), 1))(*[len(s) for s in self.shapes])
         flat = [d for s in self.shapes for d in s]
         dims = (ctypes.c_int64 * max(len(flat), 1))(*flat)
         handle = ctypes.c_void_p()
-        opt = _options(cu_budget, wg_per_cu, chunk_elems, flags)
+        opt = _options(cu_budget, wg_per_cu, chunk_elems, flags, wave_chunks)
         _check(lib.tide_plan_create(self.world, len(self.shapes), ndims, dims, ctypes.byref(opt),
                                     ctypes.byref(handle)))
         self.handle = handle
@@ -157,8 +157,8 @@ class Plan:
                                       count.value, ctypes.byref(count)))
         return table[:count.value]
 
-    def set_options(self, cu_budget=0, wg_per_cu=0, chunk_elems=0, flags=0):
-        opt = _options(cu_budget, wg_per_cu, chunk_elems, flags)
+    def set_options(self, cu_budget=0, wg_per_cu=0, chunk_elems=0, flags=0, wave_chunks=0):
+        opt = _options(cu_budget, wg_per_cu, chunk_elems, flags, wave_chunks)
         _check(lib.tide_plan_set_options(self.handle, ctypes.byref(opt)))
 
     def options(self, op=0):
@@ -167,7 +167,7 @@ class Plan:
         opt = Options()
         _check(lib.tide_plan_get_options(self.handle, int(op), ctypes.byref(opt)))
         return {"cu_budget": opt.cu_budget, "wg_per_cu": opt.wg_per_cu, "chunk_elems": opt.chunk_elems,
-                "flags": opt.flags}
+                "flags": opt.flags, "wave_chunks": opt.wave_chunks}
 
     def destroy(self):
         if getattr(self, "handle", None):

@@ -217,7 +217,9 @@ def test_knobs_do_not_change_results(tide, oracle_mod):
     knobs = [dict(), dict(cu_budget=1, wg_per_cu=1), dict(cu_budget=3, wg_per_cu=2, chunk_elems=8),
              dict(cu_budget=64, wg_per_cu=4, chunk_elems=65536), dict(flags=1), dict(flags=2), dict(flags=3),
              dict(cu_budget=256, wg_per_cu=16, chunk_elems=1024, flags=3), dict(flags=4),
-             dict(cu_budget=7, wg_per_cu=3, chunk_elems=64, flags=7)]
+             dict(cu_budget=7, wg_per_cu=3, chunk_elems=64, flags=7), dict(wave_chunks=1),
+             dict(cu_budget=2, wg_per_cu=1, chunk_elems=8, wave_chunks=3),
+             dict(cu_budget=5, wg_per_cu=2, chunk_elems=64, wave_chunks=2, flags=4)]
     for kw in knobs:
         plan = tide.Plan(W, shapes, **kw)
         got = run_rs(tide, plan, grads)

@@ -288,8 +288,8 @@ def test_destroyed_plan_is_rejected(tide):
 
 def test_options_round_trip_and_validation(tide):
     plan = tide.Plan(8, [(64, 64)], cu_budget=16, wg_per_cu=2, chunk_elems=1024, flags=tide.FLAG_CACHED_LOADS)
-    assert plan.options(0) == {"cu_budget": 16, "wg_per_cu": 2, "chunk_elems": 1024, "flags": 1}
-    assert plan.options(1) == {"cu_budget": 16, "wg_per_cu": 2, "chunk_elems": 1024, "flags": 1}
+    assert plan.options(0) == {"cu_budget": 16, "wg_per_cu": 2, "chunk_elems": 1024, "flags": 1, "wave_chunks": 64}
+    assert plan.options(1) == {"cu_budget": 16, "wg_per_cu": 2, "chunk_elems": 1024, "flags": 1, "wave_chunks": 64}
     before = plan.segments(0).copy()
     plan.set_options(chunk_elems=8)
     assert plan.options()["chunk_elems"] == 8
@@ -302,11 +302,17 @@ def test_options_round_trip_and_validation(tide):
         plan.set_options(chunk_elems=2**28 + 8)
     plan.set_options(chunk_elems=2**28)
     # zero fields take each operation's default (cu_budget resolves on a device)
+    with pytest.raises(tide.TideError):
+        plan.set_options(wave_chunks=-1)
+    with pytest.raises(tide.TideError):
+        plan.set_options(wave_chunks=2**30 + 1)
+    plan.set_options(wave_chunks=3)
+    assert plan.options(2)["wave_chunks"] == 3
     plan.set_options()
-    assert plan.options(0) == {"cu_budget": 0, "wg_per_cu": 1, "chunk_elems": 1024, "flags": 0}
-    assert plan.options(1) == {"cu_budget": 0, "wg_per_cu": 1, "chunk_elems": 4096, "flags": 0}
-    assert plan.options(2) == {"cu_budget": 0, "wg_per_cu": 2, "chunk_elems": 2048, "flags": 0}
-    assert plan.options(3) == {"cu_budget": 0, "wg_per_cu": 2, "chunk_elems": 2048, "flags": 0}
+    assert plan.options(0) == {"cu_budget": 0, "wg_per_cu": 1, "chunk_elems": 1024, "flags": 0, "wave_chunks": 64}
+    assert plan.options(1) == {"cu_budget": 0, "wg_per_cu": 1, "chunk_elems": 4096, "flags": 0, "wave_chunks": 64}
+    assert plan.options(2) == {"cu_budget": 0, "wg_per_cu": 2, "chunk_elems": 2048, "flags": 0, "wave_chunks": 64}
+    assert plan.options(3) == {"cu_budget": 0, "wg_per_cu": 2, "chunk_elems": 2048, "flags": 0, "wave_chunks": 64}
     for bad in (-1, 4):
         with pytest.raises(tide.TideError) as e:
             plan.options(bad)
