@@ -91,6 +91,17 @@ def traffic_for(kernel_key):
     return k["fetch_kib"] * 1024.0 * cal["fetch_factor"] + k["write_kib"] * 1024.0 * cal["write_factor"]
 
 
+def launches_per_call(plan, op):
+    """Kernel launches one call of operation `op` makes: its chunks are split
+    into launches of at most wave_chunks chunks per wave."""
+    o = plan.options(op)
+    segs = plan.segments(op)
+    nchunks = int(sum(-(-int(n) // o["chunk_elems"]) for n in segs[:, 5]))
+    grid = min(o["cu_budget"] * o["wg_per_cu"], -(-nchunks // 4))
+    per = max(1, min(o["wave_chunks"] * grid * 4, nchunks))
+    return -(-nchunks // per)
+
+
 def main(argv=None):
     args = parse_args(argv)
     if args.gpus != 1:
@@ -386,7 +397,8 @@ def main(argv=None):
                    "bytes_per_step": rs_bytes + co_bytes,
                    "options": {"rs_local": plan.options(0), "ag_copyout": plan.options(1)}},
         "frac_of_peak": round(value / HBM_PEAK_GBPS, 4),
-        "roofline": {"bound": "hbm", "kernel": "rs_local_kernel", "achieved": round(achieved, 1),
+        "roofline": {"bound": "hbm", "kernel": "rs_local_kernel", "unit_of_work": "one reduce-scatter call",
+                     "launches_per_call": launches_per_call(plan, 0), "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic_for(f"rs_local/{w.name}")},
         "cpu_baseline": cpu,

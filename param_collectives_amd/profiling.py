@@ -72,7 +72,22 @@ def bench_cmd(workload, extra):
     return [sys.executable, os.path.join(ROOT, "bench.py"), "--workload", workload, *extra]
 
 
-def collect_trace(workload, out, steps=10):
+TRACE_STEPS = 10
+COUNTER_LAUNCHES = 3
+
+
+def trace_op_calls(run, kernel, world):
+    """Operation calls each trace run makes of a kernel (bench.py: warm-up 2 +
+    timed steps of the reduce-scatter and copy-out, one untimed + 10 timed
+    copy-ins; the stock run: W packs and one reduce per launch).  An operation
+    call may be several dispatches (long operations are split)."""
+    calls = {("trace", "rs_local_kernel"): TRACE_STEPS + 2, ("trace", "ag_copyout_kernel"): TRACE_STEPS + 2,
+             ("trace", "ag_copyin_kernel"): 11, ("trace_stock", "stock_pack_kernel"): TRACE_STEPS * world,
+             ("trace_stock", "rs_local_kernel"): TRACE_STEPS}
+    return calls.get((run, kernel))
+
+
+def collect_trace(workload, out, steps=TRACE_STEPS):
     os.makedirs(out, exist_ok=True)
     runs = {"trace": ["--steps", str(steps), "--warmup", "2", "--no-cpu-baseline", "--no-sweep", "--no-extras"],
             "trace_stock": ["--only", "stock", "--launches", str(steps)]}
@@ -84,7 +99,7 @@ def collect_trace(workload, out, steps=10):
             f.write(_portable(" ".join(shlex.quote(c) for c in cmd), out) + "\n")
 
 
-def collect_counters(workload, out, launches=3):
+def collect_counters(workload, out, launches=COUNTER_LAUNCHES):
     os.makedirs(out, exist_ok=True)
     cmds = {}
     for only in ("rs", "co", "ci", "calib", "stock"):
@@ -167,7 +182,13 @@ def summarize(workload, out, profiles):
             lines.append("command (run in /tmp): " + _normalise(open(os.path.join(out, run + ".cmd")).read().strip()))
         except OSError:
             pass
-        lines.append(f"{'kernel':<22} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}")
+        lines.append("per dispatch (avg, min, max) and per operation call (all dispatches of one call; long "
+                     "operations are split into several dispatches)")
+        lines.append(f"{'kernel':<22} {'dispatches':>10} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6} "
+                     f"{'op_calls':>8} {'us_per_call':>12}")
+        import synth
+
+        world = synth.workload(workload).world
         for r in stats:
             name = _short(r.get("Name", r.get("KernelName", "")))
             if name not in KERNELS:
@@ -175,8 +196,10 @@ def summarize(workload, out, profiles):
             avg = float(r.get("AverageNs", 0)) / 1e3
             mn = float(r.get("MinNs", 0) or 0) / 1e3
             mx = float(r.get("MaxNs", 0) or 0) / 1e3
-            lines.append(f"{name:<22} {r.get('Calls', ''):>6} {avg:>10.2f} {mn:>10.2f} {mx:>10.2f} "
-                         f"{float(r.get('Percentage', 0)):>6.1f}")
+            calls = trace_op_calls(run, name, world)
+            per_call = float(r.get("TotalDurationNs", 0)) / 1e3 / calls if calls else float("nan")
+            lines.append(f"{name:<22} {r.get('Calls', ''):>10} {avg:>10.2f} {mn:>10.2f} {mx:>10.2f} "
+                         f"{float(r.get('Percentage', 0)):>6.1f} {calls!s:>8} {per_call:>12.2f}")
     if any_stats:
         with open(os.path.join(profiles, f"kernel_trace_{workload}.txt"), "w") as f:
             f.write("\n".join(lines) + "\n")
@@ -186,9 +209,11 @@ def summarize(workload, out, profiles):
         return
     cmds = {k: _normalise(v) for k, v in json.load(open(os.path.join(cdir, "counters.cmd.json"))).items()}
 
-    def med(only, name, counter, kernel):
+    def med(only, name, counter, kernel, calls=COUNTER_LAUNCHES):
+        """KiB of one operation call: the counter summed over every dispatch
+        of the kernel, divided by the operation calls made."""
         vals = [v for n, v in _read_counter(os.path.join(cdir, f"pmc_{only}_{name}"), counter) if kernel in n]
-        return statistics.median(vals) if vals else None
+        return sum(vals) / calls if vals else None
 
     import synth
 
@@ -213,8 +238,9 @@ def summarize(workload, out, profiles):
         kname = kname + "_kernel"
         if not os.path.isdir(os.path.join(cdir, f"pmc_{only}_fetch")):
             continue
-        f = med(only, "fetch", "FETCH_SIZE", kname)
-        wr = med(only, "write", "WRITE_SIZE", kname)
+        calls = COUNTER_LAUNCHES * (W if kname == "stock_pack_kernel" else 1)
+        f = med(only, "fetch", "FETCH_SIZE", kname, calls)
+        wr = med(only, "write", "WRITE_SIZE", kname, calls)
         if f is None or wr is None:
             continue
         traffic_r = f * 1024.0 * cal["fetch_factor"]
