@@ -97,11 +97,10 @@ typedef enum {
  *               device's CU count.  Workgroups are dispatched round-robin over
  *               the 8 XCDs, so a budget is a grid size, not a CU mask.
  *   wg_per_cu   workgroups (256 threads, four waves) per budgeted CU;
- *               default 1 (reduce-scatter, copy-out), 2 (copy-in, stock
- *               pack).
+ *               default 1.
  *   chunk_elems elements per chunk (the unit a wave takes), a multiple of 8,
- *               at most 2^28; default 1024 (reduce-scatter), 4096 (copy-out),
- *               2048 (copy-in, stock pack).
+ *               at most 2^28; default 1024 (reduce-scatter), 4096 (copy-out,
+ *               copy-in), 2048 (stock pack).
  *               A plan may have at most 2^31 - 1 chunks per operation.
  *   flags       TIDE_FLAG_* bits.
  *   wave_chunks at most this many chunks per wave in one kernel launch; an

@@ -93,9 +93,12 @@ __device__ __forceinline__ int64_t min64(int64_t a, int64_t b) { return a < b ? 
 __device__ __forceinline__ int lane_id() { return int(threadIdx.x & 63); }
 
 // Groups each lane has in flight per step (measured on MI355X: two groups of
-// W loads for the reduce-scatter, four 16-byte loads for the copies).
+// W loads for the reduce-scatter, four 16-byte loads for the bf16 copies,
+// eight for the casting and widening copies, whose groups are half as long on
+// one side).
 constexpr int kRsUnroll = 2;
 constexpr int kCoUnroll = 4;
+constexpr int kCastUnroll = 8;
 
 // Buffer-resource word 3 for raw (untyped) byte-addressed buffers on gfx9-class
 // GPUs, and the cache-policy operand bit that marks an access non-temporal.
@@ -551,7 +554,7 @@ __device__ __forceinline__ void cast_chunk(const float* src, uint16_t* dst, cons
   uint16_t* dv = dst + r.vlo;
   const int64_t ng = (r.vhi - r.vlo) >> 2;
   int64_t base = 0;
-  base = cast_steps<kCoUnroll, CL, CS>(sv, dv, base, ng, lane);
+  base = cast_steps<kCastUnroll, CL, CS>(sv, dv, base, ng, lane);
   base = cast_steps<2, CL, CS>(sv, dv, base, ng, lane);
   for (int64_t gk = base + lane; gk < ng; gk += 64) store<u32x2, CS>(dv + gk * 4, cast4(load<f32x4, CL>(sv + gk * 4)));
 }
@@ -605,7 +608,7 @@ __device__ __forceinline__ int64_t widen_steps(const uint16_t* sv, float* dv, in
 }
 
 // Stock gradient pack of one rank: its bf16 rows widened to fp32 (groups of
-// 4: 8-byte loads, 16-byte stores; kCoUnroll groups in flight per lane, then
+// 4: 8-byte loads, 16-byte stores; kCastUnroll groups in flight per lane, then
 // two, then one), padding rows +0.
 template <bool CL, bool CS, bool STAGED>
 __global__ __launch_bounds__(tide::kThreads) void stock_pack_kernel(const CallHdr* __restrict__ hdr,
@@ -632,7 +635,7 @@ __global__ __launch_bounds__(tide::kThreads) void stock_pack_kernel(const CallHd
     float* dv = dst + r.vlo;
     const int64_t ng = (r.vhi - r.vlo) >> 2;
     int64_t base = 0;
-    base = widen_steps<kCoUnroll, CL, CS>(sv, dv, base, ng, lane);
+    base = widen_steps<kCastUnroll, CL, CS>(sv, dv, base, ng, lane);
     base = widen_steps<2, CL, CS>(sv, dv, base, ng, lane);
     for (int64_t gk = base + lane; gk < ng; gk += 64) widen_group<CL, CS>(sv + gk * 4, dv + gk * 4);
   });

@@ -24,9 +24,9 @@ constexpr int32_t kRsWgPerCu = 1;
 constexpr int64_t kRsChunk = 1024;
 constexpr int32_t kCoWgPerCu = 1;
 constexpr int64_t kCoChunk = 4096;
-constexpr int32_t kCiWgPerCu = 2;    // the copy-in's cast body wants more waves in flight
-constexpr int64_t kCiChunk = 2048;
-constexpr int32_t kPkWgPerCu = 2;    // the stock pack (bf16 -> fp32 widening copy)
+constexpr int32_t kCiWgPerCu = 1;
+constexpr int64_t kCiChunk = 4096;
+constexpr int32_t kPkWgPerCu = 1;    // the stock pack (bf16 -> fp32 widening copy)
 constexpr int64_t kPkChunk = 2048;
 constexpr int32_t kMaxWaveChunks = 1 << 30;  // chunks per wave per launch: no split
 constexpr int32_t kWaveChunks = 64;  // measured on MI355X: 48-128 are equally good, 8 and no split 5-9% worse

@@ -311,8 +311,8 @@ def test_options_round_trip_and_validation(tide):
     plan.set_options()
     assert plan.options(0) == {"cu_budget": 0, "wg_per_cu": 1, "chunk_elems": 1024, "flags": 0, "wave_chunks": 64}
     assert plan.options(1) == {"cu_budget": 0, "wg_per_cu": 1, "chunk_elems": 4096, "flags": 0, "wave_chunks": 64}
-    assert plan.options(2) == {"cu_budget": 0, "wg_per_cu": 2, "chunk_elems": 2048, "flags": 0, "wave_chunks": 64}
-    assert plan.options(3) == {"cu_budget": 0, "wg_per_cu": 2, "chunk_elems": 2048, "flags": 0, "wave_chunks": 64}
+    assert plan.options(2) == {"cu_budget": 0, "wg_per_cu": 1, "chunk_elems": 4096, "flags": 0, "wave_chunks": 64}
+    assert plan.options(3) == {"cu_budget": 0, "wg_per_cu": 1, "chunk_elems": 2048, "flags": 0, "wave_chunks": 64}
     for bad in (-1, 4):
         with pytest.raises(tide.TideError) as e:
             plan.options(bad)
