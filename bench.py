@@ -15,8 +15,8 @@ bytes read plus written by both kernels divided by the step time, with
   * the roofline of the dominant kernel (the reduce-scatter) against MI355X's
     8 TB/s HBM peak, and its measured HBM traffic when a counter summary for
     the current kernel source is committed under profiles/;
-  * a CU-budget sweep (grid-limited budgets, as the workgroup budget of the
-    pages' short-lived sum kernels);
+  * a CU-budget sweep, each kernel on a stream masked to the budget's CUs
+    (GB/s per CU is the analog of the pages' per-CTA sum rate);
   * a plain device-to-device copy of the copy-out's byte count, for context;
   * Equation 5's epilogue (alpha = 1/W, accumulate into the shards) and the
     reduce-scatter from fp32 gradients, per kernel;
@@ -235,25 +235,28 @@ def main(argv=None):
 
     kernels = {"rs_local": kstats(rs_ms, rs_bytes), "ag_copyout": kstats(co_ms, co_bytes)}
 
-    # CU-budget sweep (grid-limited budgets; results are bit-identical by design)
+    # CU-budget sweep: each kernel confined to `budget` CUs by a CU-masked
+    # stream (a hard budget), four workgroups (16 waves) per CU; results are
+    # bit-identical by design
     sweep = []
     if not args.no_sweep:
-        # four workgroups (16 waves) per budgeted CU: the grid holds as many
-        # wave slots as `budget` CUs offer at this kernel's occupancy
         for budget in (8, 16, 32, 64, 128, 256):
+            masked = tide.Stream(cus=range(budget))
             plan.set_options(**dict(opts, cu_budget=budget, wg_per_cu=4))
-            row = {"cu_budget": budget, "wg_per_cu": 4}
-            for name, fn, nbytes in (("rs_local", rs, rs_bytes), ("ag_copyout", co, co_bytes)):
-                fn()
+            row = {"cu_budget": budget, "wg_per_cu": 4, "cu_masked": True}
+            for name, call, nbytes in (("rs_local", rs_call, rs_bytes), ("ag_copyout", co_call, co_bytes)):
+                ms_ = masked.torch
+                call(ms_)
                 e = [(ev(), ev()) for _ in range(10)]
                 for a, b in e:
-                    a.record(stream)
-                    fn()
-                    b.record(stream)
-                stream.synchronize()
+                    a.record(ms_)
+                    call(ms_)
+                    b.record(ms_)
+                ms_.synchronize()
                 avg = sum(a.elapsed_time(b) for a, b in e) / len(e)
                 row[name] = {"avg_ms": round(avg, 5), "gbps": round(nbytes / avg / 1e6, 1),
                              "gbps_per_cu": round(nbytes / avg / 1e6 / budget, 2)}
+            masked.destroy()
             sweep.append(row)
         plan.set_options(**opts)
 
