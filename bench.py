@@ -347,7 +347,6 @@ def main(argv=None):
         del acc_outs, acc_call
         stock_ab = stock_a_b(kstats, kernels)
 
-    # CPU oracle
     # CPU oracle on the same workload, and a bitwise check of this run's outputs
     cpu = None
     parity = None
@@ -371,7 +370,17 @@ def main(argv=None):
             if spent > 30.0:
                 break
         med = statistics.median(times)
+        # one step on a single thread as well (the oracle's threads split work
+        # between (rank, parameter) pairs, never an element's sum)
+        t = time.perf_counter()
+        one = oracle.rs_local(W, w.shapes, host_grads, nthreads=1)
+        oracle.copyout(W, w.shapes, host_rm, nthreads=1)
+        t1 = time.perf_counter() - t
+        same_threads = all(np.array_equal(one[r].view(np.uint32), want[r].view(np.uint32)) for r in range(W))
+        del one
         cpu = {"value": round((rs_bytes + co_bytes) / med / 1e9, 2), "unit": "GB/s", "cores": threads,
+               "single_thread_value": round((rs_bytes + co_bytes) / t1 / 1e9, 2),
+               "single_thread_matches": same_threads,
                "kind": "oracle",
                "sample": f"full {w.name} steps (reduce-scatter + copy-out, same inputs as the GPU), "
                          f"{len(times)} steps in {spent:.1f} s, median {med:.3f} s per step, {threads} threads"}
