@@ -17,7 +17,9 @@ Aggressors (one call each, repeated back to back on their own stream):
   tide-rs/noLDS/...  the same with the table left in global memory;
   tide-rs/mask=B     the same kernel on a stream masked to B CUs;
   stock              W stock gradient packs, then the fp32 reduce-scatter of
-                     the packed buffers.
+                     the packed buffers;
+  copy-out           the all-gather copy-out (what the pages' direct landing
+                     removes from the all-gather).
 Victims (on a second stream): the 256 MiB elementwise kernel (y = a*x + b),
 a small-M GEMM (256 x 8192 x 8192, bf16) and a large GEMM (8192^3, bf16), both
 torch.matmul (the vendor GEMM library).  Reported per pair: the victim's p50
@@ -83,6 +85,13 @@ class Study:
             call = tide.reduce_scatter_call(plan, self.grads, self.outs)
             held = min(grid, cus)
             fn = call
+        elif kind == "copyout":
+            import synth
+
+            rm = synth.rank_major_device(self.w, W * S, "cuda")
+            params = [torch.empty(sh, dtype=torch.bfloat16, device="cuda") for sh in self.w.shapes]
+            fn = tide.allgather_copyout_call(self.plan, rm, params)
+            held = cus
         else:
             pack_plan = tide.Plan(W, [(W, S)])
             packed = [torch.empty(W * S, dtype=torch.float32, device="cuda") for _ in range(W)]
@@ -238,6 +247,7 @@ DEFAULT_CONFIGS = [
     ("tide-rs mask=64", dict(kind="tide", budget=64, masked=True)),
     ("tide-rs mask=16", dict(kind="tide", budget=16, masked=True)),
     ("stock pack+reduce", dict(kind="stock")),
+    ("tide copy-out", dict(kind="copyout")),
 ]
 
 
