@@ -91,6 +91,20 @@ def traffic_for(kernel_key):
     return k["fetch_kib"] * 1024.0 * cal["fetch_factor"] + k["write_kib"] * 1024.0 * cal["write_factor"]
 
 
+def cpu_model():
+    """The host CPU's model name and the cores visible to this process."""
+    name = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    name = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return f"{name}; {len(os.sched_getaffinity(0))} cores visible"
+
+
 def launches_per_call(plan, op):
     """Kernel launches one call of operation `op` makes: its chunks are split
     into launches of at most wave_chunks chunks per wave."""
@@ -382,6 +396,7 @@ def main(argv=None):
                "single_thread_value": round((rs_bytes + co_bytes) / t1 / 1e9, 2),
                "single_thread_matches": same_threads,
                "kind": "oracle",
+               "cpu": cpu_model(),
                "sample": f"full {w.name} steps (reduce-scatter + copy-out, same inputs as the GPU), "
                          f"{len(times)} steps in {spent:.1f} s, median {med:.3f} s per step, {threads} threads"}
         ok = all(np.array_equal(outs[r].cpu().numpy().view(np.uint32), want[r].view(np.uint32)) for r in range(W))
