@@ -317,3 +317,46 @@ def test_full_size_alpha_accumulate_and_fp32(tide, oracle_mod):
     for r in range(w.world):
         gpu_util.assert_same_f32(got[r], want[r], f"fp32 rank {r}")
     print("[full-size eq5] bit-exact", flush=True)
+
+
+# ------------------------------------------------------------ split launches
+
+
+@pytest.mark.parametrize("world", [3, 8, 16])
+def test_many_launches_per_call(tide, oracle_mod, world):
+    """Operations split into many launches (a few chunks per wave per launch,
+    small grids) give the oracle's results for every operation and both
+    gradient types; launch boundaries fall inside segments and between them."""
+    import torch
+
+    rng = np.random.default_rng(400 + world)
+    shapes = random_shapes(rng, world, 5) + [(world * 40 + 3, 64), (7,)]
+    opts = dict(cu_budget=3, wg_per_cu=1, chunk_elems=64, wave_chunks=1)
+    plan = tide.Plan(world, shapes, **opts)
+    grads = [[oracle_pins.rand_bf16(rng, s) for s in shapes] for _ in range(world)]
+    init = init_shards(rng, world, plan.shard_elems)
+    got = run_rs(tide, plan, grads, alpha=0.5, accumulate=True, init=init)
+    want = oracle_mod.rs_local_ex(world, shapes, grads, 0.5, True, init)
+    for r in range(world):
+        gpu_util.assert_same_f32(got[r], want[r], f"bf16 rank {r}")
+    g32 = [[oracle_pins.rand_f32(rng, s) for s in shapes] for _ in range(world)]
+    got = run_rs(tide, plan, g32)
+    want = oracle_mod.rs_local_ex(world, shapes, g32)
+    for r in range(world):
+        gpu_util.assert_same_f32(got[r], want[r], f"fp32 rank {r}")
+    # copy-out, copy-in and the stock pack through the same many-launch options
+    X = [rng.standard_normal(s).astype(np.float32) for s in shapes]
+    rm_bits = oracle_mod.copyin(world, shapes, oracle_pins.shards_of(world, shapes, X))
+    rm = gpu_util.to_device_bf16(rm_bits)
+    params = [torch.empty(s, dtype=torch.bfloat16, device="cuda") for s in shapes]
+    tide.allgather_copyout(plan, rm, params)
+    shards = [[torch.from_numpy(np.ascontiguousarray(a)).cuda() for a in row]
+              for row in oracle_pins.shards_of(world, shapes, X)]
+    rm2 = torch.empty_like(rm)
+    tide.allgather_copyin(plan, shards, rm2)
+    torch.cuda.synchronize()
+    want_co = oracle_mod.copyout(world, shapes, rm_bits)
+    for p in range(len(shapes)):
+        assert np.array_equal(gpu_util.bf16_bits(params[p]).reshape(shapes[p]), want_co[p]), p
+    assert np.array_equal(gpu_util.bf16_bits(rm2), rm_bits)
+    gpu_util.assert_same_f32(run_pack(tide, plan, grads[0]), oracle_mod.chunk_cat(world, shapes, grads[0]), "pack")
