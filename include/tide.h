@@ -93,7 +93,8 @@ typedef enum {
  * being launched.  None of them changes any result bit (Section 4.3: tuning
  * knobs preserve operand grouping).
  *   cu_budget   the persistent grid has cu_budget * wg_per_cu workgroups
- *               (fewer if there are fewer chunks than waves); default: the
+ *               (fewer if there are fewer chunks than waves, and at most
+ *               2^27); default: the
  *               device's CU count.  Workgroups are dispatched round-robin over
  *               the 8 XCDs, so a budget is a grid size, not a CU mask.
  *   wg_per_cu   workgroups (256 threads, four waves) per budgeted CU;
@@ -101,7 +102,7 @@ typedef enum {
  *   chunk_elems elements per chunk (the unit a wave takes), a multiple of 8,
  *               at most 2^28; default 1024 (reduce-scatter), 4096 (copy-out,
  *               copy-in), 2048 (stock pack).
- *               A plan may have at most 2^31 - 1 chunks per operation.
+ *               A plan may have at most 2^30 chunks per operation.
  *   flags       TIDE_FLAG_* bits.
  *   wave_chunks at most this many chunks per wave in one kernel launch; an
  *               operation with more chunks than waves * wave_chunks is run as

@@ -272,6 +272,7 @@ tide_status run_op(tide_plan* p, tide::Op op, const std::vector<const void*>& ke
   int64_t grid = int64_t(eff.cu_budget) * eff.wg_per_cu;
   const int64_t useful = (int64_t(nchunks) + tide::kWavesPerGroup - 1) / tide::kWavesPerGroup;
   if (grid > useful) grid = useful;
+  if (grid > tide::kMaxGrid) grid = tide::kMaxGrid;
   if (grid < 1) grid = 1;
   tide::KernelArgs a;
   a.hdr = static_cast<const tide::CallHdr*>(s.d_call);

@@ -145,8 +145,8 @@ tide_status chunk_table(const std::vector<Seg>& segs, int64_t chunk, std::vector
   for (size_t s = 0; s < segs.size(); ++s) {
     (*chunk_begin)[s] = int32_t(total);
     total += segs[s].len / chunk + (segs[s].len % chunk != 0);
-    if (total > INT32_MAX) {
-      *why = "more than 2^31 - 1 chunks: use a larger chunk_elems";
+    if (total > kMaxChunks) {
+      *why = "more than 2^30 chunks: use a larger chunk_elems";
       return TIDE_ERR_RANGE;
     }
   }

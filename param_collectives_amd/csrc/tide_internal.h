@@ -14,6 +14,10 @@ namespace tide {
 constexpr int kThreads = 256;  // threads per workgroup: four wave64s, each an independent worker
 constexpr int kWavesPerGroup = kThreads / 64;
 constexpr int64_t kMaxChunk = int64_t(1) << 28;  // keeps a chunk's byte offsets within 32 bits
+// Chunk indices and wave counts are int32 on the device: with at most 2^30
+// chunks and 2^27 workgroups (2^29 waves), chunk + waves never overflows.
+constexpr int64_t kMaxChunks = int64_t(1) << 30;
+constexpr int64_t kMaxGrid = int64_t(1) << 27;
 constexpr int32_t kMaxStagedSegs = 16383;  // chunk-index table entries staged in LDS (64 KiB)
 
 // Per-operation defaults, measured on MI355X over the four layer workloads:
@@ -92,7 +96,7 @@ std::vector<Seg> pack_segments(const Geometry& g);
 
 // chunk_begin[s] = index of segment s's first chunk, chunk_begin[nseg] = total;
 // segment s owns ceil(len / chunk) chunks.  Fails (TIDE_ERR_RANGE) when the
-// total does not fit in int32.
+// total exceeds kMaxChunks.
 tide_status chunk_table(const std::vector<Seg>& segs, int64_t chunk, std::vector<int32_t>* chunk_begin,
                         std::string* why);
 

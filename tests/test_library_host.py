@@ -326,6 +326,10 @@ def test_too_many_chunks_is_a_range_error(tide):
     with pytest.raises(tide.TideError) as e:
         tide.Plan(1, [(2**34,)], chunk_elems=8)
     assert _status(e) == -2
+    tide.Plan(1, [(2**33,)], chunk_elems=8)  # exactly 2^30 chunks: the limit
+    with pytest.raises(tide.TideError) as e:
+        tide.Plan(1, [(2**33 + 8,)], chunk_elems=8)
+    assert _status(e) == -2
     plan = tide.Plan(1, [(2**34,)])  # 2^24 chunks of the default size
     with pytest.raises(tide.TideError) as e:
         plan.set_options(chunk_elems=8)
