@@ -154,6 +154,17 @@ def test_rs_random_shapes(tide, oracle_mod, world):
         check_rs(tide, oracle_mod, world, shapes, grads, chunk_elems=512)
 
 
+def test_rs_largest_world(tide, oracle_mod):
+    """W = 256, the largest world a plan accepts: 256 sources per segment on
+    the generic path, most ranks holding only padding."""
+    rng = np.random.default_rng(123)
+    world = 256
+    shapes = [(300, 2), (1,), (513, 3), (256 * 3, 8)]
+    grads = [[oracle_pins.rand_bf16(rng, s) for s in shapes] for _ in range(world)]
+    check_rs(tide, oracle_mod, world, shapes, grads, chunk_elems=8)
+    check_rs(tide, oracle_mod, world, shapes, grads)
+
+
 @pytest.mark.parametrize("world", [1, 3, 4, 8])
 def test_copyout_random_shapes(tide, oracle_mod, world):
     rng = np.random.default_rng(200 + world)
