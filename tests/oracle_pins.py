@@ -613,6 +613,29 @@ def check_chunk_cat_matches_stock_pack(orc, seed=21):
         assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
 
 
+def check_eq5_worked_golden(orc):
+    """Hand-worked Equation 5 cases: the product and the accumulation are two
+    separate roundings, padding contributes +0 scaled by alpha."""
+    g = goldens.read("eq5_worked.txt")
+    cases = sorted({k.split(".")[0] for k in g})
+    for c in cases:
+        shape = (int(g[c + ".shape"][0][0]),)
+        grads = [None, None]
+        for row in g[c + ".grad"]:
+            grads[int(row[0])] = [goldens.hex16(row[1:])]
+        alpha = np.array([int(g[c + ".alpha"][0][0], 16)], dtype=np.uint32).view(np.float32)[0]
+        acc = bool(int(g[c + ".accumulate"][0][0]))
+        old = [None, None]
+        want = [None, None]
+        for row in g[c + ".old"]:
+            old[int(row[0])] = np.array([int(v, 16) for v in row[1:]], dtype=np.uint32).view(np.float32)
+        for row in g[c + ".out"]:
+            want[int(row[0])] = np.array([int(v, 16) for v in row[1:]], dtype=np.uint32).view(np.float32)
+        got = orc.rs_local_ex(2, [shape], grads, alpha, acc, old)
+        for r in range(2):
+            assert same_bits(got[r], want[r]), (c, r, got[r].view(np.uint32), want[r].view(np.uint32))
+
+
 # ---------------------------------------------------- interference victim
 
 
@@ -681,6 +704,7 @@ ALL_CHECKS = [
     check_rs_ex_alpha,
     check_rs_ex_accumulate,
     check_chunk_cat_matches_stock_pack,
+    check_eq5_worked_golden,
     check_axpb_worked_golden,
     check_axpb_integers_are_exact,
     check_axpb_is_two_numpy_float32_operations,

@@ -360,3 +360,29 @@ def test_many_launches_per_call(tide, oracle_mod, world):
         assert np.array_equal(gpu_util.bf16_bits(params[p]).reshape(shapes[p]), want_co[p]), p
     assert np.array_equal(gpu_util.bf16_bits(rm2), rm_bits)
     gpu_util.assert_same_f32(run_pack(tide, plan, grads[0]), oracle_mod.chunk_cat(world, shapes, grads[0]), "pack")
+
+
+def test_eq5_worked_golden_on_gpu(tide, oracle_mod):
+    """The hand-worked Equation 5 cases (two roundings, scaled padding) on the
+    GPU, against the golden bits."""
+    from tests import goldens
+
+    g = goldens.read("eq5_worked.txt")
+    for c in sorted({k.split(".")[0] for k in g}):
+        shape = (int(g[c + ".shape"][0][0]),)
+        grads = [None, None]
+        for row in g[c + ".grad"]:
+            grads[int(row[0])] = [goldens.hex16(row[1:])]
+        alpha = float(np.array([int(g[c + ".alpha"][0][0], 16)], dtype=np.uint32).view(np.float32)[0])
+        acc = bool(int(g[c + ".accumulate"][0][0]))
+        fp = lambda row: np.array([int(v, 16) for v in row[1:]], dtype=np.uint32).view(np.float32)
+        old = [None, None]
+        want = [None, None]
+        for row in g[c + ".old"]:
+            old[int(row[0])] = fp(row)
+        for row in g[c + ".out"]:
+            want[int(row[0])] = fp(row)
+        plan = tide.Plan(2, [shape])
+        got = run_rs(tide, plan, grads, alpha, acc, old)
+        for r in range(2):
+            gpu_util.assert_same_f32(got[r], want[r], f"case {c} rank {r}")

@@ -83,6 +83,11 @@ MUTANTS = [
      "    for (int64_t e = 0; e < g->n[p]; ++e) {\n        float sum",
      "int64_t first = (int64_t)r * real;\n    float* dst = j->out[r] + g->o[p];\n"
      "    for (int64_t e = 0; e < g->n[p]; ++e) {\n        float sum"),
+    ("accumulate_fused",
+     "float v = j->alpha * sum;\n        dst[e] = j->accumulate ? dst[e] + v : v;",
+     "float v = j->alpha * sum;\n        dst[e] = j->accumulate ? fmaf(j->alpha, sum, dst[e]) : v;"),
+    ("padding_sum_not_scaled",
+     "float v = j->alpha * sum;", "float v = (sum == 0.0f) ? sum : j->alpha * sum;"),
     ("axpb_fused",
      "volatile float prod = a * x[i]; /* one rounding, kept apart from the sum */\n        y[i] = prod + b;",
      "y[i] = fmaf(a, x[i], b);"),
