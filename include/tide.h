@@ -51,6 +51,10 @@
  *     different pointers from the previous call.
  *   - Results never depend on tide_options: every option only changes how the
  *     work is split, never which additions happen or in what order.
+ *   - Graph capture: once a plan has run an operation with the same pointers
+ *     (and options) on the current device, a call of that operation enqueues
+ *     kernel launches only (no allocation, copy or synchronization), so it may
+ *     be recorded into a HIP graph and replayed.
  */
 #ifndef TIDE_H
 #define TIDE_H
