@@ -8,7 +8,8 @@ gradients -> W packed fp32 shards) followed by the all-gather copy-out
 shard-layout plan is made once, before timing (it is per-registration work).
 
 Reported (one JSON line): effective HBM GB/s of the step, i.e. algorithmic
-bytes read plus written by both kernels divided by the step time, with
+bytes read plus written by the step's two operations divided by the step
+time, with
   * the all-gather copy-in (fp32 master shards -> rank-major bf16, fused
     cast) timed beside the step, not part of it;
   * per-kernel figures from HIP events recorded on the kernels' own stream;

@@ -82,7 +82,7 @@ typedef enum {
 /* Largest number of simulated ranks a plan may have. */
 #define TIDE_MAX_WORLD 256
 
-/* tide_options.flags.  By default both kernels stream: loads and stores
+/* tide_options.flags.  By default every kernel streams: loads and stores
  * carry the non-temporal hint (the data is touched once). */
 #define TIDE_FLAG_CACHED_LOADS 0x1u  /* plain (temporal) loads instead */
 #define TIDE_FLAG_CACHED_STORES 0x2u /* plain (temporal) stores instead */

@@ -33,6 +33,9 @@
 //     fetch overlaps the vector loads of the current chunk.
 //   * Vector bodies use non-temporal loads and contiguous 8- or 16-byte
 //     stores; heads and tails of misaligned tensors take a scalar path.
+//   * One launch covers a span of chunks; the host splits a long operation
+//     into several launches, so that the waves of one launch cannot drift far
+//     apart (which would widen the window).
 #include <hip/hip_runtime.h>
 
 #include <climits>

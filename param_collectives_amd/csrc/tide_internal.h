@@ -22,8 +22,8 @@ constexpr int32_t kMaxStagedSegs = 16383;  // chunk-index table entries staged i
 
 // Per-operation defaults, measured on MI355X over the four layer workloads:
 // one workgroup (four waves) per CU keeps the HBM read/write mix most
-// efficient for both kernels; the reduce-scatter prefers small chunks (the
-// grid then sweeps a narrow window of every tensor), the copy-out larger ones.
+// efficient for every kernel; the reduce-scatter prefers small chunks (the
+// grid then sweeps a narrow window of every tensor), the copies larger ones.
 constexpr int32_t kRsWgPerCu = 1;
 constexpr int64_t kRsChunk = 1024;
 constexpr int32_t kCoWgPerCu = 1;
