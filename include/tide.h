@@ -138,7 +138,8 @@ typedef struct tide_plan tide_plan; /* opaque, owned by the library */
  * the device current at that time (that first call blocks the host for the
  * allocation); the plan is bound to that device afterwards.
  * Errors: TIDE_ERR_INVALID (bad counts, shapes, options, null pointers),
- * TIDE_ERR_RANGE (sizes overflow int64, too many chunks), TIDE_ERR_NOMEM.
+ * TIDE_ERR_RANGE (W * S above 2^61 elements, so that byte offsets fit
+ * int64; too many chunks), TIDE_ERR_NOMEM.
  */
 tide_status tide_plan_create(int32_t world, int32_t nparams, const int32_t* ndims, const int64_t* dims,
                              const tide_options* opt, tide_plan** out_plan);

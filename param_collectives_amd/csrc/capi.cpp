@@ -20,6 +20,7 @@
 #include <algorithm>
 #include <cstdint>
 #include <cstring>
+#include <memory>
 #include <mutex>
 #include <string>
 #include <unordered_set>
@@ -47,6 +48,15 @@ namespace tide {
 tide_status set_error(tide_status st, const std::string& msg) { return fail(st, msg); }
 
 void clear_error() { g_last_error.clear(); }
+
+tide_status set_error_nothrow(tide_status st, const char* msg) noexcept {
+  try {
+    g_last_error = msg;
+  } catch (...) {
+    g_last_error.clear();  // never allocates
+  }
+  return st;
+}
 
 }  // namespace tide
 
@@ -181,6 +191,8 @@ tide_status dev_alloc(T** out, size_t bytes) {
   return TIDE_OK;
 }
 
+// hipFree synchronizes the device first, so launches still reading the tables
+// finish before they are freed.
 void release_op(OpState* s) {
   free_upload(&s->up_chunks);
   free_upload(&s->up_call);
@@ -363,201 +375,206 @@ extern "C" {
 
 tide_status tide_plan_create(int32_t world, int32_t nparams, const int32_t* ndims, const int64_t* dims,
                              const tide_options* opt, tide_plan** out_plan) {
-  g_last_error.clear();
-  if (out_plan == nullptr) return fail(TIDE_ERR_INVALID, "out_plan must not be NULL");
-  *out_plan = nullptr;
-  std::string why;
-  tide_options given;
-  tide_status st = tide::check_options(opt, &given, &why);
-  if (st != TIDE_OK) return fail(st, why);
-  tide_plan* p = new (std::nothrow) tide_plan();
-  if (p == nullptr) return fail(TIDE_ERR_NOMEM, "out of host memory");
-  st = tide::build_geometry(world, nparams, ndims, dims, &p->geo, &why);
-  if (st != TIDE_OK) {
-    delete p;
-    return fail(st, why);
-  }
-  try {
+  return tide::guarded([&]() -> tide_status {
+    g_last_error.clear();
+    if (out_plan == nullptr) return fail(TIDE_ERR_INVALID, "out_plan must not be NULL");
+    *out_plan = nullptr;
+    std::string why;
+    tide_options given;
+    tide_status st = tide::check_options(opt, &given, &why);
+    if (st != TIDE_OK) return fail(st, why);
+    // Owned here until it is registered: any early return frees it (no device
+    // state exists before the first launch).
+    std::unique_ptr<tide_plan> p(new tide_plan());
+    st = tide::build_geometry(world, nparams, ndims, dims, &p->geo, &why);
+    if (st != TIDE_OK) return fail(st, why);
     p->rs.segs = tide::rs_segments(p->geo);
     p->co.segs = tide::copyout_segments(p->geo);
     p->ci.segs = tide::copyin_segments(p->geo);
     p->pk.segs = tide::pack_segments(p->geo);
-  } catch (...) {
-    delete p;
-    return fail(TIDE_ERR_NOMEM, "out of host memory");
-  }
-  for (tide::Op op : kOps) {
-    if (op_state(p, op).segs.size() >= size_t(INT32_MAX)) {
-      delete p;
-      return fail(TIDE_ERR_RANGE, "too many segments");
+    for (tide::Op op : kOps)
+      if (op_state(p.get(), op).segs.size() >= size_t(INT32_MAX)) return fail(TIDE_ERR_RANGE, "too many segments");
+    p->given = given;
+    st = rebuild_chunks(p.get(), given);
+    if (st != TIDE_OK) return st;
+    p->magic = kMagic;
+    {
+      std::lock_guard<std::mutex> lock(g_plans_mu);
+      g_plans.insert(p.get());
     }
-  }
-  p->given = given;
-  st = rebuild_chunks(p, given);
-  if (st != TIDE_OK) {
-    const std::string msg = g_last_error;
-    delete p;
-    return fail(st, msg);
-  }
-  p->magic = kMagic;
-  {
-    std::lock_guard<std::mutex> lock(g_plans_mu);
-    g_plans.insert(p);
-  }
-  *out_plan = p;
-  return TIDE_OK;
+    *out_plan = p.release();
+    return TIDE_OK;
+  });
 }
 
 tide_status tide_plan_layout(const tide_plan* plan, int64_t* rows_per_rank, int64_t* shard_offset,
                              int64_t* shard_elems) {
-  g_last_error.clear();
-  if (!live(plan)) return fail(TIDE_ERR_INVALID, "unknown or destroyed plan");
-  for (int32_t p = 0; p < plan->geo.nparams; ++p) {
-    if (rows_per_rank) rows_per_rank[p] = plan->geo.R[p];
-    if (shard_offset) shard_offset[p] = plan->geo.o[p];
-  }
-  if (shard_elems) *shard_elems = plan->geo.S;
-  return TIDE_OK;
+  return tide::guarded([&]() -> tide_status {
+    g_last_error.clear();
+    if (!live(plan)) return fail(TIDE_ERR_INVALID, "unknown or destroyed plan");
+    for (int32_t p = 0; p < plan->geo.nparams; ++p) {
+      if (rows_per_rank) rows_per_rank[p] = plan->geo.R[p];
+      if (shard_offset) shard_offset[p] = plan->geo.o[p];
+    }
+    if (shard_elems) *shard_elems = plan->geo.S;
+    return TIDE_OK;
+  });
 }
 
 tide_status tide_plan_segments(const tide_plan* plan, int32_t op, int64_t* table, int64_t capacity,
                                int64_t* count) {
-  g_last_error.clear();
-  if (!live(plan)) return fail(TIDE_ERR_INVALID, "unknown or destroyed plan");
-  if (op < 0 || op >= tide::kNumOps) return fail(TIDE_ERR_INVALID, std::string("op must be ") + kOpNames);
-  if (count == nullptr || capacity < 0 || (capacity > 0 && table == nullptr))
-    return fail(TIDE_ERR_INVALID, "bad table/capacity/count");
-  const std::vector<tide::Seg>& segs = op_state(plan, tide::Op(op)).segs;
-  *count = int64_t(segs.size());
-  const int64_t n = capacity < *count ? capacity : *count;
-  for (int64_t i = 0; i < n; ++i) {
-    const tide::Seg& s = segs[size_t(i)];
-    int64_t* row = table + 6 * i;
-    row[0] = s.kind;
-    row[1] = s.src_idx;
-    row[2] = s.dst_idx;
-    row[3] = s.src_off;
-    row[4] = s.dst_off;
-    row[5] = s.len;
-  }
-  return TIDE_OK;
+  return tide::guarded([&]() -> tide_status {
+    g_last_error.clear();
+    if (!live(plan)) return fail(TIDE_ERR_INVALID, "unknown or destroyed plan");
+    if (op < 0 || op >= tide::kNumOps) return fail(TIDE_ERR_INVALID, std::string("op must be ") + kOpNames);
+    if (count == nullptr || capacity < 0 || (capacity > 0 && table == nullptr))
+      return fail(TIDE_ERR_INVALID, "bad table/capacity/count");
+    const std::vector<tide::Seg>& segs = op_state(plan, tide::Op(op)).segs;
+    *count = int64_t(segs.size());
+    const int64_t n = capacity < *count ? capacity : *count;
+    for (int64_t i = 0; i < n; ++i) {
+      const tide::Seg& s = segs[size_t(i)];
+      int64_t* row = table + 6 * i;
+      row[0] = s.kind;
+      row[1] = s.src_idx;
+      row[2] = s.dst_idx;
+      row[3] = s.src_off;
+      row[4] = s.dst_off;
+      row[5] = s.len;
+    }
+    return TIDE_OK;
+  });
 }
 
 tide_status tide_plan_set_options(tide_plan* plan, const tide_options* opt) {
-  g_last_error.clear();
-  if (!live(plan)) return fail(TIDE_ERR_INVALID, "unknown or destroyed plan");
-  std::string why;
-  tide_options given;
-  tide_status st = tide::check_options(opt, &given, &why);
-  if (st != TIDE_OK) return fail(st, why);
-  st = rebuild_chunks(plan, given);
-  if (st != TIDE_OK) return st;
-  plan->given = given;
-  return TIDE_OK;
+  return tide::guarded([&]() -> tide_status {
+    g_last_error.clear();
+    if (!live(plan)) return fail(TIDE_ERR_INVALID, "unknown or destroyed plan");
+    std::string why;
+    tide_options given;
+    tide_status st = tide::check_options(opt, &given, &why);
+    if (st != TIDE_OK) return fail(st, why);
+    st = rebuild_chunks(plan, given);
+    if (st != TIDE_OK) return st;
+    plan->given = given;
+    return TIDE_OK;
+  });
 }
 
 tide_status tide_plan_get_options(const tide_plan* plan, int32_t op, tide_options* out) {
-  g_last_error.clear();
-  if (!live(plan)) return fail(TIDE_ERR_INVALID, "unknown or destroyed plan");
-  if (op < 0 || op >= tide::kNumOps) return fail(TIDE_ERR_INVALID, std::string("op must be ") + kOpNames);
-  if (out == nullptr) return fail(TIDE_ERR_INVALID, "out must not be NULL");
-  *out = tide::effective_options(plan->given, tide::Op(op), plan->cu_count);
-  return TIDE_OK;
+  return tide::guarded([&]() -> tide_status {
+    g_last_error.clear();
+    if (!live(plan)) return fail(TIDE_ERR_INVALID, "unknown or destroyed plan");
+    if (op < 0 || op >= tide::kNumOps) return fail(TIDE_ERR_INVALID, std::string("op must be ") + kOpNames);
+    if (out == nullptr) return fail(TIDE_ERR_INVALID, "out must not be NULL");
+    *out = tide::effective_options(plan->given, tide::Op(op), plan->cu_count);
+    return TIDE_OK;
+  });
 }
 
 tide_status tide_reduce_scatter_local(tide_plan* plan, const uint16_t* const* grads, float* const* out,
                                       float alpha, int32_t accumulate, void* stream) {
-  return reduce_scatter(plan, reinterpret_cast<const void* const*>(grads), false, out, alpha, accumulate, stream);
+  return tide::guarded([&]() -> tide_status {
+    return reduce_scatter(plan, reinterpret_cast<const void* const*>(grads), false, out, alpha, accumulate, stream);
+  });
 }
 
 tide_status tide_reduce_scatter_local_f32(tide_plan* plan, const float* const* grads, float* const* out,
                                           float alpha, int32_t accumulate, void* stream) {
-  return reduce_scatter(plan, reinterpret_cast<const void* const*>(grads), true, out, alpha, accumulate, stream);
+  return tide::guarded([&]() -> tide_status {
+    return reduce_scatter(plan, reinterpret_cast<const void* const*>(grads), true, out, alpha, accumulate, stream);
+  });
 }
 
 tide_status tide_allgather_copyout(tide_plan* plan, const uint16_t* rank_major, uint16_t* const* params,
                                    void* stream) {
-  g_last_error.clear();
-  if (!live(plan)) return fail(TIDE_ERR_INVALID, "unknown or destroyed plan");
-  if (params == nullptr) return fail(TIDE_ERR_INVALID, "params must not be NULL");
-  const tide::Geometry& g = plan->geo;
-  const int64_t P = g.nparams;
-  for (int64_t p = 0; p < P; ++p) {
-    if (g.D[p] * g.K[p] == 0) continue;
-    if (params[p] == nullptr) return fail(TIDE_ERR_INVALID, "params[" + std::to_string(p) + "] is NULL");
-    if (reinterpret_cast<uintptr_t>(params[p]) & 1)
-      return fail(TIDE_ERR_ALIGN, "params[" + std::to_string(p) + "] is not 2-byte aligned");
-  }
-  if (plan->co.chunk_begin.back() == 0) return TIDE_OK;  // nothing to write
-  if (rank_major == nullptr) return fail(TIDE_ERR_INVALID, "rank_major must not be NULL");
-  if (reinterpret_cast<uintptr_t>(rank_major) & 1) return fail(TIDE_ERR_ALIGN, "rank_major is not 2-byte aligned");
-  std::vector<const void*> key(params, params + P);
-  key.push_back(rank_major);
-  return run_op(
-      plan, tide::kOpCo, key,
-      [&](std::vector<tide::CallHdr>* hdr, std::vector<const void*>* ptrs) {
-        tide::co_call_table(g, plan->co.segs, rank_major, params, hdr, ptrs);
-      },
-      static_cast<hipStream_t>(stream));
+  return tide::guarded([&]() -> tide_status {
+    g_last_error.clear();
+    if (!live(plan)) return fail(TIDE_ERR_INVALID, "unknown or destroyed plan");
+    if (params == nullptr) return fail(TIDE_ERR_INVALID, "params must not be NULL");
+    const tide::Geometry& g = plan->geo;
+    const int64_t P = g.nparams;
+    for (int64_t p = 0; p < P; ++p) {
+      if (g.D[p] * g.K[p] == 0) continue;
+      if (params[p] == nullptr) return fail(TIDE_ERR_INVALID, "params[" + std::to_string(p) + "] is NULL");
+      if (reinterpret_cast<uintptr_t>(params[p]) & 1)
+        return fail(TIDE_ERR_ALIGN, "params[" + std::to_string(p) + "] is not 2-byte aligned");
+    }
+    if (plan->co.chunk_begin.back() == 0) return TIDE_OK;  // nothing to write
+    if (rank_major == nullptr) return fail(TIDE_ERR_INVALID, "rank_major must not be NULL");
+    if (reinterpret_cast<uintptr_t>(rank_major) & 1) return fail(TIDE_ERR_ALIGN, "rank_major is not 2-byte aligned");
+    std::vector<const void*> key(params, params + P);
+    key.push_back(rank_major);
+    return run_op(
+        plan, tide::kOpCo, key,
+        [&](std::vector<tide::CallHdr>* hdr, std::vector<const void*>* ptrs) {
+          tide::co_call_table(g, plan->co.segs, rank_major, params, hdr, ptrs);
+        },
+        static_cast<hipStream_t>(stream));
+  });
 }
 
 tide_status tide_allgather_copyin(tide_plan* plan, const void* const* shards, int32_t shard_dtype,
                                   uint16_t* rank_major, void* stream) {
-  g_last_error.clear();
-  if (!live(plan)) return fail(TIDE_ERR_INVALID, "unknown or destroyed plan");
-  if (shards == nullptr) return fail(TIDE_ERR_INVALID, "shards must not be NULL");
-  if (shard_dtype != TIDE_DTYPE_BF16 && shard_dtype != TIDE_DTYPE_F32)
-    return fail(TIDE_ERR_INVALID, "shard_dtype must be TIDE_DTYPE_BF16 or TIDE_DTYPE_F32");
-  const tide::Geometry& g = plan->geo;
-  const int64_t W = g.world, P = g.nparams;
-  const uintptr_t align = shard_dtype == TIDE_DTYPE_F32 ? 4 : 2;
-  for (int64_t r = 0; r < W; ++r) {
-    for (int64_t p = 0; p < P; ++p) {
-      if (tide::real_elems(g, int32_t(p), int32_t(r)) == 0) continue;
-      const void* s = shards[r * P + p];
-      if (s == nullptr) return fail(TIDE_ERR_INVALID, "shards[" + std::to_string(r * P + p) + "] is NULL");
-      if (reinterpret_cast<uintptr_t>(s) & (align - 1))
-        return fail(TIDE_ERR_ALIGN, "shards[" + std::to_string(r * P + p) + "] is not aligned to its element size");
+  return tide::guarded([&]() -> tide_status {
+    g_last_error.clear();
+    if (!live(plan)) return fail(TIDE_ERR_INVALID, "unknown or destroyed plan");
+    if (shards == nullptr) return fail(TIDE_ERR_INVALID, "shards must not be NULL");
+    if (shard_dtype != TIDE_DTYPE_BF16 && shard_dtype != TIDE_DTYPE_F32)
+      return fail(TIDE_ERR_INVALID, "shard_dtype must be TIDE_DTYPE_BF16 or TIDE_DTYPE_F32");
+    const tide::Geometry& g = plan->geo;
+    const int64_t W = g.world, P = g.nparams;
+    const uintptr_t align = shard_dtype == TIDE_DTYPE_F32 ? 4 : 2;
+    for (int64_t r = 0; r < W; ++r) {
+      for (int64_t p = 0; p < P; ++p) {
+        if (tide::real_elems(g, int32_t(p), int32_t(r)) == 0) continue;
+        const void* s = shards[r * P + p];
+        if (s == nullptr) return fail(TIDE_ERR_INVALID, "shards[" + std::to_string(r * P + p) + "] is NULL");
+        if (reinterpret_cast<uintptr_t>(s) & (align - 1))
+          return fail(TIDE_ERR_ALIGN, "shards[" + std::to_string(r * P + p) + "] is not aligned to its element size");
+      }
     }
-  }
-  if (plan->ci.chunk_begin.back() == 0) return TIDE_OK;  // nothing to write
-  if (rank_major == nullptr) return fail(TIDE_ERR_INVALID, "rank_major must not be NULL");
-  if (reinterpret_cast<uintptr_t>(rank_major) & 1) return fail(TIDE_ERR_ALIGN, "rank_major is not 2-byte aligned");
-  const bool f32 = shard_dtype == TIDE_DTYPE_F32;
-  std::vector<const void*> key(shards, shards + W * P);
-  key.push_back(rank_major);
-  key.push_back(reinterpret_cast<const void*>(uintptr_t(shard_dtype)));
-  return run_op(
-      plan, tide::kOpCi, key,
-      [&](std::vector<tide::CallHdr>* hdr, std::vector<const void*>* ptrs) {
-        tide::ci_call_table(g, plan->ci.segs, shards, f32, rank_major, hdr, ptrs);
-      },
-      static_cast<hipStream_t>(stream), f32);
+    if (plan->ci.chunk_begin.back() == 0) return TIDE_OK;  // nothing to write
+    if (rank_major == nullptr) return fail(TIDE_ERR_INVALID, "rank_major must not be NULL");
+    if (reinterpret_cast<uintptr_t>(rank_major) & 1) return fail(TIDE_ERR_ALIGN, "rank_major is not 2-byte aligned");
+    const bool f32 = shard_dtype == TIDE_DTYPE_F32;
+    std::vector<const void*> key(shards, shards + W * P);
+    key.push_back(rank_major);
+    key.push_back(reinterpret_cast<const void*>(uintptr_t(shard_dtype)));
+    return run_op(
+        plan, tide::kOpCi, key,
+        [&](std::vector<tide::CallHdr>* hdr, std::vector<const void*>* ptrs) {
+          tide::ci_call_table(g, plan->ci.segs, shards, f32, rank_major, hdr, ptrs);
+        },
+        static_cast<hipStream_t>(stream), f32);
+  });
 }
 
 tide_status tide_stock_chunk_cat(tide_plan* plan, const uint16_t* const* grads, float* packed, void* stream) {
-  g_last_error.clear();
-  if (!live(plan)) return fail(TIDE_ERR_INVALID, "unknown or destroyed plan");
-  if (grads == nullptr) return fail(TIDE_ERR_INVALID, "grads must not be NULL");
-  const tide::Geometry& g = plan->geo;
-  const int64_t P = g.nparams;
-  for (int64_t p = 0; p < P; ++p) {
-    if (g.D[p] * g.K[p] == 0) continue;
-    if (grads[p] == nullptr) return fail(TIDE_ERR_INVALID, "grads[" + std::to_string(p) + "] is NULL");
-    if (reinterpret_cast<uintptr_t>(grads[p]) & 1)
-      return fail(TIDE_ERR_ALIGN, "grads[" + std::to_string(p) + "] is not 2-byte aligned");
-  }
-  if (plan->pk.chunk_begin.back() == 0) return TIDE_OK;  // nothing to write
-  if (packed == nullptr) return fail(TIDE_ERR_INVALID, "packed must not be NULL");
-  if (reinterpret_cast<uintptr_t>(packed) & 3) return fail(TIDE_ERR_ALIGN, "packed is not 4-byte aligned");
-  std::vector<const void*> key(grads, grads + P);
-  key.push_back(packed);
-  return run_op(
-      plan, tide::kOpPack, key,
-      [&](std::vector<tide::CallHdr>* hdr, std::vector<const void*>* ptrs) {
-        tide::pk_call_table(g, plan->pk.segs, grads, packed, hdr, ptrs);
-      },
-      static_cast<hipStream_t>(stream));
+  return tide::guarded([&]() -> tide_status {
+    g_last_error.clear();
+    if (!live(plan)) return fail(TIDE_ERR_INVALID, "unknown or destroyed plan");
+    if (grads == nullptr) return fail(TIDE_ERR_INVALID, "grads must not be NULL");
+    const tide::Geometry& g = plan->geo;
+    const int64_t P = g.nparams;
+    for (int64_t p = 0; p < P; ++p) {
+      if (g.D[p] * g.K[p] == 0) continue;
+      if (grads[p] == nullptr) return fail(TIDE_ERR_INVALID, "grads[" + std::to_string(p) + "] is NULL");
+      if (reinterpret_cast<uintptr_t>(grads[p]) & 1)
+        return fail(TIDE_ERR_ALIGN, "grads[" + std::to_string(p) + "] is not 2-byte aligned");
+    }
+    if (plan->pk.chunk_begin.back() == 0) return TIDE_OK;  // nothing to write
+    if (packed == nullptr) return fail(TIDE_ERR_INVALID, "packed must not be NULL");
+    if (reinterpret_cast<uintptr_t>(packed) & 3) return fail(TIDE_ERR_ALIGN, "packed is not 4-byte aligned");
+    std::vector<const void*> key(grads, grads + P);
+    key.push_back(packed);
+    return run_op(
+        plan, tide::kOpPack, key,
+        [&](std::vector<tide::CallHdr>* hdr, std::vector<const void*>* ptrs) {
+          tide::pk_call_table(g, plan->pk.segs, grads, packed, hdr, ptrs);
+        },
+        static_cast<hipStream_t>(stream));
+  });
 }
 
 void tide_plan_destroy(tide_plan* plan) {

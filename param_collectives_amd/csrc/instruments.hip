@@ -113,102 +113,113 @@ extern "C" {
 
 tide_status tide_device_info(int32_t* cu_count, int32_t* max_lds_per_workgroup, int32_t* lds_per_cu,
                              int32_t* wall_clock_khz) {
-  tide::clear_error();
-  tide_status st;
-  if (lds_per_cu &&
-      (st = current_attribute(hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, lds_per_cu,
-                              "hipDeviceGetAttribute")) != TIDE_OK)
-    return st;
-  if (cu_count &&
-      (st = current_attribute(hipDeviceAttributeMultiprocessorCount, cu_count, "hipDeviceGetAttribute")) != TIDE_OK)
-    return st;
-  if (max_lds_per_workgroup &&
-      (st = current_attribute(hipDeviceAttributeMaxSharedMemoryPerBlock, max_lds_per_workgroup,
-                              "hipDeviceGetAttribute")) != TIDE_OK)
-    return st;
-  if (wall_clock_khz &&
-      (st = current_attribute(hipDeviceAttributeWallClockRate, wall_clock_khz, "hipDeviceGetAttribute")) != TIDE_OK)
-    return st;
-  return TIDE_OK;
+  return tide::guarded([&]() -> tide_status {
+    tide::clear_error();
+    tide_status st;
+    if (lds_per_cu &&
+        (st = current_attribute(hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, lds_per_cu,
+                                "hipDeviceGetAttribute")) != TIDE_OK)
+      return st;
+    if (cu_count &&
+        (st = current_attribute(hipDeviceAttributeMultiprocessorCount, cu_count, "hipDeviceGetAttribute")) != TIDE_OK)
+      return st;
+    if (max_lds_per_workgroup &&
+        (st = current_attribute(hipDeviceAttributeMaxSharedMemoryPerBlock, max_lds_per_workgroup,
+                                "hipDeviceGetAttribute")) != TIDE_OK)
+      return st;
+    if (wall_clock_khz &&
+        (st = current_attribute(hipDeviceAttributeWallClockRate, wall_clock_khz, "hipDeviceGetAttribute")) != TIDE_OK)
+      return st;
+    return TIDE_OK;
+  });
 }
 
 tide_status tide_probe_launch(uint32_t* records, int32_t grid, int32_t lds_bytes, int64_t hold_ns, void* stream) {
-  tide::clear_error();
-  if (records == nullptr) return tide::set_error(TIDE_ERR_INVALID, "records must not be NULL");
-  if (reinterpret_cast<uintptr_t>(records) & 3) return tide::set_error(TIDE_ERR_ALIGN, "records is not 4-byte aligned");
-  if (grid < 1 || grid > 65536) return tide::set_error(TIDE_ERR_INVALID, "grid must be in [1, 65536]");
-  if (hold_ns < 0 || hold_ns > 1000000000) return tide::set_error(TIDE_ERR_INVALID, "hold_ns must be in [0, 1e9]");
-  int32_t max_lds = 0, khz = 0;
-  tide_status st = tide_device_info(nullptr, &max_lds, nullptr, &khz);
-  if (st != TIDE_OK) return st;
-  if (lds_bytes < 0 || lds_bytes > max_lds)
-    return tide::set_error(TIDE_ERR_INVALID, "lds_bytes must be in [0, " + std::to_string(max_lds) + "]");
-  if (lds_bytes > 65536) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&hw_probe_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
-    if (e != hipSuccess) return hip_error(e, "hipFuncSetAttribute");
-  }
-  const int64_t ticks = hold_ns * int64_t(khz) / 1000000;
-  hipLaunchKernelGGL(hw_probe_kernel, dim3(unsigned(grid)), dim3(unsigned(kProbeThreads)), size_t(lds_bytes),
-                     static_cast<hipStream_t>(stream), records, ticks, int32_t(lds_bytes >= 4));
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return hip_error(e, "hw_probe_kernel launch");
-  return TIDE_OK;
+  return tide::guarded([&]() -> tide_status {
+    tide::clear_error();
+    if (records == nullptr) return tide::set_error(TIDE_ERR_INVALID, "records must not be NULL");
+    if (reinterpret_cast<uintptr_t>(records) & 3)
+      return tide::set_error(TIDE_ERR_ALIGN, "records is not 4-byte aligned");
+    if (grid < 1 || grid > 65536) return tide::set_error(TIDE_ERR_INVALID, "grid must be in [1, 65536]");
+    if (hold_ns < 0 || hold_ns > 1000000000) return tide::set_error(TIDE_ERR_INVALID, "hold_ns must be in [0, 1e9]");
+    int32_t max_lds = 0, khz = 0;
+    tide_status st = tide_device_info(nullptr, &max_lds, nullptr, &khz);
+    if (st != TIDE_OK) return st;
+    if (lds_bytes < 0 || lds_bytes > max_lds)
+      return tide::set_error(TIDE_ERR_INVALID, "lds_bytes must be in [0, " + std::to_string(max_lds) + "]");
+    if (lds_bytes > 65536) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&hw_probe_kernel),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+      if (e != hipSuccess) return hip_error(e, "hipFuncSetAttribute");
+    }
+    const int64_t ticks = hold_ns * int64_t(khz) / 1000000;
+    hipLaunchKernelGGL(hw_probe_kernel, dim3(unsigned(grid)), dim3(unsigned(kProbeThreads)), size_t(lds_bytes),
+                       static_cast<hipStream_t>(stream), records, ticks, int32_t(lds_bytes >= 4));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_error(e, "hw_probe_kernel launch");
+    return TIDE_OK;
+  });
 }
 
 tide_status tide_victim_axpb(const float* x, float* y, int64_t n, float a, float b, void* stream) {
-  tide::clear_error();
-  if (n < 0) return tide::set_error(TIDE_ERR_INVALID, "n must be >= 0");
-  if (n == 0) return TIDE_OK;
-  if (x == nullptr || y == nullptr) return tide::set_error(TIDE_ERR_INVALID, "x and y must not be NULL");
-  if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y)) & 3)
-    return tide::set_error(TIDE_ERR_ALIGN, "x and y must be 4-byte aligned");
-  const bool vec = ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y)) & 15) == 0 && n % 4 == 0;
-  const int64_t items = vec ? n / 4 : n;
-  const int64_t grid = (items + kAxpbThreads - 1) / kAxpbThreads;
-  if (grid > INT32_MAX) return tide::set_error(TIDE_ERR_RANGE, "n is too large");
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (vec) {
-    hipLaunchKernelGGL(axpb_kernel<true>, dim3(unsigned(grid)), dim3(unsigned(kAxpbThreads)), 0, s, x, y, n, a, b);
-  } else {
-    hipLaunchKernelGGL(axpb_kernel<false>, dim3(unsigned(grid)), dim3(unsigned(kAxpbThreads)), 0, s, x, y, n, a, b);
-  }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return hip_error(e, "axpb_kernel launch");
-  return TIDE_OK;
+  return tide::guarded([&]() -> tide_status {
+    tide::clear_error();
+    if (n < 0) return tide::set_error(TIDE_ERR_INVALID, "n must be >= 0");
+    if (n == 0) return TIDE_OK;
+    if (x == nullptr || y == nullptr) return tide::set_error(TIDE_ERR_INVALID, "x and y must not be NULL");
+    if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y)) & 3)
+      return tide::set_error(TIDE_ERR_ALIGN, "x and y must be 4-byte aligned");
+    const bool vec = ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y)) & 15) == 0 && n % 4 == 0;
+    const int64_t items = vec ? n / 4 : n;
+    const int64_t grid = (items + kAxpbThreads - 1) / kAxpbThreads;
+    if (grid > INT32_MAX) return tide::set_error(TIDE_ERR_RANGE, "n is too large");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (vec) {
+      hipLaunchKernelGGL(axpb_kernel<true>, dim3(unsigned(grid)), dim3(unsigned(kAxpbThreads)), 0, s, x, y, n, a, b);
+    } else {
+      hipLaunchKernelGGL(axpb_kernel<false>, dim3(unsigned(grid)), dim3(unsigned(kAxpbThreads)), 0, s, x, y, n, a, b);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_error(e, "axpb_kernel launch");
+    return TIDE_OK;
+  });
 }
 
 tide_status tide_stream_create(const uint32_t* cu_mask, int32_t mask_words, void** out_stream) {
-  tide::clear_error();
-  if (out_stream == nullptr) return tide::set_error(TIDE_ERR_INVALID, "out_stream must not be NULL");
-  *out_stream = nullptr;
-  hipStream_t s = nullptr;
-  hipError_t e;
-  if (cu_mask == nullptr) {
-    e = hipStreamCreateWithFlags(&s, hipStreamNonBlocking);
-  } else {
-    int32_t cus = 0;
-    tide_status st = tide_device_info(&cus, nullptr, nullptr, nullptr);
-    if (st != TIDE_OK) return st;
-    if (mask_words < 1 || int64_t(mask_words) * 32 < cus)
-      return tide::set_error(TIDE_ERR_INVALID, "cu_mask must have at least ceil(cu_count / 32) = " +
-                                                   std::to_string((cus + 31) / 32) + " words");
-    bool any = false;
-    for (int32_t i = 0; i < cus; ++i) any = any || ((cu_mask[i / 32] >> (i % 32)) & 1u);
-    if (!any) return tide::set_error(TIDE_ERR_INVALID, "cu_mask selects no CU");
-    e = hipExtStreamCreateWithCUMask(&s, uint32_t(mask_words), cu_mask);
-  }
-  if (e != hipSuccess) return hip_error(e, cu_mask ? "hipExtStreamCreateWithCUMask" : "hipStreamCreateWithFlags");
-  *out_stream = s;
-  return TIDE_OK;
+  return tide::guarded([&]() -> tide_status {
+    tide::clear_error();
+    if (out_stream == nullptr) return tide::set_error(TIDE_ERR_INVALID, "out_stream must not be NULL");
+    *out_stream = nullptr;
+    hipStream_t s = nullptr;
+    hipError_t e;
+    if (cu_mask == nullptr) {
+      e = hipStreamCreateWithFlags(&s, hipStreamNonBlocking);
+    } else {
+      int32_t cus = 0;
+      tide_status st = tide_device_info(&cus, nullptr, nullptr, nullptr);
+      if (st != TIDE_OK) return st;
+      if (mask_words < 1 || int64_t(mask_words) * 32 < cus)
+        return tide::set_error(TIDE_ERR_INVALID, "cu_mask must have at least ceil(cu_count / 32) = " +
+                                                     std::to_string((cus + 31) / 32) + " words");
+      bool any = false;
+      for (int32_t i = 0; i < cus; ++i) any = any || ((cu_mask[i / 32] >> (i % 32)) & 1u);
+      if (!any) return tide::set_error(TIDE_ERR_INVALID, "cu_mask selects no CU");
+      e = hipExtStreamCreateWithCUMask(&s, uint32_t(mask_words), cu_mask);
+    }
+    if (e != hipSuccess) return hip_error(e, cu_mask ? "hipExtStreamCreateWithCUMask" : "hipStreamCreateWithFlags");
+    *out_stream = s;
+    return TIDE_OK;
+  });
 }
 
 tide_status tide_stream_destroy(void* stream) {
-  tide::clear_error();
-  if (stream == nullptr) return TIDE_OK;
-  hipError_t e = hipStreamDestroy(static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_error(e, "hipStreamDestroy");
-  return TIDE_OK;
+  return tide::guarded([&]() -> tide_status {
+    tide::clear_error();
+    if (stream == nullptr) return TIDE_OK;
+    hipError_t e = hipStreamDestroy(static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_error(e, "hipStreamDestroy");
+    return TIDE_OK;
+  });
 }
 
 }  // extern "C"

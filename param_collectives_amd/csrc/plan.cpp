@@ -71,8 +71,9 @@ tide_status build_geometry(int32_t world, int32_t nparams, const int32_t* ndims,
     }
   }
   int64_t whole;
-  if (__builtin_mul_overflow(offset, int64_t(world), &whole)) {
-    *why = "W * S overflows int64";
+  // Every element offset (at most W * S) is later scaled to bytes, by up to 4.
+  if (__builtin_mul_overflow(offset, int64_t(world), &whole) || whole > INT64_MAX / 4) {
+    *why = "W * S elements exceed 2^61";
     return TIDE_ERR_RANGE;
   }
   g->S = offset;

@@ -4,6 +4,7 @@
 #pragma once
 
 #include <cstdint>
+#include <new>
 #include <string>
 #include <vector>
 
@@ -155,6 +156,23 @@ struct KernelArgs {
 // source file of the C ABI.  set_error stores `msg` and returns `st`.
 tide_status set_error(tide_status st, const std::string& msg);
 void clear_error();
+
+// Records a failure without allocating (for use where allocation failed).
+tide_status set_error_nothrow(tide_status st, const char* msg) noexcept;
+
+// Runs the body of a C-ABI entry point.  No C++ exception crosses the C ABI:
+// a failed host allocation becomes TIDE_ERR_NOMEM, anything else thrown
+// TIDE_ERR_INVALID, each with a message.
+template <typename F>
+tide_status guarded(F&& body) noexcept {
+  try {
+    return body();
+  } catch (const std::bad_alloc&) {
+    return set_error_nothrow(TIDE_ERR_NOMEM, "out of host memory");
+  } catch (...) {
+    return set_error_nothrow(TIDE_ERR_INVALID, "unexpected host-side exception");
+  }
+}
 
 // Launch with `grid` workgroups of kThreads on `stream`; returns the launch
 // status (hipError_t as int).

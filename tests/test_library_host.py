@@ -56,6 +56,16 @@ CASES = [
 ]
 
 
+def test_sizes_whose_byte_offsets_overflow_are_a_range_error(tide):
+    # W * S elements must stay within 2^61 so that fp32 byte offsets fit int64
+    with pytest.raises(tide.TideError) as e:
+        tide.Plan(4, [(2**59 + 4,)])
+    assert _status(e) == -2
+    with pytest.raises(tide.TideError) as e:
+        tide.Plan(1, [(2**60,), (2**60,)])
+    assert _status(e) == -2
+
+
 @pytest.mark.parametrize("world,shapes", CASES)
 def test_layout_matches_oracle(tide, oracle_mod, world, shapes):
     plan = tide.Plan(world, shapes)
