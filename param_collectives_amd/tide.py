@@ -182,10 +182,18 @@ class Plan:
 
     # ------------------------------------------------------------ raw calls
 
+    @staticmethod
+    def _lengths(values, n, what):
+        # the library reads exactly n entries of each pointer array
+        if len(values) != n:
+            raise ValueError(f"{what} must hold {n} addresses, got {len(values)}")
+
     def reduce_scatter_local_raw(self, grad_ptrs, out_ptrs, alpha=1.0, accumulate=0, stream=0, f32=False):
         """tide_reduce_scatter_local (bf16 gradients) or, with f32=True,
         tide_reduce_scatter_local_f32 on raw device addresses: grad_ptrs[u*P+p],
         out_ptrs[r] (ints), stream a hipStream_t handle (int)."""
+        self._lengths(grad_ptrs, self.world * len(self.shapes), "grad_ptrs")
+        self._lengths(out_ptrs, self.world, "out_ptrs")
         fn = lib.tide_reduce_scatter_local_f32 if f32 else lib.tide_reduce_scatter_local
         _check(fn(self.handle, _ptr_array(grad_ptrs), _ptr_array(out_ptrs), float(alpha), int(accumulate),
                   ctypes.c_void_p(int(stream) or None)))
@@ -193,17 +201,20 @@ class Plan:
     def stock_chunk_cat_raw(self, grad_ptrs, packed_ptr, stream=0):
         """tide_stock_chunk_cat on raw device addresses (grad_ptrs[p] of one
         rank, packed_ptr to W*S fp32 elements)."""
+        self._lengths(grad_ptrs, len(self.shapes), "grad_ptrs")
         _check(lib.tide_stock_chunk_cat(self.handle, _ptr_array(grad_ptrs), ctypes.c_void_p(int(packed_ptr) or None),
                                         ctypes.c_void_p(int(stream) or None)))
 
     def allgather_copyin_raw(self, shard_ptrs, shard_dtype, rank_major_ptr, stream=0):
         """tide_allgather_copyin on raw device addresses (shard_ptrs[r*P+p])."""
+        self._lengths(shard_ptrs, self.world * len(self.shapes), "shard_ptrs")
         _check(lib.tide_allgather_copyin(self.handle, _ptr_array(shard_ptrs), int(shard_dtype),
                                          ctypes.c_void_p(int(rank_major_ptr) or None),
                                          ctypes.c_void_p(int(stream) or None)))
 
     def allgather_copyout_raw(self, rank_major_ptr, param_ptrs, stream=0):
         """tide_allgather_copyout on raw device addresses."""
+        self._lengths(param_ptrs, len(self.shapes), "param_ptrs")
         _check(lib.tide_allgather_copyout(self.handle, ctypes.c_void_p(int(rank_major_ptr) or None),
                                           _ptr_array(param_ptrs), ctypes.c_void_p(int(stream) or None)))
 
@@ -222,6 +233,9 @@ def _require(t, dtype, numel, what):
         raise TypeError(f"{what}: expected a torch.Tensor")
     if t.device.type != "cuda":
         raise ValueError(f"{what}: expected a GPU tensor, got {t.device}")
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{what}: lives on {t.device}, but the kernels run on the current device "
+                         f"cuda:{torch.cuda.current_device()}")
     if t.dtype != dtype:
         raise TypeError(f"{what}: expected {dtype}, got {t.dtype}")
     if not t.is_contiguous():

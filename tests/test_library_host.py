@@ -283,6 +283,25 @@ def test_copyout_argument_errors(tide):
     assert _status(e) == -1
 
 
+def test_raw_calls_check_pointer_counts(tide):
+    # the library reads exactly W*P, W or P addresses: a short list is refused
+    # before the call
+    plan = tide.Plan(4, oracle_pins.TINY_SHAPES)
+    g = [FAKE + 0x1000 * i for i in range(16)]
+    o = [FAKE + 0x100000 + 0x1000 * r for r in range(4)]
+    calls = [
+        lambda: plan.reduce_scatter_local_raw(g[:15], o),
+        lambda: plan.reduce_scatter_local_raw(g, o[:3]),
+        lambda: plan.reduce_scatter_local_raw(g + [FAKE], o, f32=True),
+        lambda: plan.stock_chunk_cat_raw(g[:3], FAKE),
+        lambda: plan.allgather_copyout_raw(FAKE, g[:5]),
+        lambda: plan.allgather_copyin_raw(g[:12], tide.DTYPE_F32, FAKE),
+    ]
+    for call in calls:
+        with pytest.raises(ValueError, match="addresses"):
+            call()
+
+
 def test_destroyed_plan_is_rejected(tide):
     plan = tide.Plan(2, [(4,)])
     handle = plan.handle
