@@ -350,8 +350,31 @@ def main(argv=None):
                     "shards": "bit-identical" if same else "MISMATCH"}
         return stock_ab
 
+    def host_enqueue(n=50):
+        """Host time to enqueue one operation call, in microseconds: a
+        registered call (pointers marshalled once, as an FSDP2 group reuses its
+        buffers) and a one-off call (every tensor checked and marshalled)."""
+        out = {}
+        for name, fn in (
+                ("rs_local_registered", rs),
+                ("ag_copyout_registered", co),
+                ("rs_local_one_off", lambda: tide.reduce_scatter_local(plan, grads, outs, stream=stream)),
+                ("ag_copyout_one_off", lambda: tide.allgather_copyout(plan, rank_major, params, stream=stream))):
+            fn()
+            stream.synchronize()
+            t = time.perf_counter()
+            for _ in range(n):
+                fn()
+            dt = time.perf_counter() - t
+            stream.synchronize()
+            out[name] = round(dt / n * 1e6, 1)
+        return out
+
     stock_ab = None
+    host_us = None
     if not args.no_extras:
+        # (rewrites the timed outputs with the same values)
+        host_us = host_enqueue()
         # Equation 5's epilogue: alpha = 1/W, accumulating into separate shards
         # (the timed outputs stay as they are for the parity check below); the
         # shards are read as well: 4*W*S more bytes
@@ -436,6 +459,7 @@ def main(argv=None):
         "d2d_copy": d2d,
         "parity": parity,
         "stock_ab": stock_ab,
+        "host_enqueue_us": host_us,
     }
     print(json.dumps(line), flush=True)
     if (parity and "MISMATCH" in parity.values()) or (stock_ab and stock_ab["shards"] != "bit-identical"):

@@ -104,8 +104,9 @@ typedef enum {
  *   wg_per_cu   workgroups (256 threads, four waves) per budgeted CU;
  *               default 1.
  *   chunk_elems elements per chunk (the unit a wave takes), a multiple of 8,
- *               at most 2^28; default 1024 (reduce-scatter), 4096 (copy-out,
- *               copy-in), 2048 (stock pack).
+ *               at most 2^28; default 1024 (reduce-scatter), 512
+ *               (reduce-scatter of fp32 gradients), 4096 (copy-out, copy-in),
+ *               2048 (stock pack).
  *               A plan may have at most 2^30 chunks per operation.
  *   flags       TIDE_FLAG_* bits.
  *   wave_chunks at most this many chunks per wave in one kernel launch; an
@@ -156,7 +157,9 @@ tide_status tide_plan_layout(const tide_plan* plan, int64_t* rows_per_rank, int6
 
 /*
  * The plan's work segments, for inspection and tests.  op 0 = reduce-scatter,
- * 1 = copy-out, 2 = copy-in, 3 = stock pack.  Each segment is 6 int64 values:
+ * 1 = copy-out, 2 = copy-in, 3 = stock pack, 4 = reduce-scatter of fp32
+ * gradients (the same segments as op 0; it has its own chunk table and
+ * launch knobs).  Each segment is 6 int64 values:
  *   kind     0 = sum of the W ranks' sources, 1 = zero fill (padding),
  *            2 = copy (the copy-in casts instead when its shards are fp32;
  *            the stock pack widens bf16 to fp32)
@@ -180,8 +183,9 @@ tide_status tide_plan_segments(const tide_plan* plan, int32_t op, int64_t* table
 tide_status tide_plan_set_options(tide_plan* plan, const tide_options* opt);
 
 /* The launch knobs in effect for op 0 (reduce-scatter), 1 (copy-out),
- * 2 (copy-in) or 3 (stock pack), with defaults resolved (cu_budget is
- * resolved once the plan is bound to a device, 0 before). */
+ * 2 (copy-in), 3 (stock pack) or 4 (reduce-scatter of fp32 gradients), with
+ * defaults resolved (cu_budget is resolved once the plan is bound to a
+ * device, 0 before). */
 tide_status tide_plan_get_options(const tide_plan* plan, int32_t op, tide_options* out);
 
 /*
@@ -220,7 +224,8 @@ tide_status tide_reduce_scatter_local(tide_plan* plan, const uint16_t* const* gr
  * reduce-scatter of Section 4.3): as tide_reduce_scatter_local with
  * grads[u*P + p] fp32 (4-byte aligned) and g_u its value as it is.  With a
  * plan of one parameter of shape (W, S) this is also the reduce-scatter of
- * W ranks' pre-packed fp32 buffers (the stock path after its pack).
+ * W ranks' pre-packed fp32 buffers (the stock path after its pack).  Its
+ * launch knobs are those of op 4.
  */
 tide_status tide_reduce_scatter_local_f32(tide_plan* plan, const float* const* grads, float* const* out,
                                           float alpha, int32_t accumulate, void* stream);

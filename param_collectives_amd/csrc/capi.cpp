@@ -93,7 +93,7 @@ struct tide_plan {
   uint64_t magic = 0;
   tide::Geometry geo;
   tide_options given{};  // as passed (0 = default)
-  OpState rs, co, ci, pk;
+  OpState rs, co, ci, pk, rsf;  // rsf: the reduce-scatter of fp32 gradients
   int device = -1;
   int cu_count = 0;
 };
@@ -110,21 +110,25 @@ bool live(const tide_plan* p) {
   return g_plans.count(p) != 0 && p->magic == kMagic;
 }
 
-int32_t nsrc_of(const tide_plan* p, tide::Op op) { return op == tide::kOpRs ? p->geo.world : 1; }
+int32_t nsrc_of(const tide_plan* p, tide::Op op) {
+  return op == tide::kOpRs || op == tide::kOpRsF32 ? p->geo.world : 1;
+}
 
 OpState& op_state(tide_plan* p, tide::Op op) {
   switch (op) {
     case tide::kOpRs: return p->rs;
     case tide::kOpCo: return p->co;
     case tide::kOpCi: return p->ci;
-    default: return p->pk;
+    case tide::kOpPack: return p->pk;
+    default: return p->rsf;
   }
 }
 const OpState& op_state(const tide_plan* p, tide::Op op) { return op_state(const_cast<tide_plan*>(p), op); }
 
-const tide::Op kOps[tide::kNumOps] = {tide::kOpRs, tide::kOpCo, tide::kOpCi, tide::kOpPack};
+const tide::Op kOps[tide::kNumOps] = {tide::kOpRs, tide::kOpCo, tide::kOpCi, tide::kOpPack, tide::kOpRsF32};
 
-const char* const kOpNames = "0 (reduce-scatter), 1 (copy-out), 2 (copy-in) or 3 (stock pack)";
+const char* const kOpNames =
+    "0 (reduce-scatter), 1 (copy-out), 2 (copy-in), 3 (stock pack) or 4 (reduce-scatter of fp32 gradients)";
 
 tide_status rebuild_chunks(tide_plan* p, const tide_options& given) {
   std::string why;
@@ -311,6 +315,7 @@ tide_status run_op(tide_plan* p, tide::Op op, const std::vector<const void*>& ke
     const char* what = "";
     switch (op) {
       case tide::kOpRs:
+      case tide::kOpRsF32:
         rc = tide::launch_rs_local(a, f32, g, stream);
         what = "rs_local_kernel launch";
         break;
@@ -360,11 +365,11 @@ tide_status reduce_scatter(tide_plan* plan, const void* const* grads, bool f32, 
   }
   std::vector<const void*> key(grads, grads + W * P);
   key.insert(key.end(), out, out + W);
-  key.push_back(reinterpret_cast<const void*>(uintptr_t(f32)));
+  const tide::Op op = f32 ? tide::kOpRsF32 : tide::kOpRs;
   return run_op(
-      plan, tide::kOpRs, key,
+      plan, op, key,
       [&](std::vector<tide::CallHdr>* hdr, std::vector<const void*>* ptrs) {
-        tide::rs_call_table(g, plan->rs.segs, grads, f32, out, hdr, ptrs);
+        tide::rs_call_table(g, op_state(plan, op).segs, grads, f32, out, hdr, ptrs);
       },
       static_cast<hipStream_t>(stream), f32, alpha, accumulate);
 }
@@ -392,6 +397,7 @@ tide_status tide_plan_create(int32_t world, int32_t nparams, const int32_t* ndim
     p->co.segs = tide::copyout_segments(p->geo);
     p->ci.segs = tide::copyin_segments(p->geo);
     p->pk.segs = tide::pack_segments(p->geo);
+    p->rsf.segs = p->rs.segs;
     for (tide::Op op : kOps)
       if (op_state(p.get(), op).segs.size() >= size_t(INT32_MAX)) return fail(TIDE_ERR_RANGE, "too many segments");
     p->given = given;

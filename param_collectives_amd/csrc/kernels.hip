@@ -103,11 +103,6 @@ constexpr int kRsUnroll = 2;
 constexpr int kCoUnroll = 4;
 constexpr int kCastUnroll = 8;
 
-// Buffer-resource word 3 for raw (untyped) byte-addressed buffers on gfx9-class
-// GPUs, and the cache-policy operand bit that marks an access non-temporal.
-constexpr int kRawBuffer = 0x00020000;
-constexpr int kPolicyNT = 2;
-
 // ---------------------------------------------------------------------------
 // Chunk dealing and segment lookup (shared by every kernel)
 // ---------------------------------------------------------------------------
@@ -247,10 +242,6 @@ template <>
 struct Src<false> {
   using T = uint16_t;
   using V = u32x2;
-  template <int AUX>
-  static __device__ __forceinline__ V buffer_load(__amdgpu_buffer_rsrc_t r, int off) {
-    return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, AUX);
-  }
   static __device__ __forceinline__ void first(V v, float a[4]) {
     a[0] = bf16_lo(v.x);
     a[1] = bf16_hi(v.x);
@@ -272,11 +263,6 @@ template <>
 struct Src<true> {
   using T = float;
   using V = f32x4;
-  template <int AUX>
-  static __device__ __forceinline__ V buffer_load(__amdgpu_buffer_rsrc_t r, int off) {
-    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX);
-    return f32x4{__uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z), __uint_as_float(x.w)};
-  }
   static __device__ __forceinline__ void first(V v, float a[4]) {
     a[0] = v.x;
     a[1] = v.y;
@@ -368,13 +354,10 @@ __device__ __forceinline__ void sum_body(const void* const* src, int32_t W, floa
 #pragma unroll
     for (int u = 0; u < WT; ++u) s[u] = static_cast<const T*>(src[u]) + vlo;
     float* d = dst + vlo;
-    // Source loads go through buffer resources covering exactly this chunk's
-    // body (scalar base, 32-bit lane offsets, hardware range check).
-    __amdgpu_buffer_rsrc_t rs[WT];
-#pragma unroll
-    for (int u = 0; u < WT; ++u)
-      rs[u] = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(s[u]), 0, int((vhi - vlo) * int64_t(sizeof(T))),
-                                                kRawBuffer);
+    // Source loads address a scalar base (the chunk body's start) plus a
+    // 32-bit lane offset: two scalar registers per source, so that the next
+    // chunk's descriptor, fetched meanwhile, stays in scalar registers and no
+    // wait for it is needed before this chunk's loads.
     int64_t base = 0;
     for (; base + 64 * U <= ng; base += 64 * U) {
       V v[U][WT];
@@ -383,7 +366,7 @@ __device__ __forceinline__ void sum_body(const void* const* src, int32_t W, floa
       for (int k = 0; k < U; ++k) {
 #pragma unroll
         for (int u = 0; u < WT; ++u)
-          v[k][u] = S::template buffer_load<CL ? 0 : kPolicyNT>(rs[u], int((base + g + 64 * k) * kGroupBytes));
+          v[k][u] = load<V, CL>(reinterpret_cast<const char*>(s[u]) + uint32_t((base + g + 64 * k) * kGroupBytes));
         o[k] = old4<EPI>(d + (base + g + 64 * k) * 4);
       }
 #pragma unroll

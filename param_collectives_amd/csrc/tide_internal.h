@@ -25,8 +25,12 @@ constexpr int32_t kMaxStagedSegs = 16383;  // chunk-index table entries staged i
 // one workgroup (four waves) per CU keeps the HBM read/write mix most
 // efficient for every kernel; the reduce-scatter prefers small chunks (the
 // grid then sweeps a narrow window of every tensor), the copies larger ones.
+// With fp32 gradients the reduce-scatter reads twice the bytes per element,
+// and the best chunk is half as long (16 KiB of source reads either way).
 constexpr int32_t kRsWgPerCu = 1;
 constexpr int64_t kRsChunk = 1024;
+constexpr int32_t kRsF32WgPerCu = 1;
+constexpr int64_t kRsF32Chunk = 512;
 constexpr int32_t kCoWgPerCu = 1;
 constexpr int64_t kCoChunk = 4096;
 constexpr int32_t kCiWgPerCu = 1;
@@ -37,8 +41,10 @@ constexpr int32_t kMaxWaveChunks = 1 << 30;  // chunks per wave per launch: no s
 constexpr int32_t kWaveChunks = 64;  // measured on MI355X: 48-128 are equally good, 8 and no split 5-9% worse
 
 enum SegKind : int32_t { kSum = 0, kZero = 1, kCopy = 2, kCast = 3 };
-enum Op : int32_t { kOpRs = 0, kOpCo = 1, kOpCi = 2, kOpPack = 3 };
-constexpr int kNumOps = 4;
+// Operations with their own chunk tables and launch knobs.  kOpRsF32 is the
+// reduce-scatter of fp32 gradients: the same segments as kOpRs.
+enum Op : int32_t { kOpRs = 0, kOpCo = 1, kOpCi = 2, kOpPack = 3, kOpRsF32 = 4 };
+constexpr int kNumOps = 5;
 
 // One contiguous run of work, fixed by the plan (host only).
 struct Seg {

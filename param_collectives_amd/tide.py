@@ -148,8 +148,8 @@ class Plan:
 
     def segments(self, op):
         """The work segments (op 0: reduce-scatter, 1: copy-out, 2: copy-in,
-        3: stock pack) as an int64 array of rows (kind, src_idx, dst_idx,
-        src_off, dst_off, len)."""
+        3: stock pack, 4: reduce-scatter of fp32 gradients) as an int64 array
+        of rows (kind, src_idx, dst_idx, src_off, dst_off, len)."""
         count = ctypes.c_int64()
         _check(lib.tide_plan_segments(self.handle, int(op), None, 0, ctypes.byref(count)))
         table = np.zeros((max(count.value, 1), 6), dtype=np.int64)
@@ -163,7 +163,7 @@ class Plan:
 
     def options(self, op=0):
         """Effective launch knobs for op 0 (reduce-scatter), 1 (copy-out),
-        2 (copy-in) or 3 (stock pack)."""
+        2 (copy-in), 3 (stock pack) or 4 (reduce-scatter of fp32 gradients)."""
         opt = Options()
         _check(lib.tide_plan_get_options(self.handle, int(op), ctypes.byref(opt)))
         return {"cu_budget": opt.cu_budget, "wg_per_cu": opt.wg_per_cu, "chunk_elems": opt.chunk_elems,
