@@ -120,7 +120,7 @@ def launches_per_call(plan, op):
 def main(argv=None):
     args = parse_args(argv)
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); the W simulated ranks all live "
+        print(f"bench.py: bench.py measures one GPU only (got --gpus {args.gpus}); the W simulated ranks all live "
               "in one GPU's HBM. Run with --gpus 1.", file=sys.stderr)
         return 2
 

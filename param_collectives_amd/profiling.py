@@ -117,7 +117,7 @@ def _normalise(text):
     """Commands recorded on another machine: keep only repo-relative parts."""
     import re
 
-    text = re.sub(r"-d \S*/gpurun_out/[^/ ]+/", "-d <out>/", text)
+    text = re.sub(r"-d \S*/([^/ ]+)(?= )", r"-d <out>/\1", text)
     text = re.sub(r"\S*/bench\.py", "<repo>/bench.py", text)
     text = re.sub(r"\S*/python3?(?= )", "python", text)
     return text

@@ -73,7 +73,7 @@ class Options(ctypes.Structure):
 
 def _load():
     if not os.path.exists(LIBRARY):
-        raise ImportError(f"{LIBRARY} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
+        raise ImportError(f"{LIBRARY} is missing: build it with `python param_collectives_amd/build.py` "
                           "(the HIP path has no fallback)")
     lib = ctypes.CDLL(LIBRARY)
     vp, i32, i64, i64p = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.POINTER(ctypes.c_int64)
