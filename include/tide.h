@@ -54,7 +54,11 @@
  *   - Graph capture: once a plan has run an operation with the same pointers
  *     (and options) on the current device, a call of that operation enqueues
  *     kernel launches only (no allocation, copy or synchronization), so it may
- *     be recorded into a HIP graph and replayed.
+ *     be recorded into a HIP graph and replayed.  The recorded launches read
+ *     the plan's device tables each time they run: the plan must outlive the
+ *     graph, and a later call of that operation with other pointers, or
+ *     tide_plan_set_options, rewrites those tables and so changes what a
+ *     replay does (use one plan per set of buffers that a graph records).
  */
 #ifndef TIDE_H
 #define TIDE_H
