@@ -115,8 +115,9 @@ typedef enum {
  *   flags       TIDE_FLAG_* bits.
  *   wave_chunks at most this many chunks per wave in one kernel launch; an
  *               operation with more chunks than waves * wave_chunks is run as
- *               several launches, back to back on the stream (waves of one
- *               long launch drift apart and spread their memory traffic).
+ *               several launches of about equal length, back to back on the
+ *               stream (waves of one long launch drift apart and spread their
+ *               memory traffic).
  *               At most 2^30 (one launch for any plan); default 64.
  */
 typedef struct {

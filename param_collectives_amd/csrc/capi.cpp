@@ -303,9 +303,13 @@ tide_status run_op(tide_plan* p, tide::Op op, const std::vector<const void*>& ke
   a.alpha = alpha;
   a.accumulate = accumulate;
   // At most wave_chunks chunks per wave per launch: longer work runs as
-  // several launches of consecutive chunk ranges.
+  // several launches of consecutive chunk ranges.  A round is one chunk for
+  // every wave; the launches get equal numbers of whole rounds (a short last
+  // launch would be all ramp-up and tail, a partial round leaves waves idle).
   const int64_t waves = grid * tide::kWavesPerGroup;
-  const int64_t per_launch = std::max<int64_t>(1, std::min<int64_t>(int64_t(eff.wave_chunks) * waves, nchunks));
+  const int64_t rounds = (int64_t(nchunks) + waves - 1) / waves;
+  const int64_t launches = (rounds + eff.wave_chunks - 1) / eff.wave_chunks;
+  const int64_t per_launch = (rounds + launches - 1) / launches * waves;
   for (int64_t c0 = 0; c0 < nchunks; c0 += per_launch) {
     const int64_t c1 = std::min<int64_t>(nchunks, c0 + per_launch);
     const auto it = std::upper_bound(s.chunk_begin.begin(), s.chunk_begin.end(), int32_t(c0));
