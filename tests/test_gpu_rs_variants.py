@@ -322,16 +322,18 @@ def test_full_size_alpha_accumulate_and_fp32(tide, oracle_mod):
 # ------------------------------------------------------------ split launches
 
 
+@pytest.mark.parametrize("wave_chunks", [1, 3])
 @pytest.mark.parametrize("world", [3, 8, 16])
-def test_many_launches_per_call(tide, oracle_mod, world):
+def test_many_launches_per_call(tide, oracle_mod, world, wave_chunks):
     """Operations split into many launches (a few chunks per wave per launch,
     small grids) give the oracle's results for every operation and both
-    gradient types; launch boundaries fall inside segments and between them."""
+    gradient types; launch boundaries fall inside segments and between them,
+    and with three rounds per launch the last launch is shorter."""
     import torch
 
     rng = np.random.default_rng(400 + world)
     shapes = random_shapes(rng, world, 5) + [(world * 40 + 3, 64), (7,)]
-    opts = dict(cu_budget=3, wg_per_cu=1, chunk_elems=64, wave_chunks=1)
+    opts = dict(cu_budget=3, wg_per_cu=1, chunk_elems=64, wave_chunks=wave_chunks)
     plan = tide.Plan(world, shapes, **opts)
     grads = [[oracle_pins.rand_bf16(rng, s) for s in shapes] for _ in range(world)]
     init = init_shards(rng, world, plan.shard_elems)
