@@ -25,12 +25,12 @@ constexpr int32_t kMaxStagedSegs = 16383;  // chunk-index table entries staged i
 // one workgroup (four waves) per CU keeps the HBM read/write mix most
 // efficient for every kernel; the reduce-scatter prefers small chunks (the
 // grid then sweeps a narrow window of every tensor), the copies larger ones.
-// With fp32 gradients the reduce-scatter reads twice the bytes per element,
-// and the best chunk is half as long (16 KiB of source reads either way).
+// With fp32 gradients the reduce-scatter reads twice the bytes per element
+// and takes one group per lane per step; its best chunk is a quarter as long.
 constexpr int32_t kRsWgPerCu = 1;
 constexpr int64_t kRsChunk = 1024;
 constexpr int32_t kRsF32WgPerCu = 1;
-constexpr int64_t kRsF32Chunk = 512;
+constexpr int64_t kRsF32Chunk = 256;
 constexpr int32_t kCoWgPerCu = 1;
 constexpr int64_t kCoChunk = 4096;
 constexpr int32_t kCiWgPerCu = 1;

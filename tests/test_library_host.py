@@ -342,7 +342,7 @@ def test_options_round_trip_and_validation(tide):
     assert plan.options(1) == {"cu_budget": 0, "wg_per_cu": 1, "chunk_elems": 4096, "flags": 0, "wave_chunks": 64}
     assert plan.options(2) == {"cu_budget": 0, "wg_per_cu": 1, "chunk_elems": 4096, "flags": 0, "wave_chunks": 64}
     assert plan.options(3) == {"cu_budget": 0, "wg_per_cu": 1, "chunk_elems": 2048, "flags": 0, "wave_chunks": 64}
-    assert plan.options(4) == {"cu_budget": 0, "wg_per_cu": 1, "chunk_elems": 512, "flags": 0, "wave_chunks": 64}
+    assert plan.options(4) == {"cu_budget": 0, "wg_per_cu": 1, "chunk_elems": 256, "flags": 0, "wave_chunks": 64}
     assert np.array_equal(plan.segments(4), plan.segments(0))
     for bad in (-1, 5):
         with pytest.raises(tide.TideError) as e:
