@@ -295,7 +295,6 @@ tide_status run_op(tide_plan* p, tide::Op op, const std::vector<const void*>& ke
   a.ptrs = reinterpret_cast<const void* const*>(static_cast<unsigned char*>(s.d_call) +
                                                 s.segs.size() * sizeof(tide::CallHdr));
   a.chunk_begin = s.d_chunk_begin;
-  a.nseg = int32_t(s.segs.size());
   a.nsrc = nsrc_of(p, op);
   a.nchunks = nchunks;
   a.chunk = int32_t(eff.chunk_elems);
@@ -312,8 +311,11 @@ tide_status run_op(tide_plan* p, tide::Op op, const std::vector<const void*>& ke
   const int64_t per_launch = (rounds + launches - 1) / launches * waves;
   for (int64_t c0 = 0; c0 < nchunks; c0 += per_launch) {
     const int64_t c1 = std::min<int64_t>(nchunks, c0 + per_launch);
+    // segment of chunk c0, and one past the segment of chunk c1 - 1
     const auto it = std::upper_bound(s.chunk_begin.begin(), s.chunk_begin.end(), int32_t(c0));
-    a.span = tide::ChunkSpan{int32_t(c0), int32_t(c1), int32_t(it - s.chunk_begin.begin()) - 1};
+    const auto it_end = std::upper_bound(it, s.chunk_begin.end(), int32_t(c1 - 1));
+    a.span = tide::ChunkSpan{int32_t(c0), int32_t(c1), int32_t(it - s.chunk_begin.begin()) - 1,
+                             int32_t(it_end - s.chunk_begin.begin())};
     const int64_t g = std::min<int64_t>(grid, (c1 - c0 + tide::kWavesPerGroup - 1) / tide::kWavesPerGroup);
     int rc = 0;
     const char* what = "";

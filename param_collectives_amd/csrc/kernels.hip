@@ -107,18 +107,23 @@ constexpr int kCastUnroll = 8;
 // Chunk dealing and segment lookup (shared by every kernel)
 // ---------------------------------------------------------------------------
 
-// The chunk -> segment search table: first-chunk indices of all segments,
-// staged in LDS when it fits (it is read by every chunk of every wave).
+// The chunk -> segment search table, as far as one launch needs it: the
+// first-chunk indices of segments span.seg .. span.seg_end (the last entry
+// bounds the launch's last segment), indexed relative to span.seg and staged
+// in LDS when it fits (it is read by every chunk of every wave).  Staging only
+// the launch's slice keeps the start of every launch short on plans of many
+// tensors.
 extern __shared__ int32_t s_chunk_begin[];
 
 template <bool STAGED>
-__device__ __forceinline__ const int32_t* chunk_table(const int32_t* __restrict__ chunk_begin, int32_t nseg) {
+__device__ __forceinline__ const int32_t* chunk_table(const int32_t* __restrict__ chunk_begin, const ChunkSpan& sp) {
   if constexpr (STAGED) {
-    for (int i = threadIdx.x; i <= nseg; i += tide::kThreads) s_chunk_begin[i] = chunk_begin[i];
+    const int32_t n = sp.seg_end - sp.seg;
+    for (int i = threadIdx.x; i <= n; i += tide::kThreads) s_chunk_begin[i] = chunk_begin[sp.seg + i];
     __syncthreads();
     return s_chunk_begin;
   } else {
-    return chunk_begin;
+    return chunk_begin + sp.seg;
   }
 }
 
@@ -127,16 +132,17 @@ __device__ __forceinline__ const int32_t* chunk_table(const int32_t* __restrict_
 struct Tables {
   const CallHdr* __restrict__ hdr;
   const void* const* __restrict__ ptrs;
-  int32_t nseg, nsrc, chunk;
-  ChunkSpan span;  // the chunks of this launch
+  int32_t nsrc, chunk;
+  ChunkSpan span;  // the chunks and segments of this launch
 };
 
 // Advance `cur` (wave-uniform, non-decreasing) to the segment holding chunk
-// c: the largest s with chunk_begin[s] <= c.  64 candidates per step.
+// c: the largest s with cb[s] <= c, where cb[nseg] > c.  64 candidates per
+// step.
 __device__ __forceinline__ int32_t seek(const int32_t* cb, int32_t nseg, int32_t cur, int32_t c) {
   while (true) {
     const int32_t idx = cur + 1 + lane_id();
-    const int32_t v = idx <= nseg ? cb[idx] : INT_MAX;  // cb[nseg] = nchunks > c
+    const int32_t v = idx <= nseg ? cb[idx] : INT_MAX;
     const int32_t k = __popcll(__ballot(v <= c));
     cur += k;
     if (k < 64) return sgpr(cur);
@@ -193,12 +199,12 @@ struct Desc {
 
 template <int NS>
 __device__ __forceinline__ void fetch(const Tables& a, const int32_t* cb, int32_t* cur, int32_t c, Desc<NS>* d) {
-  *cur = seek(cb, a.nseg, *cur, c);
-  const int32_t s = *cur;
-  const int32_t first = sgpr(cb[s]);
+  *cur = seek(cb, a.span.seg_end - a.span.seg, *cur, c);  // relative to span.seg
+  const int32_t s = a.span.seg + *cur;
+  const int32_t first = sgpr(cb[*cur]);
   d->seg = s;
   d->j = c - first;
-  d->nch = sgpr(cb[s + 1]) - first;
+  d->nch = sgpr(cb[*cur + 1]) - first;
   d->h = a.hdr[s];
   const void* const* row = a.ptrs + int64_t(s) * (a.nsrc + 1);
 #pragma unroll
@@ -211,11 +217,11 @@ __device__ __forceinline__ void fetch(const Tables& a, const int32_t* cb, int32_
 // overlap the vector loads of the current chunk) and hand the chunk to `body`.
 template <int NS, bool STAGED, typename Body>
 __device__ __forceinline__ void for_each_chunk(const Tables& a, const int32_t* __restrict__ chunk_begin, Body body) {
-  const int32_t* cb = chunk_table<STAGED>(chunk_begin, a.nseg);
+  const int32_t* cb = chunk_table<STAGED>(chunk_begin, a.span);
   int32_t w, nw;
   wave_slot(&w, &nw);
   const int32_t end = a.span.end;
-  int32_t cur = a.span.seg;
+  int32_t cur = 0;
   int32_t c = a.span.first + w;
   Desc<NS> next;
   if (c < end) fetch<NS>(a, cb, &cur, c, &next);
@@ -451,9 +457,9 @@ template <int WT, bool F32, bool CL, bool CS, bool STAGED>
 __global__ __launch_bounds__(tide::kThreads) void rs_local_kernel(const CallHdr* __restrict__ hdr,
                                                                   const void* const* __restrict__ ptrs,
                                                                   const int32_t* __restrict__ chunk_begin,
-                                                                  int32_t nseg, int32_t nsrc, ChunkSpan span,
+                                                                  int32_t nsrc, ChunkSpan span,
                                                                   int32_t chunk, float alpha, int32_t accumulate) {
-  const Tables a{hdr, ptrs, nseg, nsrc, chunk, span};
+  const Tables a{hdr, ptrs, nsrc, chunk, span};
   const int epi = accumulate != 0 ? kScaleAcc : !(alpha == 1.0f) ? kScale : kPlain;
   const int32_t W = WT > 0 ? WT : nsrc;
   for_each_chunk<WT, STAGED>(a, chunk_begin, [&](const Desc<WT>& d) {
@@ -505,8 +511,8 @@ template <bool CL, bool CS, bool STAGED>
 __global__ __launch_bounds__(tide::kThreads) void ag_copyout_kernel(const CallHdr* __restrict__ hdr,
                                                                     const void* const* __restrict__ ptrs,
                                                                     const int32_t* __restrict__ chunk_begin,
-                                                                    int32_t nseg, ChunkSpan span, int32_t chunk) {
-  const Tables a{hdr, ptrs, nseg, 1, chunk, span};
+                                                                    ChunkSpan span, int32_t chunk) {
+  const Tables a{hdr, ptrs, 1, chunk, span};
   for_each_chunk<1, STAGED>(a, chunk_begin, [&](const Desc<1>& d) {
     copy_chunk<CL, CS>(static_cast<const uint16_t*>(d.src[0]), static_cast<uint16_t*>(d.dst),
                        chunk_range(d.h, d.j, d.nch, a.chunk, 8));
@@ -558,8 +564,8 @@ template <bool F32, bool CL, bool CS, bool STAGED>
 __global__ __launch_bounds__(tide::kThreads) void ag_copyin_kernel(const CallHdr* __restrict__ hdr,
                                                                    const void* const* __restrict__ ptrs,
                                                                    const int32_t* __restrict__ chunk_begin,
-                                                                   int32_t nseg, ChunkSpan span, int32_t chunk) {
-  const Tables a{hdr, ptrs, nseg, 1, chunk, span};
+                                                                   ChunkSpan span, int32_t chunk) {
+  const Tables a{hdr, ptrs, 1, chunk, span};
   for_each_chunk<1, STAGED>(a, chunk_begin, [&](const Desc<1>& d) {
     uint16_t* dst = static_cast<uint16_t*>(d.dst);
     const int lane = lane_id();
@@ -609,8 +615,8 @@ template <bool CL, bool CS, bool STAGED>
 __global__ __launch_bounds__(tide::kThreads) void stock_pack_kernel(const CallHdr* __restrict__ hdr,
                                                                     const void* const* __restrict__ ptrs,
                                                                     const int32_t* __restrict__ chunk_begin,
-                                                                    int32_t nseg, ChunkSpan span, int32_t chunk) {
-  const Tables a{hdr, ptrs, nseg, 1, chunk, span};
+                                                                    ChunkSpan span, int32_t chunk) {
+  const Tables a{hdr, ptrs, 1, chunk, span};
   for_each_chunk<1, STAGED>(a, chunk_begin, [&](const Desc<1>& d) {
     float* dst = static_cast<float*>(d.dst);
     const Chunk r = chunk_range(d.h, d.j, d.nch, a.chunk, 4);
@@ -643,8 +649,9 @@ __global__ __launch_bounds__(tide::kThreads) void stock_pack_kernel(const CallHd
 // LDS for the staged chunk table; large tables, and calls with
 // TIDE_FLAG_NO_LDS, keep it in global memory.
 size_t staged_bytes(const KernelArgs& a, bool* staged) {
-  *staged = a.nseg <= tide::kMaxStagedSegs && !(a.flags & TIDE_FLAG_NO_LDS);
-  return *staged ? size_t(a.nseg + 1) * sizeof(int32_t) : 0;
+  const int32_t n = a.span.seg_end - a.span.seg;  // entries n + 1
+  *staged = n <= tide::kMaxStagedSegs && !(a.flags & TIDE_FLAG_NO_LDS);
+  return *staged ? size_t(n + 1) * sizeof(int32_t) : 0;
 }
 
 // Calls f(CL, CS, STAGED, lds_bytes) with the kernel instance's flags as
@@ -678,7 +685,7 @@ template <int WT, bool F32>
 int launch_rs_w(const KernelArgs& a, int64_t grid, hipStream_t s) {
   by_instance(a, [&](auto CL, auto CS, auto ST, size_t lds) {
     hipLaunchKernelGGL((rs_local_kernel<WT, F32, TIDE_V(CL), TIDE_V(CS), TIDE_V(ST)>), dim3(unsigned(grid)),
-                       dim3(unsigned(tide::kThreads)), lds, s, a.hdr, a.ptrs, a.chunk_begin, a.nseg, a.nsrc,
+                       dim3(unsigned(tide::kThreads)), lds, s, a.hdr, a.ptrs, a.chunk_begin, a.nsrc,
                        a.span, a.chunk, a.alpha, a.accumulate);
   });
   return int(hipGetLastError());
@@ -706,7 +713,7 @@ int launch_ag_copyout(const KernelArgs& a, int64_t grid, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   by_instance(a, [&](auto CL, auto CS, auto ST, size_t lds) {
     hipLaunchKernelGGL((ag_copyout_kernel<TIDE_V(CL), TIDE_V(CS), TIDE_V(ST)>), dim3(unsigned(grid)),
-                       dim3(unsigned(kThreads)), lds, s, a.hdr, a.ptrs, a.chunk_begin, a.nseg, a.span, a.chunk);
+                       dim3(unsigned(kThreads)), lds, s, a.hdr, a.ptrs, a.chunk_begin, a.span, a.chunk);
   });
   return int(hipGetLastError());
 }
@@ -716,10 +723,10 @@ int launch_ag_copyin(const KernelArgs& a, bool f32, int64_t grid, void* stream) 
   by_instance(a, [&](auto CL, auto CS, auto ST, size_t lds) {
     if (f32) {
       hipLaunchKernelGGL((ag_copyin_kernel<true, TIDE_V(CL), TIDE_V(CS), TIDE_V(ST)>), dim3(unsigned(grid)),
-                         dim3(unsigned(kThreads)), lds, s, a.hdr, a.ptrs, a.chunk_begin, a.nseg, a.span, a.chunk);
+                         dim3(unsigned(kThreads)), lds, s, a.hdr, a.ptrs, a.chunk_begin, a.span, a.chunk);
     } else {
       hipLaunchKernelGGL((ag_copyin_kernel<false, TIDE_V(CL), TIDE_V(CS), TIDE_V(ST)>), dim3(unsigned(grid)),
-                         dim3(unsigned(kThreads)), lds, s, a.hdr, a.ptrs, a.chunk_begin, a.nseg, a.span, a.chunk);
+                         dim3(unsigned(kThreads)), lds, s, a.hdr, a.ptrs, a.chunk_begin, a.span, a.chunk);
     }
   });
   return int(hipGetLastError());
@@ -729,7 +736,7 @@ int launch_stock_pack(const KernelArgs& a, int64_t grid, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   by_instance(a, [&](auto CL, auto CS, auto ST, size_t lds) {
     hipLaunchKernelGGL((stock_pack_kernel<TIDE_V(CL), TIDE_V(CS), TIDE_V(ST)>), dim3(unsigned(grid)),
-                       dim3(unsigned(kThreads)), lds, s, a.hdr, a.ptrs, a.chunk_begin, a.nseg, a.span, a.chunk);
+                       dim3(unsigned(kThreads)), lds, s, a.hdr, a.ptrs, a.chunk_begin, a.span, a.chunk);
   });
   return int(hipGetLastError());
 }

@@ -134,21 +134,20 @@ void ci_call_table(const Geometry& g, const std::vector<Seg>& segs, const void* 
 void pk_call_table(const Geometry& g, const std::vector<Seg>& segs, const uint16_t* const* grads, float* packed,
                    std::vector<CallHdr>* hdr, std::vector<const void*>* ptrs);
 
-// The chunks one launch covers, [first, end), and the segment holding chunk
-// `first`.  Long work is split into several launches: within one persistent
-// launch the waves drift apart over time, widening the window of HBM they
-// touch at once (measured on MI355X: one 17 GB reduce-scatter launch 5.85
-// TB/s, the same work in four launches 6.28 TB/s).
+// The chunks one launch covers, [first, end), and the segments they fall in,
+// [seg, seg_end).  Long work is split into several launches: within one
+// persistent launch the waves drift apart over time, widening the window of
+// HBM they touch at once (measured on MI355X: one 17 GB reduce-scatter launch
+// 5.85 TB/s, the same work in four launches 6.28 TB/s).
 struct ChunkSpan {
-  int32_t first, end, seg;
+  int32_t first, end, seg, seg_end;
 };
 
 // Device-side launch arguments (kernels.hip).
 struct KernelArgs {
   const CallHdr* hdr;       // [nseg]
   const void* const* ptrs;  // [nseg * (nsrc + 1)]
-  const int32_t* chunk_begin;  // [nseg + 1]
-  int32_t nseg;
+  const int32_t* chunk_begin;  // [nseg + 1], nseg the operation's segment count
   int32_t nsrc;  // W (reduce-scatter) or 1 (the copies)
   int32_t nchunks;  // of the whole operation
   ChunkSpan span;   // of this launch
