@@ -96,7 +96,8 @@ __device__ __forceinline__ int64_t min64(int64_t a, int64_t b) { return a < b ? 
 __device__ __forceinline__ int lane_id() { return int(threadIdx.x & 63); }
 
 // Groups each lane has in flight per step (measured on MI355X: two groups of
-// W loads for the reduce-scatter, four 16-byte loads for the bf16 copies,
+// W loads for the reduce-scatter of bf16 gradients, one of fp32 gradients,
+// whose groups are twice as long; four 16-byte loads for the bf16 copies,
 // eight for the casting and widening copies, whose groups are half as long on
 // one side).
 constexpr int kRsUnroll = 2;

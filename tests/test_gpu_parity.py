@@ -262,6 +262,25 @@ def test_repeat_calls_and_pointer_table_changes(tide, oracle_mod):
                 gpu_util.assert_same_f32(outs[r].cpu().numpy(), want[r], f"trial {trial} rank {r}")
 
 
+def test_launch_table_slice_staged_or_not(tide, oracle_mod):
+    """Each launch stages its own slice of the chunk-to-segment table in LDS
+    when it fits.  Here the first copy-out launch covers 16,384 one-element
+    segments, one more than fits, so it reads its slice from global memory,
+    and the second covers the 8 segments of one large parameter (staged)."""
+    W = 8
+    shapes = [(8,)] * 2048 + [(8, 8 * 1024 * 1024)]
+    # 1024 waves, 32 rounds of 4096-element chunks, 16 rounds per launch
+    plan = tide.Plan(W, shapes, cu_budget=256, wg_per_cu=1, wave_chunks=16)
+    assert len(plan.segments(1)) == 2048 * W + W
+    assert plan.options(1)["chunk_elems"] == 4096
+    rng = np.random.default_rng(88)
+    rm_bits = rng.integers(0, 0x10000, size=W * plan.shard_elems, dtype=np.uint16)
+    got = run_copyout(tide, plan, rm_bits)
+    want = oracle_mod.copyout(W, shapes, rm_bits)
+    for p in range(len(shapes)):
+        assert np.array_equal(got[p], want[p]), p
+
+
 def test_empty_work_is_a_no_op(tide):
     import torch
 
