@@ -107,14 +107,9 @@ def cpu_model():
 
 
 def launches_per_call(plan, op):
-    """Kernel launches one call of operation `op` makes: its chunks are split
-    into launches of at most wave_chunks chunks per wave."""
-    o = plan.options(op)
-    segs = plan.segments(op)
-    nchunks = int(sum(-(-int(n) // o["chunk_elems"]) for n in segs[:, 5]))
-    grid = min(o["cu_budget"] * o["wg_per_cu"], -(-nchunks // 4))
-    per = max(1, min(o["wave_chunks"] * grid * 4, nchunks))
-    return -(-nchunks // per)
+    """Kernel launches one call of operation `op` makes (the library's own
+    split: at most wave_chunks chunks per wave per launch)."""
+    return len(plan.launches(op))
 
 
 def main(argv=None):

@@ -183,6 +183,21 @@ tide_status tide_plan_layout(const tide_plan* plan, int64_t* rows_per_rank, int6
 tide_status tide_plan_segments(const tide_plan* plan, int32_t op, int64_t* table, int64_t capacity,
                                int64_t* count);
 
+/*
+ * How one call of `op` is split into kernel launches under the plan's current
+ * options, for inspection and tests (host only).  A launch covers chunks
+ * [first, end) of the operation, which fall in its segments [seg, seg_end)
+ * (indices into tide_plan_segments' table), with `workgroups` workgroups.
+ * Each launch is 5 int64 values: first, end, seg, seg_end, workgroups.
+ *   cu_count  the CU count that a cu_budget of 0 stands for; 0 = that of the
+ *             device the plan is bound to (TIDE_ERR_INVALID if it is not
+ *             bound and the options set no cu_budget).
+ * Writes min(capacity, count) launches to `table` (may be NULL when capacity
+ * is 0) and the total count to *count (0 when the operation has no work).
+ */
+tide_status tide_plan_launches(const tide_plan* plan, int32_t op, int32_t cu_count, int64_t* table,
+                               int64_t capacity, int64_t* count);
+
 /* Replace the launch knobs (NULL = defaults).  Results are unaffected.
  * Errors: TIDE_ERR_INVALID, TIDE_ERR_RANGE (too many chunks). */
 tide_status tide_plan_set_options(tide_plan* plan, const tide_options* opt);

@@ -255,6 +255,45 @@ tide_status bind_device(tide_plan* p) {
   return TIDE_OK;
 }
 
+// How one call of an operation is split into kernel launches.  At most
+// wave_chunks chunks per wave per launch: longer work runs as several
+// launches of consecutive chunk ranges.  A round is one chunk for every wave;
+// the launches get equal numbers of whole rounds (a short last launch would be
+// all ramp-up and tail, a partial round leaves waves idle).
+struct Launches {
+  int64_t grid;        // workgroups of a full launch
+  int64_t per_launch;  // chunks of every launch but the last (which may have fewer)
+  int64_t nchunks;     // of the whole operation
+};
+
+Launches split_launches(const OpState& s, const tide_options& eff) {
+  Launches L;
+  L.nchunks = s.chunk_begin.back();
+  int64_t grid = int64_t(eff.cu_budget) * eff.wg_per_cu;
+  const int64_t useful = (L.nchunks + tide::kWavesPerGroup - 1) / tide::kWavesPerGroup;
+  if (grid > useful) grid = useful;
+  if (grid > tide::kMaxGrid) grid = tide::kMaxGrid;
+  if (grid < 1) grid = 1;
+  L.grid = grid;
+  const int64_t waves = grid * tide::kWavesPerGroup;
+  const int64_t rounds = (L.nchunks + waves - 1) / waves;
+  const int64_t launches = std::max<int64_t>(1, (rounds + eff.wave_chunks - 1) / eff.wave_chunks);
+  L.per_launch = std::max<int64_t>(1, (rounds + launches - 1) / launches * waves);
+  return L;
+}
+
+// The launch that starts at chunk c0: its span (chunks, and the segments they
+// fall in) and its workgroup count.
+void launch_at(const OpState& s, const Launches& L, int64_t c0, tide::ChunkSpan* span, int64_t* grid) {
+  const int64_t c1 = std::min<int64_t>(L.nchunks, c0 + L.per_launch);
+  // the segment of chunk c0, and one past the segment of chunk c1 - 1
+  const auto it = std::upper_bound(s.chunk_begin.begin(), s.chunk_begin.end(), int32_t(c0));
+  const auto it_end = std::upper_bound(it, s.chunk_begin.end(), int32_t(c1 - 1));
+  *span = tide::ChunkSpan{int32_t(c0), int32_t(c1), int32_t(it - s.chunk_begin.begin()) - 1,
+                          int32_t(it_end - s.chunk_begin.begin())};
+  *grid = std::min<int64_t>(L.grid, (c1 - c0 + tide::kWavesPerGroup - 1) / tide::kWavesPerGroup);
+}
+
 // Upload what is stale, then launch.  `f32`: the reduce-scatter's gradients
 // or the copy-in's shards are fp32.  `alpha`, `accumulate`: the
 // reduce-scatter's Equation 5 terms.
@@ -285,11 +324,7 @@ tide_status run_op(tide_plan* p, tide::Op op, const std::vector<const void*>& ke
     s.key_valid = true;
   }
   const tide_options eff = tide::effective_options(p->given, op, p->cu_count);
-  int64_t grid = int64_t(eff.cu_budget) * eff.wg_per_cu;
-  const int64_t useful = (int64_t(nchunks) + tide::kWavesPerGroup - 1) / tide::kWavesPerGroup;
-  if (grid > useful) grid = useful;
-  if (grid > tide::kMaxGrid) grid = tide::kMaxGrid;
-  if (grid < 1) grid = 1;
+  const Launches L = split_launches(s, eff);
   tide::KernelArgs a;
   a.hdr = static_cast<const tide::CallHdr*>(s.d_call);
   a.ptrs = reinterpret_cast<const void* const*>(static_cast<unsigned char*>(s.d_call) +
@@ -301,22 +336,9 @@ tide_status run_op(tide_plan* p, tide::Op op, const std::vector<const void*>& ke
   a.flags = eff.flags;
   a.alpha = alpha;
   a.accumulate = accumulate;
-  // At most wave_chunks chunks per wave per launch: longer work runs as
-  // several launches of consecutive chunk ranges.  A round is one chunk for
-  // every wave; the launches get equal numbers of whole rounds (a short last
-  // launch would be all ramp-up and tail, a partial round leaves waves idle).
-  const int64_t waves = grid * tide::kWavesPerGroup;
-  const int64_t rounds = (int64_t(nchunks) + waves - 1) / waves;
-  const int64_t launches = (rounds + eff.wave_chunks - 1) / eff.wave_chunks;
-  const int64_t per_launch = (rounds + launches - 1) / launches * waves;
-  for (int64_t c0 = 0; c0 < nchunks; c0 += per_launch) {
-    const int64_t c1 = std::min<int64_t>(nchunks, c0 + per_launch);
-    // segment of chunk c0, and one past the segment of chunk c1 - 1
-    const auto it = std::upper_bound(s.chunk_begin.begin(), s.chunk_begin.end(), int32_t(c0));
-    const auto it_end = std::upper_bound(it, s.chunk_begin.end(), int32_t(c1 - 1));
-    a.span = tide::ChunkSpan{int32_t(c0), int32_t(c1), int32_t(it - s.chunk_begin.begin()) - 1,
-                             int32_t(it_end - s.chunk_begin.begin())};
-    const int64_t g = std::min<int64_t>(grid, (c1 - c0 + tide::kWavesPerGroup - 1) / tide::kWavesPerGroup);
+  for (int64_t c0 = 0; c0 < nchunks; c0 += L.per_launch) {
+    int64_t g = 0;
+    launch_at(s, L, c0, &a.span, &g);
     int rc = 0;
     const char* what = "";
     switch (op) {
@@ -454,6 +476,41 @@ tide_status tide_plan_segments(const tide_plan* plan, int32_t op, int64_t* table
       row[4] = s.dst_off;
       row[5] = s.len;
     }
+    return TIDE_OK;
+  });
+}
+
+tide_status tide_plan_launches(const tide_plan* plan, int32_t op, int32_t cu_count, int64_t* table,
+                               int64_t capacity, int64_t* count) {
+  return tide::guarded([&]() -> tide_status {
+    g_last_error.clear();
+    if (!live(plan)) return fail(TIDE_ERR_INVALID, "unknown or destroyed plan");
+    if (op < 0 || op >= tide::kNumOps) return fail(TIDE_ERR_INVALID, std::string("op must be ") + kOpNames);
+    if (count == nullptr || capacity < 0 || (capacity > 0 && table == nullptr))
+      return fail(TIDE_ERR_INVALID, "bad table/capacity/count");
+    if (cu_count < 0) return fail(TIDE_ERR_INVALID, "cu_count must be >= 0");
+    const tide_options eff =
+        tide::effective_options(plan->given, tide::Op(op), cu_count > 0 ? cu_count : plan->cu_count);
+    if (eff.cu_budget <= 0)
+      return fail(TIDE_ERR_INVALID, "the plan is not bound to a device and has no cu_budget: pass cu_count");
+    const OpState& s = op_state(plan, tide::Op(op));
+    *count = 0;
+    if (s.chunk_begin.back() == 0) return TIDE_OK;
+    const Launches L = split_launches(s, eff);
+    int64_t n = 0;
+    for (int64_t c0 = 0; c0 < L.nchunks; c0 += L.per_launch, ++n) {
+      if (n >= capacity) continue;
+      tide::ChunkSpan sp;
+      int64_t g = 0;
+      launch_at(s, L, c0, &sp, &g);
+      int64_t* row = table + 5 * n;
+      row[0] = sp.first;
+      row[1] = sp.end;
+      row[2] = sp.seg;
+      row[3] = sp.seg_end;
+      row[4] = g;
+    }
+    *count = n;
     return TIDE_OK;
   });
 }

@@ -45,6 +45,7 @@ EXPORTS = (
     "tide_plan_segments",
     "tide_plan_set_options",
     "tide_plan_get_options",
+    "tide_plan_launches",
     "tide_reduce_scatter_local",
     "tide_allgather_copyout",
     "tide_allgather_copyin",
@@ -83,6 +84,7 @@ def _load():
     lib.tide_plan_segments.argtypes = [vp, i32, i64p, i64, i64p]
     lib.tide_plan_set_options.argtypes = [vp, ctypes.POINTER(Options)]
     lib.tide_plan_get_options.argtypes = [vp, i32, ctypes.POINTER(Options)]
+    lib.tide_plan_launches.argtypes = [vp, i32, i32, i64p, i64, i64p]
     lib.tide_reduce_scatter_local.argtypes = [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.c_float, i32, vp]
     lib.tide_allgather_copyout.argtypes = [vp, vp, ctypes.POINTER(vp), vp]
     lib.tide_allgather_copyin.argtypes = [vp, ctypes.POINTER(vp), i32, vp, vp]
@@ -155,6 +157,19 @@ class Plan:
         table = np.zeros((max(count.value, 1), 6), dtype=np.int64)
         _check(lib.tide_plan_segments(self.handle, int(op), table.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
                                       count.value, ctypes.byref(count)))
+        return table[:count.value]
+
+    def launches(self, op=0, cu_count=0):
+        """The kernel launches one call of `op` makes under the current
+        options, as an int64 array of rows (first chunk, end chunk, first
+        segment, end segment, workgroups); cu_count stands for a cu_budget of
+        0 (0: the bound device's CU count)."""
+        count = ctypes.c_int64()
+        _check(lib.tide_plan_launches(self.handle, int(op), int(cu_count), None, 0, ctypes.byref(count)))
+        table = np.zeros((max(count.value, 1), 5), dtype=np.int64)
+        _check(lib.tide_plan_launches(self.handle, int(op), int(cu_count),
+                                      table.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), count.value,
+                                      ctypes.byref(count)))
         return table[:count.value]
 
     def set_options(self, cu_budget=0, wg_per_cu=0, chunk_elems=0, flags=0, wave_chunks=0):

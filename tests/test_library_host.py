@@ -9,6 +9,8 @@ import subprocess
 import numpy as np
 import pytest
 
+import synth
+
 from tests import oracle_pins
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -351,6 +353,67 @@ def test_options_round_trip_and_validation(tide):
         with pytest.raises(tide.TideError) as e:
             plan.segments(bad)
         assert _status(e) == -1
+
+
+def _check_launches(plan, op, L, waves, wave_chunks):
+    """The launch table of one operation against its definition: consecutive
+    chunk ranges covering every chunk, equal whole rounds per launch but the
+    last, at most wave_chunks rounds each, and the segment range of each
+    launch found from the chunk table of the plan's segments."""
+    segs = plan.segments(op)
+    chunk = plan.options(op)["chunk_elems"]
+    cb = np.concatenate([[0], np.cumsum(-(-segs[:, 5] // chunk))])
+    nchunks = int(cb[-1])
+    assert L[0, 0] == 0 and L[-1, 1] == nchunks
+    assert np.array_equal(L[1:, 0], L[:-1, 1])
+    lens = L[:, 1] - L[:, 0]
+    assert np.all(lens[:-1] == lens[0]) and lens[-1] <= lens[0] and lens[-1] > 0
+    assert lens[0] % waves == 0 or len(L) == 1
+    assert np.all(lens <= wave_chunks * waves)
+    rounds = -(-nchunks // waves)
+    assert len(L) == -(-rounds // wave_chunks)
+    for first, end, seg, seg_end, g in L:
+        assert cb[seg] <= first < cb[seg + 1]
+        assert cb[seg_end - 1] <= end - 1 < cb[seg_end]
+        assert g == min(waves // 4, -(-(end - first) // 4))
+
+
+def test_launch_split(tide):
+    w = synth.workload("llama3.1-8b-layer")
+    plan = tide.Plan(w.world, w.shapes)
+    L = plan.launches(0, cu_count=256)
+    _check_launches(plan, 0, L, 1024, 64)
+    # 213,008 chunks are 209 rounds of 1024 waves: four launches of 53 rounds, the last shorter
+    assert len(L) == 4
+    assert list(L[:, 1] - L[:, 0]) == [53 * 1024] * 3 + [213008 - 3 * 53 * 1024]
+    for op in range(5):
+        _check_launches(plan, op, plan.launches(op, cu_count=256), 1024, 64)
+    # the Qwen3 layer's launches each touch a few hundred of its segments
+    q = synth.workload("qwen3-30b-a3b-moe-layer")
+    qplan = tide.Plan(q.world, q.shapes)
+    QL = qplan.launches(0, cu_count=256)
+    _check_launches(qplan, 0, QL, 1024, 64)
+    assert np.all(QL[:, 3] - QL[:, 2] < 400)
+    # a small grid, three rounds per launch, a short last launch
+    rng = np.random.default_rng(5)
+    shapes = [(int(rng.integers(1, 40)), int(rng.integers(1, 70))) for _ in range(30)]
+    small = tide.Plan(3, shapes, cu_budget=2, wg_per_cu=1, chunk_elems=16, wave_chunks=3)
+    for op in range(5):
+        _check_launches(small, op, small.launches(op), 8, 3)
+    assert len(small.launches(0)) > 3
+
+
+def test_launches_need_a_cu_count_until_bound(tide):
+    plan = tide.Plan(2, [(64, 64)])
+    with pytest.raises(tide.TideError) as e:
+        plan.launches(0)
+    assert _status(e) == -1
+    with pytest.raises(tide.TideError) as e:
+        plan.launches(0, cu_count=-1)
+    assert _status(e) == -1
+    assert len(plan.launches(0, cu_count=4)) == 1
+    empty = tide.Plan(2, [(0, 4)])
+    assert empty.launches(0, cu_count=4).shape == (0, 5)
 
 
 def test_too_many_chunks_is_a_range_error(tide):
