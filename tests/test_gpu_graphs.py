@@ -78,3 +78,61 @@ def test_captured_step_replays_match_the_oracle(tide, oracle_mod):
         want_co = oracle_mod.copyout(W, shapes, rm_bits)
         for p in range(len(shapes)):
             assert np.array_equal(gpu_util.bf16_bits(params[p]).reshape(shapes[p]), want_co[p]), (replay, p)
+
+
+def test_captured_copyin_and_fp32_reduce_scatter_replays(tide, oracle_mod):
+    """The copy-in of fp32 shards and the reduce-scatter of fp32 gradients,
+    captured after a warm-up call and replayed with new inputs written
+    eagerly between the replays: every replay matches the oracle."""
+    import torch
+
+    W = 4
+    shapes = [(W * 70 + 1, 96), (9,), (W * 8, 300)]
+    plan = tide.Plan(W, shapes, wave_chunks=2)
+    P = len(shapes)
+    shards = [[torch.empty(plan.n_real[r][p], dtype=torch.float32, device="cuda") for p in range(P)]
+              for r in range(W)]
+    rm = torch.empty(W * plan.shard_elems, dtype=torch.bfloat16, device="cuda")
+    grads = [[torch.empty(s, dtype=torch.float32, device="cuda") for s in shapes] for _ in range(W)]
+    outs = [torch.empty(plan.shard_elems, dtype=torch.float32, device="cuda") for _ in range(W)]
+    ci = tide.allgather_copyin_call(plan, shards, rm)
+    rs = tide.reduce_scatter_call(plan, grads, outs)
+
+    def fill(seed):
+        r = np.random.default_rng(seed)
+        X = [r.standard_normal(s).astype(np.float32) for s in shapes]
+        host_shards = oracle_pins.shards_of(W, shapes, X)
+        for a in range(W):
+            for p in range(P):
+                shards[a][p].copy_(torch.from_numpy(np.ascontiguousarray(host_shards[a][p]).reshape(-1)))
+        g = [[oracle_pins.rand_f32(r, s) for s in shapes] for _ in range(W)]
+        for u in range(W):
+            for p in range(P):
+                grads[u][p].copy_(torch.from_numpy(g[u][p]))
+        rm.view(torch.int16).fill_(-1)
+        for o in outs:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        return host_shards, g
+
+    fill(0)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        ci()
+        rs()  # warm-up: binds the plan and uploads its tables
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        ci()
+        rs()
+    for replay in range(3):
+        host_shards, g = fill(500 + replay)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(gpu_util.bf16_bits(rm), oracle_mod.copyin(W, shapes, host_shards)), replay
+        want = oracle_mod.rs_local_ex(W, shapes, g)
+        for r in range(W):
+            gpu_util.assert_same_f32(outs[r].cpu().numpy(), want[r], f"replay {replay} rank {r}")
