@@ -306,6 +306,25 @@ def main(argv=None):
     d2d = {"bytes": co_bytes, "avg_ms": round(d2d_ms, 5), "gbps": round(co_bytes / d2d_ms / 1e6, 1)}
     del src, dst
 
+    # the copy-out kernel on one flat tensor of the same byte count, same
+    # launch options: what a plain 1:1 bf16 copy reaches on this GPU, without
+    # segment boundaries (context for the copy-out's fraction of peak)
+    with torch.cuda.stream(stream):
+        fsrc = torch.empty(sum_dk, dtype=torch.bfloat16, device="cuda")
+        fdst = torch.empty_like(fsrc)
+        fplan = tide.Plan(1, [(sum_dk,)], **opts)
+        fcall = tide.allgather_copyout_call(fplan, fsrc, [fdst])
+        fcall(stream)
+        e = [(ev(), ev()) for _ in range(20)]
+        for a, b in e:
+            a.record(stream)
+            fcall(stream)
+            b.record(stream)
+    stream.synchronize()
+    flat = kstats([a.elapsed_time(b) for a, b in e], co_bytes)
+    flat["copyout_over_flat"] = round(flat["avg_ms"] / kernels["ag_copyout"]["avg_ms"], 4)
+    del fsrc, fdst, fplan, fcall
+
     def timed(fn, n=10):
         fn()
         e = [(ev(), ev()) for _ in range(n)]
@@ -452,6 +471,7 @@ def main(argv=None):
         "event_ms_per_step": round(step_ms_events, 5),
         "cu_sweep": sweep,
         "d2d_copy": d2d,
+        "flat_copy": flat,
         "parity": parity,
         "stock_ab": stock_ab,
         "host_enqueue_us": host_us,
