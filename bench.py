@@ -61,8 +61,8 @@ def parse_args(argv=None):
     ap.add_argument("--no-sweep", action="store_true", help="skip the CU-budget sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the Equation 5 epilogue and stock-path A/B sections (their reduce-scatter launches "
-                         "share the kernel name of the timed one)")
+                    help="skip the Equation 5 epilogue, stock-path A/B and flat-copy sections (their launches "
+                         "share the kernel names of the timed ones)")
     ap.add_argument("--only", choices=["rs", "co", "ci", "calib", "stock"],
                     help="launch just one kernel (stock: the W packs and the fp32 reduce-scatter of the stock "
                          "path) --launches times, for profiling, and exit")
@@ -306,24 +306,6 @@ def main(argv=None):
     d2d = {"bytes": co_bytes, "avg_ms": round(d2d_ms, 5), "gbps": round(co_bytes / d2d_ms / 1e6, 1)}
     del src, dst
 
-    # the copy-out kernel on one flat tensor of the same byte count, same
-    # launch options: what a plain 1:1 bf16 copy reaches on this GPU, without
-    # segment boundaries (context for the copy-out's fraction of peak)
-    with torch.cuda.stream(stream):
-        fsrc = torch.empty(sum_dk, dtype=torch.bfloat16, device="cuda")
-        fdst = torch.empty_like(fsrc)
-        fplan = tide.Plan(1, [(sum_dk,)], **opts)
-        fcall = tide.allgather_copyout_call(fplan, fsrc, [fdst])
-        fcall(stream)
-        e = [(ev(), ev()) for _ in range(20)]
-        for a, b in e:
-            a.record(stream)
-            fcall(stream)
-            b.record(stream)
-    stream.synchronize()
-    flat = kstats([a.elapsed_time(b) for a, b in e], co_bytes)
-    flat["copyout_over_flat"] = round(flat["avg_ms"] / kernels["ag_copyout"]["avg_ms"], 4)
-    del fsrc, fdst, fplan, fcall
 
     def timed(fn, n=10):
         fn()
@@ -386,6 +368,7 @@ def main(argv=None):
 
     stock_ab = None
     host_us = None
+    flat = None
     if not args.no_extras:
         # (rewrites the timed outputs with the same values)
         host_us = host_enqueue()
@@ -398,6 +381,24 @@ def main(argv=None):
         kernels["rs_local_alpha_accumulate"] = kstats(timed(lambda: acc_call(stream)), rs_bytes + 4 * W * S)
         del acc_outs, acc_call
         stock_ab = stock_a_b(kstats, kernels)
+        # the copy-out kernel on one flat tensor of the same byte count, same
+        # launch options: what a plain 1:1 bf16 copy reaches on this GPU, without
+        # segment boundaries (context for the copy-out's fraction of peak)
+        with torch.cuda.stream(stream):
+            fsrc = torch.empty(sum_dk, dtype=torch.bfloat16, device="cuda")
+            fdst = torch.empty_like(fsrc)
+            fplan = tide.Plan(1, [(sum_dk,)], **opts)
+            fcall = tide.allgather_copyout_call(fplan, fsrc, [fdst])
+            fcall(stream)
+            e = [(ev(), ev()) for _ in range(20)]
+            for a, b in e:
+                a.record(stream)
+                fcall(stream)
+                b.record(stream)
+        stream.synchronize()
+        flat = kstats([a.elapsed_time(b) for a, b in e], co_bytes)
+        flat["copyout_over_flat"] = round(flat["avg_ms"] / kernels["ag_copyout"]["avg_ms"], 4)
+        del fsrc, fdst, fplan, fcall
 
     # CPU oracle on the same workload, and a bitwise check of this run's outputs
     cpu = None
