@@ -57,6 +57,7 @@ def parse_args(argv=None):
     ap.add_argument("--cu-budget", type=int, default=0)
     ap.add_argument("--wg-per-cu", type=int, default=0)
     ap.add_argument("--chunk", type=int, default=0)
+    ap.add_argument("--wave-chunks", type=int, default=0, help="chunks per wave per launch (0 = default)")
     ap.add_argument("--flags", type=int, default=0)
     ap.add_argument("--no-sweep", action="store_true", help="skip the CU-budget sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
@@ -130,7 +131,8 @@ def main(argv=None):
         return 1
     torch.cuda.set_device(0)
     w = synth.workload(args.workload)
-    opts = dict(cu_budget=args.cu_budget, wg_per_cu=args.wg_per_cu, chunk_elems=args.chunk, flags=args.flags)
+    opts = dict(cu_budget=args.cu_budget, wg_per_cu=args.wg_per_cu, chunk_elems=args.chunk, flags=args.flags,
+                wave_chunks=args.wave_chunks)
     plan = tide.Plan(w.world, w.shapes, **opts)
     W, S = w.world, plan.shard_elems
     sum_dk = sum(w.numel(p) for p in range(w.nparams))
