@@ -18,7 +18,8 @@ time, with
     the current kernel source is committed under profiles/;
   * a CU-budget sweep, each kernel on a stream masked to the budget's CUs
     (GB/s per CU is the analog of the pages' per-CTA sum rate);
-  * a plain device-to-device copy of the copy-out's byte count, for context;
+  * a plain device-to-device copy of the copy-out's byte count, and the
+    copy-out kernel on one flat tensor of the same bytes, for context;
   * Equation 5's epilogue (alpha = 1/W, accumulate into the shards) and the
     reduce-scatter from fp32 gradients, per kernel;
   * the stock path A/B: W stock gradient packs (slice, zero-pad, widen, pack
