@@ -31,6 +31,7 @@ Algorithmic bytes: reduce-scatter 2*W*sum(D*K) read + 4*W*S written (padding
 is written, never read); copy-out 2*sum(D*K) read + 2*sum(D*K) written.
 """
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -55,6 +56,8 @@ def parse_args(argv=None):
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--world", type=int, default=0,
+                    help="simulated ranks W, overriding the workload's (same shapes; 0 = the workload's own)")
     ap.add_argument("--cu-budget", type=int, default=0)
     ap.add_argument("--wg-per-cu", type=int, default=0)
     ap.add_argument("--chunk", type=int, default=0)
@@ -132,6 +135,9 @@ def main(argv=None):
         return 1
     torch.cuda.set_device(0)
     w = synth.workload(args.workload)
+    own_world = args.world in (0, w.world)  # the committed counters are for the workload's own W
+    if args.world:
+        w = dataclasses.replace(w, world=args.world)
     opts = dict(cu_budget=args.cu_budget, wg_per_cu=args.wg_per_cu, chunk_elems=args.chunk, flags=args.flags,
                 wave_chunks=args.wave_chunks)
     plan = tide.Plan(w.world, w.shapes, **opts)
@@ -469,7 +475,7 @@ def main(argv=None):
         "roofline": {"bound": "hbm", "kernel": "rs_local_kernel", "unit_of_work": "one reduce-scatter call",
                      "launches_per_call": launches_per_call(plan, 0), "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic_for(f"rs_local/{w.name}")},
+                     "traffic": traffic_for(f"rs_local/{w.name}") if own_world else None},
         "cpu_baseline": cpu,
         "kernels": kernels,
         "event_ms_per_step": round(step_ms_events, 5),

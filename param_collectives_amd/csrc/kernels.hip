@@ -343,6 +343,89 @@ __device__ __forceinline__ float sum_one(const void* const* src, int32_t W, int6
   return acc;
 }
 
+// One batch of NB consecutive ranks u0 .. u0+NB-1 for U groups of 4 elements
+// per lane, the first at group index g0 of the chunk body starting at vlo:
+// all NB*U loads first, then the additions in rank order into acc; FIRST
+// starts the sums with rank u0's value.  Loads address a scalar base plus a
+// 32-bit lane offset, as in the templated paths.
+template <bool F32, bool CL, int U, int NB, bool FIRST>
+__device__ __forceinline__ void rs_batch(const void* const* src, int32_t u0, int64_t vlo, int64_t g0,
+                                         float (&acc)[U][4]) {
+  using S = Src<F32>;
+  using T = typename S::T;
+  using V = typename S::V;
+  constexpr int kGroupBytes = 4 * int(sizeof(T));
+  const char* s[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) s[j] = reinterpret_cast<const char*>(static_cast<const T*>(src[u0 + j]) + vlo);
+  V v[U][NB];
+#pragma unroll
+  for (int k = 0; k < U; ++k) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) v[k][j] = load<V, CL>(s[j] + uint32_t((g0 + 64 * k) * kGroupBytes));
+  }
+#pragma unroll
+  for (int k = 0; k < U; ++k) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      if (FIRST && j == 0) {
+        S::first(v[k][0], acc[k]);
+      } else {
+        S::add(v[k][j], acc[k]);
+      }
+    }
+  }
+}
+
+// A batch of nb (1..8, wave-uniform) ranks.
+template <bool F32, bool CL, int U, bool FIRST>
+__device__ __forceinline__ void rs_batch_n(int32_t nb, const void* const* src, int32_t u0, int64_t vlo, int64_t g0,
+                                           float (&acc)[U][4]) {
+  switch (nb) {
+    case 1: rs_batch<F32, CL, U, 1, FIRST>(src, u0, vlo, g0, acc); break;
+    case 2: rs_batch<F32, CL, U, 2, FIRST>(src, u0, vlo, g0, acc); break;
+    case 3: rs_batch<F32, CL, U, 3, FIRST>(src, u0, vlo, g0, acc); break;
+    case 4: rs_batch<F32, CL, U, 4, FIRST>(src, u0, vlo, g0, acc); break;
+    case 5: rs_batch<F32, CL, U, 5, FIRST>(src, u0, vlo, g0, acc); break;
+    case 6: rs_batch<F32, CL, U, 6, FIRST>(src, u0, vlo, g0, acc); break;
+    case 7: rs_batch<F32, CL, U, 7, FIRST>(src, u0, vlo, g0, acc); break;
+    default: rs_batch<F32, CL, U, 8, FIRST>(src, u0, vlo, g0, acc); break;
+  }
+}
+
+// Instances of the reduce-scatter for a W fixed at run time (WT <= 0): any
+// W, and any W below 4 (whose steps cover twice the groups per lane).
+constexpr int kAnyW = 0;
+constexpr int kAnySmallW = -1;
+
+// Full steps of U groups per lane over the chunk body [vlo, vlo + 4 ng) for
+// any W: batches of 8 ranks (the last one shorter), each batch's loads issued
+// together; each batch's source pointers come from the call table through
+// the scalar cache.  Returns where the steps stopped.
+template <bool F32, bool CL, bool CS, int EPI, int U>
+__device__ __forceinline__ int64_t any_steps(const void* const* src, int32_t W, float* dst, int64_t vlo, int64_t ng,
+                                             int64_t g, float alpha) {
+  const int32_t full = W >> 3, rest = W & 7;
+  float* d = dst + vlo;
+  int64_t base = 0;
+  for (; base + 64 * U <= ng; base += 64 * U) {
+    float acc[U][4];
+    f32x4 o[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) o[k] = old4<EPI, CL>(d + (base + g + 64 * k) * 4);
+    if (full > 0) {
+      rs_batch<F32, CL, U, 8, true>(src, 0, vlo, base + g, acc);
+      for (int32_t b = 1; b < full; ++b) rs_batch<F32, CL, U, 8, false>(src, b * 8, vlo, base + g, acc);
+      if (rest > 0) rs_batch_n<F32, CL, U, false>(rest, src, full * 8, vlo, base + g, acc);
+    } else {
+      rs_batch_n<F32, CL, U, true>(rest, src, 0, vlo, base + g, acc);
+    }
+#pragma unroll
+    for (int k = 0; k < U; ++k) put4<CS, EPI>(d + (base + g + 64 * k) * 4, acc[k], alpha, o[k]);
+  }
+  return base;
+}
+
 // Vector body of a sum chunk: groups of 4 elements in [vlo, vhi), every
 // source and the destination group-aligned there.  Lane l handles groups
 // l, l + 64, ...; kRsUnroll groups per step keep kRsUnroll*W independent loads
@@ -357,7 +440,7 @@ __device__ __forceinline__ void sum_body(const void* const* src, int32_t W, floa
   const int64_t ng = (vhi - vlo) >> 2;
   const int64_t g = lane_id();
   if constexpr (WT > 0) {
-    constexpr int U = kRsUnroll;  // bf16 only, see below
+    constexpr int U = WT <= 4 ? 2 * kRsUnroll : kRsUnroll;  // bf16 only, see below
     const T* s[WT];
 #pragma unroll
     for (int u = 0; u < WT; ++u) s[u] = static_cast<const T*>(src[u]) + vlo;
@@ -366,9 +449,10 @@ __device__ __forceinline__ void sum_body(const void* const* src, int32_t W, floa
     // 32-bit lane offset: two scalar registers per source, so that the next
     // chunk's descriptor, fetched meanwhile, stays in scalar registers and no
     // wait for it is needed before this chunk's loads.
-    // bf16 sources: U groups per lane per step.  fp32 sources have twice the
-    // bytes per group and take one group per lane per step, the loop after
-    // this one; either way a wave has 8 KiB of source loads in flight
+    // bf16 sources: U groups per lane per step (twice as many for W = 4, whose
+    // groups have half the sources).  fp32 sources have twice the bytes per
+    // group and take one group per lane per step, the loop after this one;
+    // either way a wave of the W = 8 path has 8 KiB of source loads in flight
     // (measured on MI355X: twice that is 6-9% slower for fp32, as it is for
     // bf16).
     int64_t base = 0;
@@ -405,8 +489,16 @@ __device__ __forceinline__ void sum_body(const void* const* src, int32_t W, floa
       put4<CS, EPI>(d + gk * 4, a, alpha, o);
     }
   } else {
-    // Any W: sources in batches of 8, still added in rank order.
-    for (int64_t gk = g; gk < ng; gk += 64) {
+    // Any W: sources in batches of 8 (the last one shorter), added in rank
+    // order into accumulators that carry from batch to batch.  A step covers
+    // the groups per lane of the templated W = 8 path, and twice as many in
+    // the instance for fewer than 4 sources, so that a batch keeps about the
+    // same bytes of loads in flight per wave.  (The two step widths are two
+    // kernel instances: one kernel holding both measured 10% slower.)
+    constexpr int U = (WT == kAnySmallW ? 2 : 1) * (F32 ? 1 : kRsUnroll);
+    const int64_t base = any_steps<F32, CL, CS, EPI, U>(src, W, dst, vlo, ng, g, alpha);
+    // the groups left over (fewer than one step's), one per lane
+    for (int64_t gk = base + g; gk < ng; gk += 64) {
       const int64_t e = vlo + gk * 4;
       float acc[4];
       S::first(load<V, CL>(static_cast<const T*>(src[0]) + e), acc);
@@ -697,7 +789,7 @@ int launch_rs_t(const KernelArgs& a, int64_t grid, hipStream_t s) {
   switch (a.nsrc) {
     case 8: return launch_rs_w<8, F32>(a, grid, s);
     case 4: return launch_rs_w<4, F32>(a, grid, s);
-    default: return launch_rs_w<0, F32>(a, grid, s);
+    default: return a.nsrc < 4 ? launch_rs_w<kAnySmallW, F32>(a, grid, s) : launch_rs_w<kAnyW, F32>(a, grid, s);
   }
 }
 
