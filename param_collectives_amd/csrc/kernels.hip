@@ -582,8 +582,52 @@ __device__ __forceinline__ int64_t copy_steps(const uint16_t* sv, uint16_t* dv, 
   return base;
 }
 
-// bf16 [lo, hi): groups of 8 in [vlo, vhi) with both sides 16-byte aligned
-// (kCoUnroll 16-byte loads in flight per lane, then two, then one), the rest
+// Eight bf16 elements starting PS elements (1..7) into the 32 bytes a, b:
+// a funnel shift of the two 16-byte blocks.
+template <int PS>
+__device__ __forceinline__ u32x4 shift8(u32x4 a, u32x4 b) {
+  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  constexpr int q = PS >> 1;
+  if constexpr ((PS & 1) != 0) {
+    return u32x4{__builtin_amdgcn_alignbyte(w[q + 1], w[q], 2), __builtin_amdgcn_alignbyte(w[q + 2], w[q + 1], 2),
+                 __builtin_amdgcn_alignbyte(w[q + 3], w[q + 2], 2), __builtin_amdgcn_alignbyte(w[q + 4], w[q + 3], 2)};
+  } else {
+    return u32x4{w[q], w[q + 1], w[q + 2], w[q + 3]};
+  }
+}
+
+// Realigned steps of U groups of 8 per lane: the destination is 16-byte
+// aligned, the source PS elements past a 16-byte boundary, so destination
+// group k takes source blocks k and k + 1 of the aligned blocks sb[] (both
+// hold elements of the group, so no load leaves the source's pages; the
+// second is the neighbouring lane's first and comes from the cache).
+template <int PS, int U, bool CL, bool CS>
+__device__ __forceinline__ int64_t shift_steps(const u32x4* sb, uint16_t* dv, int64_t base, int64_t ng, int lane) {
+  for (; base + 64 * U <= ng; base += 64 * U) {
+    u32x4 a[U], b[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      a[k] = load<u32x4, CL>(sb + (base + lane + 64 * k));
+      b[k] = load<u32x4, CL>(sb + (base + lane + 64 * k + 1));
+    }
+#pragma unroll
+    for (int k = 0; k < U; ++k) store<u32x4, CS>(dv + (base + lane + 64 * k) * 8, shift8<PS>(a[k], b[k]));
+  }
+  return base;
+}
+
+template <int PS, bool CL, bool CS>
+__device__ __forceinline__ void shift_body(const uint16_t* sv, uint16_t* dv, int64_t ng, int lane) {
+  const u32x4* sb = reinterpret_cast<const u32x4*>(sv - PS);
+  int64_t base = shift_steps<PS, kCoUnroll / 2, CL, CS>(sb, dv, 0, ng, lane);
+  base = shift_steps<PS, 1, CL, CS>(sb, dv, base, ng, lane);
+  for (int64_t gk = base + lane; gk < ng; gk += 64)
+    store<u32x4, CS>(dv + gk * 8, shift8<PS>(load<u32x4, CL>(sb + gk), load<u32x4, CL>(sb + gk + 1)));
+}
+
+// bf16 [lo, hi): groups of 8 in [vlo, vhi), where the destination is 16-byte
+// aligned (kCoUnroll 16-byte loads in flight per lane, then two, then one;
+// a source at another 16-byte phase takes the realigned body), the rest
 // element by element.
 template <bool CL, bool CS>
 __device__ __forceinline__ void copy_chunk(const uint16_t* src, uint16_t* dst, const Chunk& r) {
@@ -594,6 +638,17 @@ __device__ __forceinline__ void copy_chunk(const uint16_t* src, uint16_t* dst, c
   const uint16_t* sv = src + r.vlo;
   uint16_t* dv = dst + r.vlo;
   const int64_t ng = (r.vhi - r.vlo) >> 3;
+  const int ps = sgpr(int32_t((reinterpret_cast<uintptr_t>(sv) & 15) >> 1));
+  switch (ps) {
+    case 0: break;
+    case 1: shift_body<1, CL, CS>(sv, dv, ng, lane); return;
+    case 2: shift_body<2, CL, CS>(sv, dv, ng, lane); return;
+    case 3: shift_body<3, CL, CS>(sv, dv, ng, lane); return;
+    case 4: shift_body<4, CL, CS>(sv, dv, ng, lane); return;
+    case 5: shift_body<5, CL, CS>(sv, dv, ng, lane); return;
+    case 6: shift_body<6, CL, CS>(sv, dv, ng, lane); return;
+    default: shift_body<7, CL, CS>(sv, dv, ng, lane); return;
+  }
   int64_t base = 0;
   base = copy_steps<kCoUnroll, CL, CS>(sv, dv, base, ng, lane);
   base = copy_steps<2, CL, CS>(sv, dv, base, ng, lane);
@@ -636,8 +691,39 @@ __device__ __forceinline__ int64_t cast_steps(const float* sv, uint16_t* dv, int
   return base;
 }
 
-// fp32 [lo, hi) -> bf16: groups of 4 in [vlo, vhi) (16-byte loads, 8-byte
-// stores, each contiguous across the wave), the rest element by element.
+// Four fp32 elements starting PS elements (1..3) into the 32 bytes a, b.
+template <int PS>
+__device__ __forceinline__ f32x4 shift4(f32x4 a, f32x4 b) {
+  const float w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  return f32x4{w[PS], w[PS + 1], w[PS + 2], w[PS + 3]};
+}
+
+// Realigned cast body: the destination is 8-byte aligned, the source PS fp32
+// elements past a 16-byte boundary; destination group k takes aligned source
+// blocks k and k + 1 (both hold elements of the group).
+template <int PS, bool CL, bool CS>
+__device__ __forceinline__ void cast_shift_body(const float* sv, uint16_t* dv, int64_t ng, int lane) {
+  const f32x4* sb = reinterpret_cast<const f32x4*>(sv - PS);
+  constexpr int U = kCastUnroll / 2;
+  int64_t base = 0;
+  for (; base + 64 * U <= ng; base += 64 * U) {
+    f32x4 a[U], b[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      a[k] = load<f32x4, CL>(sb + (base + lane + 64 * k));
+      b[k] = load<f32x4, CL>(sb + (base + lane + 64 * k + 1));
+    }
+#pragma unroll
+    for (int k = 0; k < U; ++k) store<u32x2, CS>(dv + (base + lane + 64 * k) * 4, cast4(shift4<PS>(a[k], b[k])));
+  }
+  for (int64_t gk = base + lane; gk < ng; gk += 64)
+    store<u32x2, CS>(dv + gk * 4, cast4(shift4<PS>(load<f32x4, CL>(sb + gk), load<f32x4, CL>(sb + gk + 1))));
+}
+
+// fp32 [lo, hi) -> bf16: groups of 4 in [vlo, vhi), where the destination is
+// 8-byte aligned (16-byte loads, 8-byte stores, each contiguous across the
+// wave; a source at another 16-byte phase takes the realigned body), the rest
+// element by element.
 template <bool CL, bool CS>
 __device__ __forceinline__ void cast_chunk(const float* src, uint16_t* dst, const Chunk& r) {
   const int lane = lane_id();
@@ -647,6 +733,13 @@ __device__ __forceinline__ void cast_chunk(const float* src, uint16_t* dst, cons
   const float* sv = src + r.vlo;
   uint16_t* dv = dst + r.vlo;
   const int64_t ng = (r.vhi - r.vlo) >> 2;
+  const int ps = sgpr(int32_t((reinterpret_cast<uintptr_t>(sv) & 15) >> 2));
+  switch (ps) {
+    case 0: break;
+    case 1: cast_shift_body<1, CL, CS>(sv, dv, ng, lane); return;
+    case 2: cast_shift_body<2, CL, CS>(sv, dv, ng, lane); return;
+    default: cast_shift_body<3, CL, CS>(sv, dv, ng, lane); return;
+  }
   int64_t base = 0;
   base = cast_steps<kCastUnroll, CL, CS>(sv, dv, base, ng, lane);
   base = cast_steps<2, CL, CS>(sv, dv, base, ng, lane);

@@ -249,8 +249,9 @@ void co_call_table(const Geometry& g, const std::vector<Seg>& segs, const uint16
     uint16_t* dst = params[sg.dst_idx] + sg.dst_off;
     (*ptrs)[2 * s] = src;
     (*ptrs)[2 * s + 1] = dst;
-    const uintptr_t ps = reinterpret_cast<uintptr_t>(src) & 15, pd = reinterpret_cast<uintptr_t>(dst) & 15;
-    const int32_t head = ps == pd ? int32_t(skip_to(reinterpret_cast<uintptr_t>(src), 2, 16)) : -1;
+    // the vector body starts where the destination is 16-byte aligned; a
+    // source at another phase there takes the kernel's realigned body
+    const int32_t head = int32_t(skip_to(reinterpret_cast<uintptr_t>(dst), 2, 16));
     (*hdr)[s] = CallHdr{sg.len, sg.kind, head};
   }
 }
@@ -272,14 +273,14 @@ void ci_call_table(const Geometry& g, const std::vector<Seg>& segs, const void* 
       kind = kCast;
       const float* src = static_cast<const float*>(shards[sg.src_idx]) + sg.src_off;
       (*ptrs)[2 * s] = src;
-      // 16-byte fp32 loads feeding 8-byte bf16 stores: 4 elements
-      const int64_t h = skip_to(reinterpret_cast<uintptr_t>(src), 4, 16);
-      if (((d + uintptr_t(2 * h)) & 7) == 0) head = int32_t(h);
+      // 16-byte fp32 loads feeding 8-byte bf16 stores: 4 elements; the body
+      // starts where the destination is 8-byte aligned (a source at another
+      // 16-byte phase there takes the kernel's realigned body)
+      head = int32_t(skip_to(d, 2, 8));
     } else {
       const uint16_t* src = static_cast<const uint16_t*>(shards[sg.src_idx]) + sg.src_off;
       (*ptrs)[2 * s] = src;
-      const uintptr_t ps = reinterpret_cast<uintptr_t>(src) & 15;
-      if (ps == (d & 15)) head = int32_t(skip_to(reinterpret_cast<uintptr_t>(src), 2, 16));
+      head = int32_t(skip_to(d, 2, 16));  // as for the copy-out
     }
     (*hdr)[s] = CallHdr{sg.len, kind, head};
   }

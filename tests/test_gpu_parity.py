@@ -206,6 +206,33 @@ def test_copyout_misaligned_tensors(tide, oracle_mod):
                 assert np.array_equal(got[p], want[p]), (rm_offset, poffs, p)
 
 
+def test_copies_every_source_phase(tide, oracle_mod):
+    """Every 16-byte phase of the source against an aligned destination (and
+    against a destination at phase 3): the copy-out's and the bf16 copy-in's
+    realigned bodies for shifts of 1..7 elements, the fp32 copy-in's for 1..3,
+    with ragged tails and several chunks per segment."""
+    rng = np.random.default_rng(31)
+    for W, shapes, chunk in ((1, [(4099,), (37, 29)], 256), (3, [(3 * 37 + 1, 29), (1001,)], 64)):
+        plan = tide.Plan(W, shapes, chunk_elems=chunk)
+        rm = rng.integers(0, 0x10000, size=W * plan.shard_elems, dtype=np.uint16)
+        want = oracle_mod.copyout(W, shapes, rm)
+        for rm_offset in range(8):
+            for poff in (0, 3):
+                got = run_copyout(tide, plan, rm, param_offsets=[poff] * len(shapes), rm_offset=rm_offset)
+                for p in range(len(shapes)):
+                    assert np.array_equal(got[p], want[p]), (W, rm_offset, poff, p)
+        X = [rng.standard_normal(s).astype(np.float32) for s in shapes]
+        shards = oracle_pins.shards_of(W, shapes, X)
+        cwant = oracle_mod.copyin(W, shapes, shards)
+        bits = [rng.integers(0, 0x10000, size=s, dtype=np.uint16) for s in shapes]
+        bshards = oracle_pins.shards_of(W, shapes, bits)
+        bwant = oracle_mod.copyin(W, shapes, bshards)
+        for off in range(8):
+            offs = [[off] * len(shapes) for _ in range(W)]
+            assert np.array_equal(run_copyin(tide, plan, shards, shard_offsets=offs), cwant), (W, off, "fp32")
+            assert np.array_equal(run_copyin(tide, plan, bshards, shard_offsets=offs), bwant), (W, off, "bf16")
+
+
 def test_rs_special_values(tide, oracle_mod):
     rng = np.random.default_rng(9)
     W = 8
