@@ -81,6 +81,7 @@ struct OpState {
   size_t call_bytes = 0;
   std::vector<const void*> key;      // pointers of the last uploaded call table
   bool key_valid = false;
+  bool has_shift = false;            // reduce-scatter: the call table needs the realigning instance
   std::vector<tide::CallHdr> hdr;    // host scratch for building the call table
   std::vector<const void*> ptrs;
   std::vector<unsigned char> call_host;
@@ -294,6 +295,26 @@ void launch_at(const OpState& s, const Launches& L, int64_t c0, tide::ChunkSpan*
   *grid = std::min<int64_t>(L.grid, (c1 - c0 + tide::kWavesPerGroup - 1) / tide::kWavesPerGroup);
 }
 
+// Whether a reduce-scatter call should run the kernel instance that realigns
+// sum segments whose sources (all at one phase) are off a 4-element group
+// boundary where the destination is 16-byte aligned: when such segments hold
+// more than 1/50 of the call's elements.  (That instance is a few percent
+// slower on aligned segments; the plain ones sum a few off-phase segments,
+// say the norms of a layer, element by element.)
+bool needs_shift(const OpState& s, int32_t nsrc, bool f32) {
+  const uintptr_t esize = f32 ? 4 : 2;
+  int64_t off = 0, total = 0;
+  for (size_t i = 0; i < s.hdr.size(); ++i) {
+    const tide::CallHdr& h = s.hdr[i];
+    if (h.kind != tide::kSum) continue;
+    total += h.len;
+    if (h.head < 0 || h.len <= h.head) continue;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(s.ptrs[i * size_t(nsrc + 1)]) + uintptr_t(h.head) * esize;
+    if ((a & (4 * esize - 1)) != 0) off += h.len;
+  }
+  return off > total / 50;
+}
+
 // Upload what is stale, then launch.  `f32`: the reduce-scatter's gradients
 // or the copy-in's shards are fp32.  `alpha`, `accumulate`: the
 // reduce-scatter's Equation 5 terms.
@@ -314,6 +335,7 @@ tide_status run_op(tide_plan* p, tide::Op op, const std::vector<const void*>& ke
   if (!s.key_valid || s.key != key) {
     s.key_valid = false;
     build(&s.hdr, &s.ptrs);
+    s.has_shift = (op == tide::kOpRs || op == tide::kOpRsF32) && needs_shift(s, nsrc_of(p, op), f32);
     const size_t hb = s.hdr.size() * sizeof(tide::CallHdr), pb = s.ptrs.size() * sizeof(void*);
     s.call_host.resize(hb + pb);
     std::memcpy(s.call_host.data(), s.hdr.data(), hb);
@@ -336,6 +358,7 @@ tide_status run_op(tide_plan* p, tide::Op op, const std::vector<const void*>& ke
   a.flags = eff.flags;
   a.alpha = alpha;
   a.accumulate = accumulate;
+  a.realign = s.has_shift;
   for (int64_t c0 = 0; c0 < nchunks; c0 += L.per_launch) {
     int64_t g = 0;
     launch_at(s, L, c0, &a.span, &g);

@@ -397,6 +397,11 @@ __device__ __forceinline__ void rs_batch_n(int32_t nb, const void* const* src, i
 // W, and any W below 4 (whose steps cover twice the groups per lane).
 constexpr int kAnyW = 0;
 constexpr int kAnySmallW = -1;
+// Any W (W below 4), for calls with sum segments whose sources are off the
+// destination's phase: the any-W body plus the realigned one.  (Each step
+// width is its own instance: one kernel holding both measured 10-15% slower.)
+constexpr int kAnyWShift = -2;
+constexpr int kAnySmallWShift = -3;
 
 // Full steps of U groups per lane over the chunk body [vlo, vlo + 4 ng) for
 // any W: batches of 8 ranks (the last one shorter), each batch's loads issued
@@ -424,6 +429,117 @@ __device__ __forceinline__ int64_t any_steps(const void* const* src, int32_t W, 
     for (int k = 0; k < U; ++k) put4<CS, EPI>(d + (base + g + 64 * k) * 4, acc[k], alpha, o[k]);
   }
   return base;
+}
+
+// Four bf16 elements starting PS elements (1..3) into the 16 bytes a, b.
+template <int PS>
+__device__ __forceinline__ u32x2 shift4h(u32x2 a, u32x2 b) {
+  const uint32_t w[4] = {a.x, a.y, b.x, b.y};
+  constexpr int q = PS >> 1;
+  if constexpr ((PS & 1) != 0) {
+    return u32x2{__builtin_amdgcn_alignbyte(w[q + 1], w[q], 2), __builtin_amdgcn_alignbyte(w[q + 2], w[q + 1], 2)};
+  } else {
+    return u32x2{w[q], w[q + 1]};
+  }
+}
+
+// Four fp32 elements starting PS elements (1..3) into the 32 bytes a, b.
+template <int PS>
+__device__ __forceinline__ f32x4 shift4(f32x4 a, f32x4 b) {
+  const float w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  return f32x4{w[PS], w[PS + 1], w[PS + 2], w[PS + 3]};
+}
+
+// A realigned group of 4 source elements starting PS elements past a block
+// boundary: the aligned blocks a (holding the first element) and b (the next).
+template <bool F32, int PS>
+__device__ __forceinline__ typename Src<F32>::V shift_group(typename Src<F32>::V a, typename Src<F32>::V b) {
+  if constexpr (F32) {
+    return shift4<PS>(a, b);
+  } else {
+    return shift4h<PS>(a, b);
+  }
+}
+
+// rs_batch for sources PS elements (1..3) past a group boundary at the
+// chunk body's start, where the destination is 16-byte aligned: each source
+// group is built from the two aligned blocks that hold it (both hold
+// elements of the group, so no load leaves the source's pages).
+template <bool F32, bool CL, int U, int NB, bool FIRST, int PS>
+__device__ __forceinline__ void rs_batch_shift(const void* const* src, int32_t u0, int64_t vlo, int64_t g0,
+                                               float (&acc)[U][4]) {
+  using S = Src<F32>;
+  using T = typename S::T;
+  using V = typename S::V;
+  constexpr int kGroupBytes = 4 * int(sizeof(T));
+  const char* s[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) s[j] = reinterpret_cast<const char*>(static_cast<const T*>(src[u0 + j]) + vlo - PS);
+  V a[U][NB], b[U][NB];
+#pragma unroll
+  for (int k = 0; k < U; ++k) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      a[k][j] = load<V, CL>(s[j] + uint32_t((g0 + 64 * k) * kGroupBytes));
+      b[k][j] = load<V, CL>(s[j] + uint32_t((g0 + 64 * k + 1) * kGroupBytes));
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < U; ++k) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const V v = shift_group<F32, PS>(a[k][j], b[k][j]);
+      if (FIRST && j == 0) {
+        S::first(v, acc[k]);
+      } else {
+        S::add(v, acc[k]);
+      }
+    }
+  }
+}
+
+template <bool F32, bool CL, int U, bool FIRST, int PS>
+__device__ __forceinline__ void rs_batch_shift_n(int32_t nb, const void* const* src, int32_t u0, int64_t vlo,
+                                                 int64_t g0, float (&acc)[U][4]) {
+  switch (nb) {
+    case 1: rs_batch_shift<F32, CL, U, 1, FIRST, PS>(src, u0, vlo, g0, acc); break;
+    case 2: rs_batch_shift<F32, CL, U, 2, FIRST, PS>(src, u0, vlo, g0, acc); break;
+    case 3: rs_batch_shift<F32, CL, U, 3, FIRST, PS>(src, u0, vlo, g0, acc); break;
+    case 4: rs_batch_shift<F32, CL, U, 4, FIRST, PS>(src, u0, vlo, g0, acc); break;
+    case 5: rs_batch_shift<F32, CL, U, 5, FIRST, PS>(src, u0, vlo, g0, acc); break;
+    case 6: rs_batch_shift<F32, CL, U, 6, FIRST, PS>(src, u0, vlo, g0, acc); break;
+    case 7: rs_batch_shift<F32, CL, U, 7, FIRST, PS>(src, u0, vlo, g0, acc); break;
+    default: rs_batch_shift<F32, CL, U, 8, FIRST, PS>(src, u0, vlo, g0, acc); break;
+  }
+}
+
+// Realigned sum body for any W: full steps as in any_steps, then the groups
+// left over element by element (so that no load is unaligned).
+template <bool F32, bool CL, bool CS, int EPI, int PS>
+__device__ __forceinline__ void shift_sum_body(const void* const* src, int32_t W, float* dst, int64_t vlo,
+                                               int64_t vhi, float alpha) {
+  constexpr int U = F32 ? 1 : kRsUnroll;
+  const int64_t ng = (vhi - vlo) >> 2;
+  const int64_t g = lane_id();
+  const int32_t full = W >> 3, rest = W & 7;
+  float* d = dst + vlo;
+  int64_t base = 0;
+  for (; base + 64 * U <= ng; base += 64 * U) {
+    float acc[U][4];
+    f32x4 o[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) o[k] = old4<EPI, CL>(d + (base + g + 64 * k) * 4);
+    if (full > 0) {
+      rs_batch_shift<F32, CL, U, 8, true, PS>(src, 0, vlo, base + g, acc);
+      for (int32_t b = 1; b < full; ++b) rs_batch_shift<F32, CL, U, 8, false, PS>(src, b * 8, vlo, base + g, acc);
+      if (rest > 0) rs_batch_shift_n<F32, CL, U, false, PS>(rest, src, full * 8, vlo, base + g, acc);
+    } else {
+      rs_batch_shift_n<F32, CL, U, true, PS>(rest, src, 0, vlo, base + g, acc);
+    }
+#pragma unroll
+    for (int k = 0; k < U; ++k) put4<CS, EPI>(d + (base + g + 64 * k) * 4, acc[k], alpha, o[k]);
+  }
+  for (int64_t e = vlo + base * 4 + g; e < vhi; e += 64) put1<EPI>(dst + e, sum_one<F32>(src, W, e), alpha);
 }
 
 // Vector body of a sum chunk: groups of 4 elements in [vlo, vhi), every
@@ -528,6 +644,14 @@ __device__ __forceinline__ void zero_rows(float* dst, const Chunk& c, float alph
     put4<CS, EPI>(dst + e, z, alpha, old4<EPI, CL>(dst + e));
 }
 
+// Elements (0..3) by which a source is past a group boundary at element e.
+template <bool F32>
+__device__ __forceinline__ int src_phase(const void* src, int64_t e) {
+  using T = typename Src<F32>::T;
+  const uintptr_t sa = reinterpret_cast<uintptr_t>(static_cast<const T*>(src) + e);
+  return sgpr(int32_t((sa & (4 * sizeof(T) - 1)) / sizeof(T)));
+}
+
 // One chunk of the reduce-scatter: the sum of a kSum segment's piece, or the
 // zeros of a padding piece.
 template <int WT, bool F32, bool CL, bool CS, int EPI>
@@ -543,7 +667,25 @@ __device__ __forceinline__ void rs_chunk(const Tables& a, const Desc<WT>& d, int
   const int lane = lane_id();
   for (int64_t e = r.lo + lane; e < r.vlo; e += 64) put1<EPI>(dst + e, sum_one<F32>(src, W, e), alpha);
   for (int64_t e = r.vhi + lane; e < r.hi; e += 64) put1<EPI>(dst + e, sum_one<F32>(src, W, e), alpha);
-  if (r.vhi > r.vlo) sum_body<WT, F32, CL, CS, EPI>(src, W, dst, r.vlo, r.vhi, alpha);
+  if (r.vhi <= r.vlo) return;
+  // The destination is 16-byte aligned at vlo and all W sources share one
+  // phase; sources off a group boundary there are realigned by the instance
+  // launched for calls that have such segments (the others never meet one:
+  // should they, the chunk goes element by element).
+  const int ps = src_phase<F32>(src[0], r.vlo);
+  if constexpr (WT == kAnyWShift || WT == kAnySmallWShift) {
+    switch (ps) {
+      case 0: sum_body<WT == kAnySmallWShift ? kAnySmallW : kAnyW, F32, CL, CS, EPI>(src, W, dst, r.vlo, r.vhi, alpha); break;
+      case 1: shift_sum_body<F32, CL, CS, EPI, 1>(src, W, dst, r.vlo, r.vhi, alpha); break;
+      case 2: shift_sum_body<F32, CL, CS, EPI, 2>(src, W, dst, r.vlo, r.vhi, alpha); break;
+      default: shift_sum_body<F32, CL, CS, EPI, 3>(src, W, dst, r.vlo, r.vhi, alpha); break;
+    }
+  } else if (ps == 0) {
+    sum_body<WT, F32, CL, CS, EPI>(src, W, dst, r.vlo, r.vhi, alpha);
+  } else {
+    const void* const* row = a.ptrs + int64_t(d.seg) * (a.nsrc + 1);
+    for (int64_t e = r.vlo + lane; e < r.vhi; e += 64) put1<EPI>(dst + e, sum_one<F32>(row, W, e), alpha);
+  }
 }
 
 template <int WT, bool F32, bool CL, bool CS, bool STAGED>
@@ -691,12 +833,6 @@ __device__ __forceinline__ int64_t cast_steps(const float* sv, uint16_t* dv, int
   return base;
 }
 
-// Four fp32 elements starting PS elements (1..3) into the 32 bytes a, b.
-template <int PS>
-__device__ __forceinline__ f32x4 shift4(f32x4 a, f32x4 b) {
-  const float w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-  return f32x4{w[PS], w[PS + 1], w[PS + 2], w[PS + 3]};
-}
 
 // Realigned cast body: the destination is 8-byte aligned, the source PS fp32
 // elements past a 16-byte boundary; destination group k takes aligned source
@@ -877,8 +1013,29 @@ int launch_rs_w(const KernelArgs& a, int64_t grid, hipStream_t s) {
   return int(hipGetLastError());
 }
 
+// The realigning instances exist with the default (non-temporal) cache
+// policy only; the cache flags are hints and never change results.
+template <int WT, bool F32>
+int launch_rs_realign(const KernelArgs& a, int64_t grid, hipStream_t s) {
+  bool staged;
+  const size_t lds = staged_bytes(a, &staged);
+  if (staged) {
+    hipLaunchKernelGGL((rs_local_kernel<WT, F32, false, false, true>), dim3(unsigned(grid)),
+                       dim3(unsigned(tide::kThreads)), lds, s, a.hdr, a.ptrs, a.chunk_begin, a.nsrc, a.span, a.chunk,
+                       a.alpha, a.accumulate);
+  } else {
+    hipLaunchKernelGGL((rs_local_kernel<WT, F32, false, false, false>), dim3(unsigned(grid)),
+                       dim3(unsigned(tide::kThreads)), 0, s, a.hdr, a.ptrs, a.chunk_begin, a.nsrc, a.span, a.chunk,
+                       a.alpha, a.accumulate);
+  }
+  return int(hipGetLastError());
+}
+
 template <bool F32>
 int launch_rs_t(const KernelArgs& a, int64_t grid, hipStream_t s) {
+  if (a.realign)
+    return a.nsrc < 4 ? launch_rs_realign<kAnySmallWShift, F32>(a, grid, s)
+                      : launch_rs_realign<kAnyWShift, F32>(a, grid, s);
   switch (a.nsrc) {
     case 8: return launch_rs_w<8, F32>(a, grid, s);
     case 4: return launch_rs_w<4, F32>(a, grid, s);

@@ -231,8 +231,10 @@ void rs_call_table(const Geometry& g, const std::vector<Seg>& segs, const void* 
         row[u] = reinterpret_cast<const void*>(su);
         same = same && (su & (salign - 1)) == phase;
       }
-      const int64_t h = skip_to(s0, esize, salign);
-      if (same && ((d + uintptr_t(4 * h)) & 15) == 0) head = int32_t(h);
+      // the vector body starts where the destination is 16-byte aligned; the
+      // kernel realigns sources at another phase there, provided all W share
+      // one phase (else the segment goes element by element)
+      if (same) head = int32_t(skip_to(d, 4, 16));
     }
     (*hdr)[s] = CallHdr{sg.len, sg.kind, head};
   }

@@ -155,6 +155,7 @@ struct KernelArgs {
   uint32_t flags;
   float alpha;         // reduce-scatter only: Equation 5's scale
   int32_t accumulate;  // reduce-scatter only: add into the shards' old values
+  bool realign = false;  // reduce-scatter only: some sum segment's sources are off the destination's phase
 };
 
 // The calling thread's error message (tide_last_error), shared by every

@@ -154,6 +154,38 @@ def test_rs_fp32_misaligned_and_special_values(tide, oracle_mod):
               chunk_elems=chunk)
 
 
+@pytest.mark.parametrize("f32", [False, True])
+@pytest.mark.parametrize("world", [1, 3, 4, 8, 12])
+def test_rs_every_source_phase(tide, oracle_mod, world, f32):
+    """All ranks' gradients at one common element offset 0..3 against shards
+    at offset 0 or 2: every phase of the realigned sum body (shifts of 1..3
+    elements, for the templated and the any-W instances), with and without
+    Equation 5's epilogue, several chunks per segment and ragged tails."""
+    rng = np.random.default_rng(300 + world + (50 if f32 else 0))
+    shapes = [(world * 40 + 3, 37), (world * 16, 64), (5,)]
+    rand = oracle_pins.rand_f32 if f32 else oracle_pins.rand_bf16
+    grads = [[rand(rng, s) for s in shapes] for _ in range(world)]
+    for off in range(4):
+        offs = [[off] * len(shapes) for _ in range(world)]
+        for out_offset in (0, 2):
+            for alpha, accumulate in ((1.0, False), (0.37, True)):
+                check(tide, oracle_mod, world, shapes, grads, alpha, accumulate, seed=off, grad_offsets=offs,
+                      out_offset=out_offset, chunk_elems=64 if off % 2 else 1024)
+
+
+@pytest.mark.parametrize("world", [3, 6, 12])
+def test_rs_few_off_phase_segments(tide, oracle_mod, world):
+    """Small 1-D parameters at the end of a layer whose shards start off a
+    group boundary for some ranks (too few elements for the realigning
+    instance): the plain instances sum those chunks element by element."""
+    rng = np.random.default_rng(400 + world)
+    shapes = [(world * 512, 256), (world * 64, 64), (31,), (61,), (world * 5 + 2,)]
+    grads = [[oracle_pins.rand_bf16(rng, s) for s in shapes] for _ in range(world)]
+    for alpha, accumulate in ((1.0, False), (0.37, True)):
+        check(tide, oracle_mod, world, shapes, grads, alpha, accumulate, seed=world)
+        check(tide, oracle_mod, world, shapes, grads, alpha, accumulate, seed=world, chunk_elems=8)
+
+
 def test_rs_accumulate_twice_is_two_additions(tide, oracle_mod):
     """Accumulating twice equals the oracle applied twice (the shards are read
     back each time, not cached)."""
