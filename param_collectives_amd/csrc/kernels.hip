@@ -32,7 +32,9 @@
 //     are then fetched with scalar loads one chunk ahead, so the scalar
 //     fetch overlaps the vector loads of the current chunk.
 //   * Vector bodies use non-temporal loads and contiguous 8- or 16-byte
-//     stores; heads and tails of misaligned tensors take a scalar path.
+//     stores; heads and tails of misaligned tensors take a scalar path, and a
+//     source at another 16-byte phase than its destination is realigned in
+//     registers (two aligned blocks per group, shifted).
 //   * One launch covers a span of chunks; the host splits a long operation
 //     into several launches, so that the waves of one launch cannot drift far
 //     apart (which would widen the window).
