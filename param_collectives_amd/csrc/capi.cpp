@@ -135,7 +135,7 @@ tide_status rebuild_chunks(tide_plan* p, const tide_options& given) {
   std::string why;
   std::vector<int32_t> cb[tide::kNumOps];
   for (int i = 0; i < tide::kNumOps; ++i) {
-    const tide_options eff = tide::effective_options(given, kOps[i], 0);
+    const tide_options eff = tide::effective_options(given, kOps[i], 0, p->geo.world);
     tide_status st = tide::chunk_table(op_state(p, kOps[i]).segs, eff.chunk_elems, &cb[i], &why);
     if (st != TIDE_OK) return fail(st, why);
   }
@@ -345,7 +345,7 @@ tide_status run_op(tide_plan* p, tide::Op op, const std::vector<const void*>& ke
     s.key = key;
     s.key_valid = true;
   }
-  const tide_options eff = tide::effective_options(p->given, op, p->cu_count);
+  const tide_options eff = tide::effective_options(p->given, op, p->cu_count, p->geo.world);
   const Launches L = split_launches(s, eff);
   tide::KernelArgs a;
   a.hdr = static_cast<const tide::CallHdr*>(s.d_call);
@@ -513,7 +513,7 @@ tide_status tide_plan_launches(const tide_plan* plan, int32_t op, int32_t cu_cou
       return fail(TIDE_ERR_INVALID, "bad table/capacity/count");
     if (cu_count < 0) return fail(TIDE_ERR_INVALID, "cu_count must be >= 0");
     const tide_options eff =
-        tide::effective_options(plan->given, tide::Op(op), cu_count > 0 ? cu_count : plan->cu_count);
+        tide::effective_options(plan->given, tide::Op(op), cu_count > 0 ? cu_count : plan->cu_count, plan->geo.world);
     if (eff.cu_budget <= 0)
       return fail(TIDE_ERR_INVALID, "the plan is not bound to a device and has no cu_budget: pass cu_count");
     const OpState& s = op_state(plan, tide::Op(op));
@@ -559,7 +559,7 @@ tide_status tide_plan_get_options(const tide_plan* plan, int32_t op, tide_option
     if (!live(plan)) return fail(TIDE_ERR_INVALID, "unknown or destroyed plan");
     if (op < 0 || op >= tide::kNumOps) return fail(TIDE_ERR_INVALID, std::string("op must be ") + kOpNames);
     if (out == nullptr) return fail(TIDE_ERR_INVALID, "out must not be NULL");
-    *out = tide::effective_options(plan->given, tide::Op(op), plan->cu_count);
+    *out = tide::effective_options(plan->given, tide::Op(op), plan->cu_count, plan->geo.world);
     return TIDE_OK;
   });
 }

@@ -399,6 +399,9 @@ __device__ __forceinline__ void rs_batch_n(int32_t nb, const void* const* src, i
 // W, and any W below 4 (whose steps cover twice the groups per lane).
 constexpr int kAnyW = 0;
 constexpr int kAnySmallW = -1;
+// bf16, W <= 2 with chunks of at least 2048 elements: four times the groups per
+// step of the W = 8 path.
+constexpr int kAnyTinyW = -4;
 // Any W (W below 4), for calls with sum segments whose sources are off the
 // destination's phase: the any-W body plus the realigned one.  (Each step
 // width is its own instance: one kernel holding both measured 10-15% slower.)
@@ -613,7 +616,7 @@ __device__ __forceinline__ void sum_body(const void* const* src, int32_t W, floa
     // the instance for fewer than 4 sources, so that a batch keeps about the
     // same bytes of loads in flight per wave.  (The two step widths are two
     // kernel instances: one kernel holding both measured 10% slower.)
-    constexpr int U = (WT == kAnySmallW ? 2 : 1) * (F32 ? 1 : kRsUnroll);
+    constexpr int U = (WT == kAnyTinyW ? 4 : WT == kAnySmallW ? 2 : 1) * (F32 ? 1 : kRsUnroll);
     const int64_t base = any_steps<F32, CL, CS, EPI, U>(src, W, dst, vlo, ng, g, alpha);
     // the groups left over (fewer than one step's), one per lane
     for (int64_t gk = base + g; gk < ng; gk += 64) {
@@ -1041,7 +1044,11 @@ int launch_rs_t(const KernelArgs& a, int64_t grid, hipStream_t s) {
   switch (a.nsrc) {
     case 8: return launch_rs_w<8, F32>(a, grid, s);
     case 4: return launch_rs_w<4, F32>(a, grid, s);
-    default: return a.nsrc < 4 ? launch_rs_w<kAnySmallW, F32>(a, grid, s) : launch_rs_w<kAnyW, F32>(a, grid, s);
+    default:
+      if constexpr (!F32) {
+        if (a.nsrc <= 2 && a.chunk >= 2048) return launch_rs_w<kAnyTinyW, F32>(a, grid, s);
+      }
+      return a.nsrc < 4 ? launch_rs_w<kAnySmallW, F32>(a, grid, s) : launch_rs_w<kAnyW, F32>(a, grid, s);
   }
 }
 

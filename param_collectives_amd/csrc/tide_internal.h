@@ -29,6 +29,7 @@ constexpr int32_t kMaxStagedSegs = 16383;  // chunk-index table entries staged i
 // and takes one group per lane per step; its best chunk is a quarter as long.
 constexpr int32_t kRsWgPerCu = 1;
 constexpr int64_t kRsChunk = 1024;
+constexpr int64_t kRsChunkFewRanks = 2048;  // W <= 2: fewer bytes per element, longer chunks for full steps
 constexpr int32_t kRsF32WgPerCu = 1;
 constexpr int64_t kRsF32Chunk = 256;
 constexpr int32_t kCoWgPerCu = 1;
@@ -109,7 +110,7 @@ tide_status chunk_table(const std::vector<Seg>& segs, int64_t chunk, std::vector
 
 // Options as given (0 = default) -> effective options for one operation.
 tide_status check_options(const tide_options* in, tide_options* out, std::string* why);
-tide_options effective_options(const tide_options& given, Op op, int32_t cu_count);
+tide_options effective_options(const tide_options& given, Op op, int32_t cu_count, int32_t world);
 
 // Per-call tables.  Vector groups are 4 elements for the reduce-scatter
 // (8-byte bf16 or 16-byte fp32 loads, 16-byte fp32 stores) and 8 elements for

@@ -424,11 +424,13 @@ def test_too_many_chunks_is_a_range_error(tide):
     with pytest.raises(tide.TideError) as e:
         tide.Plan(1, [(2**33 + 8,)], chunk_elems=8)
     assert _status(e) == -2
-    plan = tide.Plan(1, [(2**34,)])  # 2^24 chunks of the default size
+    plan = tide.Plan(1, [(2**34,)])  # 2^23 chunks of the default size (2048 elements for W <= 2)
+    before = plan.options(0)
+    assert before["chunk_elems"] == 2048
     with pytest.raises(tide.TideError) as e:
         plan.set_options(chunk_elems=8)
     assert _status(e) == -2
-    assert plan.options(0)["chunk_elems"] == 1024  # unchanged after the failed call
+    assert plan.options(0) == before  # unchanged after the failed call
 
 
 @pytest.mark.parametrize("world,shapes", CASES)
