@@ -396,13 +396,14 @@ __device__ __forceinline__ void rs_batch_n(int32_t nb, const void* const* src, i
 }
 
 // Instances of the reduce-scatter for a W fixed at run time (WT <= 0): any
-// W, and any W below 4 (whose steps cover twice the groups per lane).
+// W, and any W below 8 (whose steps cover twice the groups per lane: its
+// batches hold fewer than 8 sources).
 constexpr int kAnyW = 0;
 constexpr int kAnySmallW = -1;
 // bf16, W <= 2 with chunks of at least 2048 elements: four times the groups per
 // step of the W = 8 path.
 constexpr int kAnyTinyW = -4;
-// Any W (W below 4), for calls with sum segments whose sources are off the
+// Any W (W below 8), for calls with sum segments whose sources are off the
 // destination's phase: the any-W body plus the realigned one.  (Each step
 // width is its own instance: one kernel holding both measured 10-15% slower.)
 constexpr int kAnyWShift = -2;
@@ -613,7 +614,7 @@ __device__ __forceinline__ void sum_body(const void* const* src, int32_t W, floa
     // Any W: sources in batches of 8 (the last one shorter), added in rank
     // order into accumulators that carry from batch to batch.  A step covers
     // the groups per lane of the templated W = 8 path, and twice as many in
-    // the instance for fewer than 4 sources, so that a batch keeps about the
+    // the instance for fewer than 8 sources, so that a batch keeps about the
     // same bytes of loads in flight per wave.  (The two step widths are two
     // kernel instances: one kernel holding both measured 10% slower.)
     constexpr int U = (WT == kAnyTinyW ? 4 : WT == kAnySmallW ? 2 : 1) * (F32 ? 1 : kRsUnroll);
@@ -1039,7 +1040,7 @@ int launch_rs_realign(const KernelArgs& a, int64_t grid, hipStream_t s) {
 template <bool F32>
 int launch_rs_t(const KernelArgs& a, int64_t grid, hipStream_t s) {
   if (a.realign)
-    return a.nsrc < 4 ? launch_rs_realign<kAnySmallWShift, F32>(a, grid, s)
+    return a.nsrc < 8 ? launch_rs_realign<kAnySmallWShift, F32>(a, grid, s)
                       : launch_rs_realign<kAnyWShift, F32>(a, grid, s);
   switch (a.nsrc) {
     case 8: return launch_rs_w<8, F32>(a, grid, s);
@@ -1048,7 +1049,7 @@ int launch_rs_t(const KernelArgs& a, int64_t grid, hipStream_t s) {
       if constexpr (!F32) {
         if (a.nsrc <= 2 && a.chunk >= 2048) return launch_rs_w<kAnyTinyW, F32>(a, grid, s);
       }
-      return a.nsrc < 4 ? launch_rs_w<kAnySmallW, F32>(a, grid, s) : launch_rs_w<kAnyW, F32>(a, grid, s);
+      return a.nsrc < 8 ? launch_rs_w<kAnySmallW, F32>(a, grid, s) : launch_rs_w<kAnyW, F32>(a, grid, s);
   }
 }
 
