@@ -108,7 +108,7 @@ typedef enum {
  *   wg_per_cu   workgroups (256 threads, four waves) per budgeted CU;
  *               default 1.
  *   chunk_elems elements per chunk (the unit a wave takes), a multiple of 8,
- *               at most 2^28; default 1024 (reduce-scatter; 2048 when W <= 2), 256
+ *               at most 2^28; default 1024 (reduce-scatter; 2048 when W <= 3), 256
  *               (reduce-scatter of fp32 gradients), 4096 (copy-out, copy-in),
  *               2048 (stock pack).
  *               A plan may have at most 2^30 chunks per operation.

@@ -400,7 +400,7 @@ __device__ __forceinline__ void rs_batch_n(int32_t nb, const void* const* src, i
 // batches hold fewer than 8 sources).
 constexpr int kAnyW = 0;
 constexpr int kAnySmallW = -1;
-// bf16, W <= 2 with chunks of at least 2048 elements: four times the groups per
+// bf16, W <= 3 with chunks of at least 2048 elements: four times the groups per
 // step of the W = 8 path.
 constexpr int kAnyTinyW = -4;
 // Any W (W below 8), for calls with sum segments whose sources are off the
@@ -1047,7 +1047,7 @@ int launch_rs_t(const KernelArgs& a, int64_t grid, hipStream_t s) {
     case 4: return launch_rs_w<4, F32>(a, grid, s);
     default:
       if constexpr (!F32) {
-        if (a.nsrc <= 2 && a.chunk >= 2048) return launch_rs_w<kAnyTinyW, F32>(a, grid, s);
+        if (a.nsrc <= 3 && a.chunk >= 2048) return launch_rs_w<kAnyTinyW, F32>(a, grid, s);
       }
       return a.nsrc < 8 ? launch_rs_w<kAnySmallW, F32>(a, grid, s) : launch_rs_w<kAnyW, F32>(a, grid, s);
   }

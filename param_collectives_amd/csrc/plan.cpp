@@ -186,7 +186,7 @@ tide_options effective_options(const tide_options& given, Op op, int32_t cu_coun
   tide_options o = given;
   if (o.cu_budget == 0) o.cu_budget = cu_count;
   const int32_t wg[kNumOps] = {kRsWgPerCu, kCoWgPerCu, kCiWgPerCu, kPkWgPerCu, kRsF32WgPerCu};
-  const int64_t chunk[kNumOps] = {world <= 2 ? kRsChunkFewRanks : kRsChunk, kCoChunk, kCiChunk, kPkChunk, kRsF32Chunk};
+  const int64_t chunk[kNumOps] = {world <= 3 ? kRsChunkFewRanks : kRsChunk, kCoChunk, kCiChunk, kPkChunk, kRsF32Chunk};
   if (o.wg_per_cu == 0) o.wg_per_cu = wg[op];
   if (o.chunk_elems == 0) o.chunk_elems = chunk[op];
   if (o.wave_chunks == 0) o.wave_chunks = kWaveChunks;

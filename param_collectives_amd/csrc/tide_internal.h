@@ -29,7 +29,7 @@ constexpr int32_t kMaxStagedSegs = 16383;  // chunk-index table entries staged i
 // and takes one group per lane per step; its best chunk is a quarter as long.
 constexpr int32_t kRsWgPerCu = 1;
 constexpr int64_t kRsChunk = 1024;
-constexpr int64_t kRsChunkFewRanks = 2048;  // W <= 2: fewer bytes per element, longer chunks for full steps
+constexpr int64_t kRsChunkFewRanks = 2048;  // W <= 3: fewer bytes per element, longer chunks for full steps
 constexpr int32_t kRsF32WgPerCu = 1;
 constexpr int64_t kRsF32Chunk = 256;
 constexpr int32_t kCoWgPerCu = 1;

@@ -424,7 +424,7 @@ def test_too_many_chunks_is_a_range_error(tide):
     with pytest.raises(tide.TideError) as e:
         tide.Plan(1, [(2**33 + 8,)], chunk_elems=8)
     assert _status(e) == -2
-    plan = tide.Plan(1, [(2**34,)])  # 2^23 chunks of the default size (2048 elements for W <= 2)
+    plan = tide.Plan(1, [(2**34,)])  # 2^23 chunks of the default size (2048 elements for W <= 3)
     before = plan.options(0)
     assert before["chunk_elems"] == 2048
     with pytest.raises(tide.TideError) as e:
