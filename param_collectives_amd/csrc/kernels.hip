@@ -395,19 +395,17 @@ __device__ __forceinline__ void rs_batch_n(int32_t nb, const void* const* src, i
   }
 }
 
-// Instances of the reduce-scatter for a W fixed at run time (WT <= 0): any
-// W, and any W below 8 (whose steps cover twice the groups per lane: its
-// batches hold fewer than 8 sources).
+// Instances of the reduce-scatter for a W fixed at run time (WT <= 0).  Their
+// steps cover twice the groups per lane of the templated W = 8 path (batches
+// of up to 8 sources, often fewer in the last one; measured on MI355X: 3-15%
+// faster than the W = 8 step width for every W tried, 5 to 64).
 constexpr int kAnyW = 0;
-constexpr int kAnySmallW = -1;
 // bf16, W <= 3 with chunks of at least 2048 elements: four times the groups per
 // step of the W = 8 path.
 constexpr int kAnyTinyW = -4;
-// Any W (W below 8), for calls with sum segments whose sources are off the
-// destination's phase: the any-W body plus the realigned one.  (Each step
-// width is its own instance: one kernel holding both measured 10-15% slower.)
+// Any W, for calls with sum segments whose sources are off the destination's
+// phase: the any-W body plus the realigned one.
 constexpr int kAnyWShift = -2;
-constexpr int kAnySmallWShift = -3;
 
 // Full steps of U groups per lane over the chunk body [vlo, vlo + 4 ng) for
 // any W: batches of 8 ranks (the last one shorter), each batch's loads issued
@@ -613,11 +611,9 @@ __device__ __forceinline__ void sum_body(const void* const* src, int32_t W, floa
   } else {
     // Any W: sources in batches of 8 (the last one shorter), added in rank
     // order into accumulators that carry from batch to batch.  A step covers
-    // the groups per lane of the templated W = 8 path, and twice as many in
-    // the instance for fewer than 8 sources, so that a batch keeps about the
-    // same bytes of loads in flight per wave.  (The two step widths are two
-    // kernel instances: one kernel holding both measured 10% slower.)
-    constexpr int U = (WT == kAnyTinyW ? 4 : WT == kAnySmallW ? 2 : 1) * (F32 ? 1 : kRsUnroll);
+    // twice the groups per lane of the templated W = 8 path (four times with
+    // W <= 3), since a batch often holds fewer than 8 sources.
+    constexpr int U = (WT == kAnyTinyW ? 4 : 2) * (F32 ? 1 : kRsUnroll);
     const int64_t base = any_steps<F32, CL, CS, EPI, U>(src, W, dst, vlo, ng, g, alpha);
     // the groups left over (fewer than one step's), one per lane
     for (int64_t gk = base + g; gk < ng; gk += 64) {
@@ -679,9 +675,9 @@ __device__ __forceinline__ void rs_chunk(const Tables& a, const Desc<WT>& d, int
   // launched for calls that have such segments (the others never meet one:
   // should they, the chunk goes element by element).
   const int ps = src_phase<F32>(src[0], r.vlo);
-  if constexpr (WT == kAnyWShift || WT == kAnySmallWShift) {
+  if constexpr (WT == kAnyWShift) {
     switch (ps) {
-      case 0: sum_body<WT == kAnySmallWShift ? kAnySmallW : kAnyW, F32, CL, CS, EPI>(src, W, dst, r.vlo, r.vhi, alpha); break;
+      case 0: sum_body<kAnyW, F32, CL, CS, EPI>(src, W, dst, r.vlo, r.vhi, alpha); break;
       case 1: shift_sum_body<F32, CL, CS, EPI, 1>(src, W, dst, r.vlo, r.vhi, alpha); break;
       case 2: shift_sum_body<F32, CL, CS, EPI, 2>(src, W, dst, r.vlo, r.vhi, alpha); break;
       default: shift_sum_body<F32, CL, CS, EPI, 3>(src, W, dst, r.vlo, r.vhi, alpha); break;
@@ -1039,9 +1035,7 @@ int launch_rs_realign(const KernelArgs& a, int64_t grid, hipStream_t s) {
 
 template <bool F32>
 int launch_rs_t(const KernelArgs& a, int64_t grid, hipStream_t s) {
-  if (a.realign)
-    return a.nsrc < 8 ? launch_rs_realign<kAnySmallWShift, F32>(a, grid, s)
-                      : launch_rs_realign<kAnyWShift, F32>(a, grid, s);
+  if (a.realign) return launch_rs_realign<kAnyWShift, F32>(a, grid, s);
   switch (a.nsrc) {
     case 8: return launch_rs_w<8, F32>(a, grid, s);
     case 4: return launch_rs_w<4, F32>(a, grid, s);
@@ -1049,7 +1043,7 @@ int launch_rs_t(const KernelArgs& a, int64_t grid, hipStream_t s) {
       if constexpr (!F32) {
         if (a.nsrc <= 3 && a.chunk >= 2048) return launch_rs_w<kAnyTinyW, F32>(a, grid, s);
       }
-      return a.nsrc < 8 ? launch_rs_w<kAnySmallW, F32>(a, grid, s) : launch_rs_w<kAnyW, F32>(a, grid, s);
+      return launch_rs_w<kAnyW, F32>(a, grid, s);
   }
 }
 
