@@ -763,7 +763,7 @@ __device__ __forceinline__ int64_t shift_steps(const u32x4* sb, uint16_t* dv, in
 template <int PS, bool CL, bool CS>
 __device__ __forceinline__ void shift_body(const uint16_t* sv, uint16_t* dv, int64_t ng, int lane) {
   const u32x4* sb = reinterpret_cast<const u32x4*>(sv - PS);
-  int64_t base = shift_steps<PS, kCoUnroll / 2, CL, CS>(sb, dv, 0, ng, lane);
+  int64_t base = shift_steps<PS, kCoUnroll, CL, CS>(sb, dv, 0, ng, lane);
   base = shift_steps<PS, 1, CL, CS>(sb, dv, base, ng, lane);
   for (int64_t gk = base + lane; gk < ng; gk += 64)
     store<u32x4, CS>(dv + gk * 8, shift8<PS>(load<u32x4, CL>(sb + gk), load<u32x4, CL>(sb + gk + 1)));
@@ -842,7 +842,7 @@ __device__ __forceinline__ int64_t cast_steps(const float* sv, uint16_t* dv, int
 template <int PS, bool CL, bool CS>
 __device__ __forceinline__ void cast_shift_body(const float* sv, uint16_t* dv, int64_t ng, int lane) {
   const f32x4* sb = reinterpret_cast<const f32x4*>(sv - PS);
-  constexpr int U = kCastUnroll / 2;
+  constexpr int U = kCastUnroll;
   int64_t base = 0;
   for (; base + 64 * U <= ng; base += 64 * U) {
     f32x4 a[U], b[U];
