@@ -16,8 +16,9 @@ time, with
   * the roofline of the dominant kernel (the reduce-scatter) against MI355X's
     8 TB/s HBM peak, and its measured HBM traffic when a counter summary for
     the current kernel source is committed under profiles/;
-  * a CU-budget sweep, each kernel on a stream masked to the budget's CUs
-    (GB/s per CU is the analog of the pages' per-CTA sum rate);
+  * a CU-budget sweep, each kernel on a stream masked to the budget's CUs,
+    with one and with four workgroups per CU (GB/s per CU is the analog of
+    the pages' per-CTA sum rate);
   * a plain device-to-device copy of the copy-out's byte count, and the
     copy-out kernel on one flat tensor of the same bytes, for context;
   * Equation 5's epilogue (alpha = 1/W, accumulate into the shards) and the
@@ -26,7 +27,9 @@ time, with
     rank-major into W*S fp32 per rank) followed by the fp32 reduce-scatter
     of the packed buffers, against the layout-aware reduce-scatter that
     replaces both (same shards, bit for bit, checked in the run);
-  * the CPU oracle timed on the host's cores on the same workload.
+  * the CPU oracle timed on the host's cores on the same workload, streamed
+    in groups of parameters so that host memory stays bounded, with a
+    bitwise check of the run's outputs against it.
 Algorithmic bytes: reduce-scatter 2*W*sum(D*K) read + 4*W*S written (padding
 is written, never read); copy-out 2*sum(D*K) read + 2*sum(D*K) written.
 """
@@ -45,7 +48,9 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 METRIC = "effective HBM GB/s (and % of peak) for RS-local reduce and AG copy-out"
-DEFAULT_WORKLOAD = "llama3.1-8b-layer"
+DEFAULT_WORKLOAD = "llama3.1-70b-layer"
+# host memory the CPU leg holds at once: one group of parameters' gradients
+GROUP_BYTES = 8_000_000_000
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 KERNEL_SOURCE = os.path.join(ROOT, "param_collectives_amd", "csrc", "kernels.hip")
 
@@ -65,6 +70,8 @@ def parse_args(argv=None):
     ap.add_argument("--flags", type=int, default=0)
     ap.add_argument("--no-sweep", action="store_true", help="skip the CU-budget sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="CPU work the oracle leg repeats its steps for (at least 3 per parameter group)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the Equation 5 epilogue, stock-path A/B and flat-copy sections (their launches "
                          "share the kernel names of the timed ones)")
@@ -115,6 +122,90 @@ def launches_per_call(plan, op):
     """Kernel launches one call of operation `op` makes (the library's own
     split: at most wave_chunks chunks per wave per launch)."""
     return len(plan.launches(op))
+
+
+def param_groups(w, max_bytes):
+    """Consecutive parameters grouped so that one group's W ranks' bf16
+    gradients take at most max_bytes of host memory (a larger parameter is a
+    group of its own)."""
+    groups, cur, cur_bytes = [], [], 0
+    for p in range(w.nparams):
+        b = 2 * w.world * w.numel(p)
+        if cur and cur_bytes + b > max_bytes:
+            groups.append(cur)
+            cur, cur_bytes = [], 0
+        cur.append(p)
+        cur_bytes += b
+    if cur:
+        groups.append(cur)
+    return groups
+
+
+def cpu_leg(w, plan, grads, outs, rank_major, params, step_bytes, budget_s):
+    """The CPU oracle timed on the host's cores on the same workload, and the
+    bitwise verdict of this run's GPU outputs against it.
+
+    Host memory stays bounded: the parameters are taken in consecutive groups
+    of at most GROUP_BYTES of gradients.  A group's parameters occupy one
+    contiguous range of every rank's shard and of every rank-major slot, so
+    the oracle run on the group's shapes alone yields exactly those ranges.
+    Each group's oracle step (reduce-scatter, then copy-out) is repeated for
+    its share of `budget_s`; the step time is the sum over groups of the
+    median repetition, and one repetition on a single thread must give the
+    same bits."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    W, S = w.world, plan.shard_elems
+    threads = min(16, len(os.sched_getaffinity(0)))
+    total_elems = sum(w.numel(p) for p in range(w.nparams))
+    med_sum = one_sum = spent = 0.0
+    reps_total = 0
+    ok = ok_co = same_threads = True
+    groups = param_groups(w, GROUP_BYTES)
+    rm2d = rank_major.view(W, S)
+    for grp in groups:
+        shapes = [w.shapes[p] for p in grp]
+        lo = int(plan.shard_offset[grp[0]])
+        hi = int(plan.shard_offset[grp[-1] + 1]) if grp[-1] + 1 < w.nparams else S
+        host_g = [[grads[u][p].view(torch.int16).cpu().numpy().view(np.uint16) for p in grp] for u in range(W)]
+        host_rm = rm2d[:, lo:hi].contiguous().view(torch.int16).cpu().numpy().view(np.uint16).reshape(-1)
+        share = budget_s * sum(w.numel(p) for p in grp) / max(total_elems, 1)
+        times = []
+        want = want_co = None
+        while len(times) < 3 or (sum(times) < share and len(times) < 1000):
+            t = time.perf_counter()
+            want = oracle.rs_local(W, shapes, host_g, nthreads=threads)
+            want_co = oracle.copyout(W, shapes, host_rm, nthreads=threads)
+            times.append(time.perf_counter() - t)
+        t = time.perf_counter()
+        one = oracle.rs_local(W, shapes, host_g, nthreads=1)
+        oracle.copyout(W, shapes, host_rm, nthreads=1)
+        one_sum += time.perf_counter() - t
+        med_sum += statistics.median(times)
+        spent += sum(times)
+        reps_total += len(times)
+        same_threads = same_threads and all(
+            np.array_equal(one[r].view(np.uint32), want[r].view(np.uint32)) for r in range(W))
+        ok = ok and all(np.array_equal(outs[r][lo:hi].cpu().numpy().view(np.uint32), want[r].view(np.uint32))
+                        for r in range(W))
+        ok_co = ok_co and all(
+            np.array_equal(params[p].view(torch.int16).cpu().numpy().view(np.uint16), want_co[i])
+            for i, p in enumerate(grp))
+        del host_g, host_rm, want, want_co, one
+    cpu = {"value": round(step_bytes / med_sum / 1e9, 2), "unit": "GB/s", "cores": threads,
+           "single_thread_value": round(step_bytes / one_sum / 1e9, 2),
+           "single_thread_matches": same_threads,
+           "kind": "oracle",
+           "cpu": cpu_model(),
+           "sample": f"every parameter of {w.name} (reduce-scatter + copy-out, same inputs as the GPU), streamed in "
+                     f"{len(groups)} groups of at most {GROUP_BYTES / 1e9:.0f} GB of gradients; {reps_total} group "
+                     f"steps in {spent:.1f} s; step = sum of the groups' median times, {med_sum:.3f} s; "
+                     f"{threads} threads"}
+    parity = {"rs_local": "bit-exact" if ok else "MISMATCH", "ag_copyout": "bit-exact" if ok_co else "MISMATCH"}
+    return cpu, parity
 
 
 def main(argv=None):
@@ -255,28 +346,29 @@ def main(argv=None):
     kernels = {"rs_local": kstats(rs_ms, rs_bytes), "ag_copyout": kstats(co_ms, co_bytes)}
 
     # CU-budget sweep: each kernel confined to `budget` CUs by a CU-masked
-    # stream (a hard budget), four workgroups (16 waves) per CU; results are
-    # bit-identical by design
+    # stream (a hard budget), with one workgroup (4 waves, the default) and
+    # four workgroups (16 waves) per CU; results are bit-identical by design
     sweep = []
     if not args.no_sweep:
         for budget in (8, 16, 32, 64, 128, 256):
             masked = tide.Stream(cus=range(budget))
-            plan.set_options(**dict(opts, cu_budget=budget, wg_per_cu=4))
-            row = {"cu_budget": budget, "wg_per_cu": 4, "cu_masked": True}
-            for name, call, nbytes in (("rs_local", rs_call, rs_bytes), ("ag_copyout", co_call, co_bytes)):
-                ms_ = masked.torch
-                call(ms_)
-                e = [(ev(), ev()) for _ in range(10)]
-                for a, b in e:
-                    a.record(ms_)
+            for wg in (1, 4):
+                plan.set_options(**dict(opts, cu_budget=budget, wg_per_cu=wg))
+                row = {"cu_budget": budget, "wg_per_cu": wg, "cu_masked": True}
+                for name, call, nbytes in (("rs_local", rs_call, rs_bytes), ("ag_copyout", co_call, co_bytes)):
+                    ms_ = masked.torch
                     call(ms_)
-                    b.record(ms_)
-                ms_.synchronize()
-                avg = sum(a.elapsed_time(b) for a, b in e) / len(e)
-                row[name] = {"avg_ms": round(avg, 5), "gbps": round(nbytes / avg / 1e6, 1),
-                             "gbps_per_cu": round(nbytes / avg / 1e6 / budget, 2)}
+                    e = [(ev(), ev()) for _ in range(10)]
+                    for a, b in e:
+                        a.record(ms_)
+                        call(ms_)
+                        b.record(ms_)
+                    ms_.synchronize()
+                    avg = sum(a.elapsed_time(b) for a, b in e) / len(e)
+                    row[name] = {"avg_ms": round(avg, 5), "gbps": round(nbytes / avg / 1e6, 1),
+                                 "gbps_per_cu": round(nbytes / avg / 1e6 / budget, 2)}
+                sweep.append(row)
             masked.destroy()
-            sweep.append(row)
         plan.set_options(**opts)
 
     # the all-gather copy-in (fp32 master shards of every rank -> rank-major
@@ -409,48 +501,12 @@ def main(argv=None):
         flat["copyout_over_flat"] = round(flat["avg_ms"] / kernels["ag_copyout"]["avg_ms"], 4)
         del fsrc, fdst, fplan, fcall
 
-    # CPU oracle on the same workload, and a bitwise check of this run's outputs
+    # CPU oracle on the same workload, streamed in groups of parameters, and a
+    # bitwise check of this run's outputs against it
     cpu = None
     parity = None
     if not args.no_cpu_baseline:
-        import oracle
-
-        host_grads = [[g.view(torch.int16).cpu().numpy().view(np.uint16) for g in row] for row in grads]
-        host_rm = rank_major.view(torch.int16).cpu().numpy().view(np.uint16)
-        threads = min(16, os.cpu_count() or 1)
-        times = []
-        want = want_co = None
-        spent = 0.0
-        # repeat whole steps for about 10 s of CPU work (at least 3, at most 30 s)
-        while len(times) < 3 or (spent < 10.0 and len(times) < 1000):
-            t = time.perf_counter()
-            want = oracle.rs_local(W, w.shapes, host_grads, nthreads=threads)
-            want_co = oracle.copyout(W, w.shapes, host_rm, nthreads=threads)
-            dt = time.perf_counter() - t
-            times.append(dt)
-            spent += dt
-            if spent > 30.0:
-                break
-        med = statistics.median(times)
-        # one step on a single thread as well (the oracle's threads split work
-        # between (rank, parameter) pairs, never an element's sum)
-        t = time.perf_counter()
-        one = oracle.rs_local(W, w.shapes, host_grads, nthreads=1)
-        oracle.copyout(W, w.shapes, host_rm, nthreads=1)
-        t1 = time.perf_counter() - t
-        same_threads = all(np.array_equal(one[r].view(np.uint32), want[r].view(np.uint32)) for r in range(W))
-        del one
-        cpu = {"value": round((rs_bytes + co_bytes) / med / 1e9, 2), "unit": "GB/s", "cores": threads,
-               "single_thread_value": round((rs_bytes + co_bytes) / t1 / 1e9, 2),
-               "single_thread_matches": same_threads,
-               "kind": "oracle",
-               "cpu": cpu_model(),
-               "sample": f"full {w.name} steps (reduce-scatter + copy-out, same inputs as the GPU), "
-                         f"{len(times)} steps in {spent:.1f} s, median {med:.3f} s per step, {threads} threads"}
-        ok = all(np.array_equal(outs[r].cpu().numpy().view(np.uint32), want[r].view(np.uint32)) for r in range(W))
-        ok_co = all(np.array_equal(params[p].view(torch.int16).cpu().numpy().view(np.uint16), want_co[p])
-                    for p in range(w.nparams))
-        parity = {"rs_local": "bit-exact" if ok else "MISMATCH", "ag_copyout": "bit-exact" if ok_co else "MISMATCH"}
+        cpu, parity = cpu_leg(w, plan, grads, outs, rank_major, params, rs_bytes + co_bytes, args.cpu_seconds)
 
     rs_k = kernels["rs_local"]
     achieved = rs_bytes / (rs_k["avg_ms"] * 1e-3) / 1e9

@@ -59,6 +59,10 @@
  *     graph, and a later call of that operation with other pointers, or
  *     tide_plan_set_options, rewrites those tables and so changes what a
  *     replay does (use one plan per set of buffers that a graph records).
+ *     A call on a stream that is capturing, which would set up or upload
+ *     those tables (the plan's first call of that operation, other pointers
+ *     or other options than the previous call's), returns TIDE_ERR_INVALID
+ *     and enqueues nothing.
  */
 #ifndef TIDE_H
 #define TIDE_H
@@ -159,6 +163,17 @@ tide_status tide_plan_create(int32_t world, int32_t nparams, const int32_t* ndim
  */
 tide_status tide_plan_layout(const tide_plan* plan, int64_t* rows_per_rank, int64_t* shard_offset,
                              int64_t* shard_elems);
+
+/*
+ * Element counts of a plan's tensors (Section 2.1), for sizing the buffers a
+ * call takes.  Any output pointer may be NULL.
+ *   param_elems  [P] D_p * K_p: the elements of parameter p (of each rank's
+ *                gradient of p, and of the copy-out's destination params[p])
+ *   real_elems   [W*P] at index r*P + p, n_real(p, r): the real (non-padding)
+ *                elements of rank r's shard of p, i.e. of the local shard
+ *                that tide_allgather_copyin reads as shards[r*P + p]
+ */
+tide_status tide_plan_sizes(const tide_plan* plan, int64_t* param_elems, int64_t* real_elems);
 
 /*
  * The plan's work segments, for inspection and tests.  op 0 = reduce-scatter,

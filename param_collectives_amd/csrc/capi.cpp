@@ -301,19 +301,23 @@ void launch_at(const OpState& s, const Launches& L, int64_t c0, tide::ChunkSpan*
 // more than 1/50 of the call's elements.  (That instance is a few percent
 // slower on aligned segments; the plain ones sum a few off-phase segments,
 // say the norms of a layer, element by element.)
-bool needs_shift(const OpState& s, int32_t nsrc, bool f32) {
+bool needs_shift(const std::vector<tide::CallHdr>& hdr, const std::vector<const void*>& ptrs, int32_t nsrc,
+                 bool f32) {
   const uintptr_t esize = f32 ? 4 : 2;
   int64_t off = 0, total = 0;
-  for (size_t i = 0; i < s.hdr.size(); ++i) {
-    const tide::CallHdr& h = s.hdr[i];
+  for (size_t i = 0; i < hdr.size(); ++i) {
+    const tide::CallHdr& h = hdr[i];
     if (h.kind != tide::kSum) continue;
     total += h.len;
     if (h.head < 0 || h.len <= h.head) continue;
-    const uintptr_t a = reinterpret_cast<uintptr_t>(s.ptrs[i * size_t(nsrc + 1)]) + uintptr_t(h.head) * esize;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(ptrs[i * size_t(nsrc + 1)]) + uintptr_t(h.head) * esize;
     if ((a & (4 * esize - 1)) != 0) off += h.len;
   }
   return off > total / 50;
 }
+
+tide_status launch_op(const OpState& s, tide::Op op, const tide_options& eff, tide::KernelArgs a, hipStream_t stream,
+                      bool f32);
 
 // Upload what is stale, then launch.  `f32`: the reduce-scatter's gradients
 // or the copy-in's shards are fp32.  `alpha`, `accumulate`: the
@@ -324,6 +328,16 @@ tide_status run_op(tide_plan* p, tide::Op op, const std::vector<const void*>& ke
   OpState& s = op_state(p, op);
   const int32_t nchunks = s.chunk_begin.back();
   if (nchunks == 0) return TIDE_OK;  // nothing to write
+  // Under graph capture a call may only enqueue kernel launches: the plan's
+  // first call (device set-up) and table uploads (new pointers or options)
+  // would allocate, copy or synchronize, so they are refused before any of it.
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  hipError_t ce = hipStreamIsCapturing(stream, &cap);
+  if (ce != hipSuccess) return hip_fail(ce, "hipStreamIsCapturing");
+  if (cap != hipStreamCaptureStatusNone && (p->device < 0 || s.chunks_stale || !s.key_valid || s.key != key))
+    return fail(TIDE_ERR_INVALID,
+                "the stream is capturing a graph, but this call would set up or upload the plan's device tables "
+                "(first call, new pointers or new options): make the same call once before capturing");
   tide_status st = bind_device(p);
   if (st != TIDE_OK) return st;
   if (s.chunks_stale) {
@@ -335,7 +349,7 @@ tide_status run_op(tide_plan* p, tide::Op op, const std::vector<const void*>& ke
   if (!s.key_valid || s.key != key) {
     s.key_valid = false;
     build(&s.hdr, &s.ptrs);
-    s.has_shift = (op == tide::kOpRs || op == tide::kOpRsF32) && needs_shift(s, nsrc_of(p, op), f32);
+    s.has_shift = (op == tide::kOpRs || op == tide::kOpRsF32) && needs_shift(s.hdr, s.ptrs, nsrc_of(p, op), f32);
     const size_t hb = s.hdr.size() * sizeof(tide::CallHdr), pb = s.ptrs.size() * sizeof(void*);
     s.call_host.resize(hb + pb);
     std::memcpy(s.call_host.data(), s.hdr.data(), hb);
@@ -345,20 +359,28 @@ tide_status run_op(tide_plan* p, tide::Op op, const std::vector<const void*>& ke
     s.key = key;
     s.key_valid = true;
   }
-  const tide_options eff = tide::effective_options(p->given, op, p->cu_count, p->geo.world);
-  const Launches L = split_launches(s, eff);
   tide::KernelArgs a;
   a.hdr = static_cast<const tide::CallHdr*>(s.d_call);
   a.ptrs = reinterpret_cast<const void* const*>(static_cast<unsigned char*>(s.d_call) +
                                                 s.segs.size() * sizeof(tide::CallHdr));
   a.chunk_begin = s.d_chunk_begin;
   a.nsrc = nsrc_of(p, op);
-  a.nchunks = nchunks;
-  a.chunk = int32_t(eff.chunk_elems);
-  a.flags = eff.flags;
   a.alpha = alpha;
   a.accumulate = accumulate;
   a.realign = s.has_shift;
+  return launch_op(s, op, tide::effective_options(p->given, op, p->cu_count, p->geo.world), a, stream, f32);
+}
+
+// Launch every kernel of one call of `op` whose tables `a` points to (its
+// hdr, ptrs, chunk_begin, nsrc and Equation 5 fields set; the rest is filled
+// in here from the options).
+tide_status launch_op(const OpState& s, tide::Op op, const tide_options& eff, tide::KernelArgs a, hipStream_t stream,
+                      bool f32) {
+  const int32_t nchunks = s.chunk_begin.back();
+  const Launches L = split_launches(s, eff);
+  a.nchunks = nchunks;
+  a.chunk = int32_t(eff.chunk_elems);
+  a.flags = eff.flags;
   for (int64_t c0 = 0; c0 < nchunks; c0 += L.per_launch) {
     int64_t g = 0;
     launch_at(s, L, c0, &a.span, &g);
@@ -388,11 +410,10 @@ tide_status run_op(tide_plan* p, tide::Op op, const std::vector<const void*>& ke
   return TIDE_OK;
 }
 
-// Both reduce-scatter entry points: `grads` holds uint16_t (bf16) or float
-// pointers, as `f32` says.
-tide_status reduce_scatter(tide_plan* plan, const void* const* grads, bool f32, float* const* out, float alpha,
-                           int32_t accumulate, void* stream) {
-  g_last_error.clear();
+// Argument checks of every reduce-scatter entry point: `grads` holds uint16_t
+// (bf16) or float pointers, as `f32` says.
+tide_status check_rs(const tide_plan* plan, const void* const* grads, bool f32, float* const* out,
+                     int32_t accumulate) {
   if (!live(plan)) return fail(TIDE_ERR_INVALID, "unknown or destroyed plan");
   if (grads == nullptr || out == nullptr) return fail(TIDE_ERR_INVALID, "grads and out must not be NULL");
   if (accumulate != 0 && accumulate != 1) return fail(TIDE_ERR_INVALID, "accumulate must be 0 or 1");
@@ -414,6 +435,17 @@ tide_status reduce_scatter(tide_plan* plan, const void* const* grads, bool f32, 
     if (reinterpret_cast<uintptr_t>(out[r]) & 3)
       return fail(TIDE_ERR_ALIGN, "out[" + std::to_string(r) + "] is not 4-byte aligned");
   }
+  return TIDE_OK;
+}
+
+// Both reduce-scatter entry points with plan-owned device tables.
+tide_status reduce_scatter(tide_plan* plan, const void* const* grads, bool f32, float* const* out, float alpha,
+                           int32_t accumulate, void* stream) {
+  g_last_error.clear();
+  tide_status st = check_rs(plan, grads, f32, out, accumulate);
+  if (st != TIDE_OK) return st;
+  const tide::Geometry& g = plan->geo;
+  const int64_t W = g.world, P = g.nparams;
   std::vector<const void*> key(grads, grads + W * P);
   key.insert(key.end(), out, out + W);
   const tide::Op op = f32 ? tide::kOpRsF32 : tide::kOpRs;
@@ -474,6 +506,20 @@ tide_status tide_plan_layout(const tide_plan* plan, int64_t* rows_per_rank, int6
       if (shard_offset) shard_offset[p] = plan->geo.o[p];
     }
     if (shard_elems) *shard_elems = plan->geo.S;
+    return TIDE_OK;
+  });
+}
+
+tide_status tide_plan_sizes(const tide_plan* plan, int64_t* param_elems, int64_t* real_elems) {
+  return tide::guarded([&]() -> tide_status {
+    g_last_error.clear();
+    if (!live(plan)) return fail(TIDE_ERR_INVALID, "unknown or destroyed plan");
+    const tide::Geometry& g = plan->geo;
+    for (int32_t p = 0; p < g.nparams; ++p) {
+      if (param_elems) param_elems[p] = g.D[p] * g.K[p];
+      if (real_elems)
+        for (int32_t r = 0; r < g.world; ++r) real_elems[int64_t(r) * g.nparams + p] = tide::real_elems(g, p, r);
+    }
     return TIDE_OK;
   });
 }

@@ -42,6 +42,7 @@ MAX_WORLD = 256
 EXPORTS = (
     "tide_plan_create",
     "tide_plan_layout",
+    "tide_plan_sizes",
     "tide_plan_segments",
     "tide_plan_set_options",
     "tide_plan_get_options",
@@ -81,6 +82,7 @@ def _load():
     lib.tide_plan_create.argtypes = [i32, i32, ctypes.POINTER(i32), i64p, ctypes.POINTER(Options),
                                      ctypes.POINTER(vp)]
     lib.tide_plan_layout.argtypes = [vp, i64p, i64p, i64p]
+    lib.tide_plan_sizes.argtypes = [vp, i64p, i64p]
     lib.tide_plan_segments.argtypes = [vp, i32, i64p, i64, i64p]
     lib.tide_plan_set_options.argtypes = [vp, ctypes.POINTER(Options)]
     lib.tide_plan_get_options.argtypes = [vp, i32, ctypes.POINTER(Options)]
@@ -143,10 +145,14 @@ class Plan:
                                     o.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
                                     S.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))))
         self.rows_per_rank, self.shard_offset, self.shard_elems = R, o, int(S[0])
-        self.numel = [int(np.prod(s, dtype=np.int64)) for s in self.shapes]
-        # real elements of rank r's shard of parameter p
-        self.n_real = [[max(0, min(int(R[p]), s[0] - r * int(R[p]))) * (self.numel[p] // s[0] if s[0] else 0)
-                        for p, s in enumerate(self.shapes)] for r in range(self.world)]
+        # element counts as the library sizes them: numel[p] of parameter p,
+        # n_real[r][p] of rank r's shard of p (its real, non-padding elements)
+        numel = np.zeros(len(self.shapes), dtype=np.int64)
+        real = np.zeros(self.world * len(self.shapes), dtype=np.int64)
+        _check(lib.tide_plan_sizes(self.handle, numel.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                   real.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))))
+        self.numel = [int(v) for v in numel]
+        self.n_real = real.reshape(self.world, len(self.shapes)).tolist()
 
     def segments(self, op):
         """The work segments (op 0: reduce-scatter, 1: copy-out, 2: copy-in,

@@ -1,5 +1,5 @@
 """The benchmark's one JSON line, on the GPU: a short run of the default
-workload (the Llama-3.1-8B layer) with the CPU-oracle leg, checked for every
+workload (the Llama-3.1-70B layer) with the CPU-oracle leg, checked for every
 field the report is read by, for internal consistency (rates against bytes
 and times, the roofline fraction against its peak), and for the bitwise
 parity verdict the run itself takes against the oracle."""
@@ -13,7 +13,7 @@ pytestmark = pytest.mark.gpu
 def test_bench_line(capsys):
     import bench
 
-    rc = bench.main(["--steps", "3", "--warmup", "1", "--no-sweep", "--no-extras"])
+    rc = bench.main(["--steps", "3", "--warmup", "1", "--no-sweep", "--no-extras", "--cpu-seconds", "1"])
     out = capsys.readouterr().out.strip().splitlines()
     assert rc == 0
     assert len(out) == 1, out
@@ -24,8 +24,8 @@ def test_bench_line(capsys):
     assert d["higher_is_better"] is True and d["scaling"] == "weak" and d["vs_baseline"] is None
     assert d["dtype"] == "f32" and d["data"] == "synthetic"
     cfg = d["config"]
-    assert cfg["workload"] == "llama3.1-8b-layer" and cfg["world"] == 8 and cfg["params"] == 9
-    assert cfg["elements"] == 218112000 and cfg["shard_elems"] == 27264000
+    assert cfg["workload"] == "llama3.1-70b-layer" and cfg["world"] == 8 and cfg["params"] == 9
+    assert cfg["elements"] == 855654400 and cfg["shard_elems"] == 106956800
 
     # the step's algorithmic bytes: reduce-scatter 2*W*sum(D*K) + 4*W*S, copy-out 4*sum(D*K)
     rs_bytes = 2 * 8 * cfg["elements"] + 4 * 8 * cfg["shard_elems"]

@@ -136,3 +136,66 @@ def test_captured_copyin_and_fp32_reduce_scatter_replays(tide, oracle_mod):
         want = oracle_mod.rs_local_ex(W, shapes, g)
         for r in range(W):
             gpu_util.assert_same_f32(outs[r].cpu().numpy(), want[r], f"replay {replay} rank {r}")
+
+
+def test_capture_refuses_set_up_and_uploads(tide, oracle_mod):
+    """A call that would set up or upload the plan's tables while its stream
+    is capturing is refused before it enqueues anything (first call, other
+    pointers, other options); after a warm-up call with the same pointers the
+    capture succeeds and its replays match the eager result."""
+    import torch
+
+    W = 4
+    shapes = [(W * 33 + 2, 40), (7,)]
+    plan = tide.Plan(W, shapes)
+    rng = np.random.default_rng(5)
+    host = [[oracle_pins.rand_bf16(rng, s) for s in shapes] for _ in range(W)]
+    grads = [[gpu_util.to_device_bf16(host[u][p]).view(shapes[p]) for p in range(len(shapes))] for u in range(W)]
+    outs = [torch.full((plan.shard_elems,), float("nan"), device="cuda") for _ in range(W)]
+    other = [torch.full((plan.shard_elems,), float("nan"), device="cuda") for _ in range(W)]
+    rs = tide.reduce_scatter_call(plan, grads, outs)
+    rs_other = tide.reduce_scatter_call(plan, grads, other)
+    marker = torch.zeros(16, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+
+    def refused(call):
+        graph = torch.cuda.CUDAGraph()
+        with pytest.raises(tide.TideError, match="capturing") as e:
+            with torch.cuda.graph(graph, stream=s):
+                marker.add_(1.0)  # the graph is never empty
+                call()
+        assert e.value.status == -1
+        torch.cuda.synchronize()
+
+    refused(lambda: rs(s))  # first call: the plan is not set up yet
+    with torch.cuda.stream(s):
+        rs()  # eager warm-up: set-up and uploads happen here
+    torch.cuda.synchronize()
+    want = oracle_mod.rs_local(W, shapes, host)
+    for r in range(W):
+        gpu_util.assert_same_f32(outs[r].cpu().numpy(), want[r], f"eager rank {r}")
+    refused(lambda: rs_other(s))  # other pointers: the call table would be re-uploaded
+    for o in other:
+        assert torch.isnan(o).all()  # nothing was enqueued for them
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        rs()
+    for replay in range(3):
+        for o in outs:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for r in range(W):
+            gpu_util.assert_same_f32(outs[r].cpu().numpy(), want[r], f"replay {replay} rank {r}")
+
+    plan.set_options(chunk_elems=512)  # new chunk table: must be uploaded eagerly first
+    refused(lambda: rs(s))
+    with torch.cuda.stream(s):
+        rs()
+    torch.cuda.synchronize()
+    for r in range(W):
+        gpu_util.assert_same_f32(outs[r].cpu().numpy(), want[r], f"after new options, rank {r}")

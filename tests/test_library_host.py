@@ -78,6 +78,34 @@ def test_layout_matches_oracle(tide, oracle_mod, world, shapes):
 
 
 @pytest.mark.parametrize("world,shapes", CASES)
+def test_exported_sizes_match_oracle(tide, oracle_mod, world, shapes):
+    """The element counts the binding sizes its buffers by come from the
+    library (tide_plan_sizes), and they are the oracle's: D_p*K_p per
+    parameter, n_real(p, r) per rank's local shard."""
+    plan = tide.Plan(world, shapes)
+    geo = oracle_mod.plan(world, shapes)
+    assert plan.numel == [int(d * k) for d, k in zip(geo["D"], geo["K"])]
+    assert plan.n_real == [[int(geo["n_real"][p, r]) for p in range(len(shapes))] for r in range(world)]
+    # either output may be omitted
+    import ctypes
+
+    buf = np.full(world * len(shapes), -7, dtype=np.int64)
+    assert tide.lib.tide_plan_sizes(plan.handle, None, buf.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))) == 0
+    assert buf.reshape(world, -1).tolist() == plan.n_real
+    assert tide.lib.tide_plan_sizes(plan.handle, None, None) == 0
+    assert tide.lib.tide_plan_sizes(None, None, None) == -1
+
+
+def test_binding_holds_no_layout_arithmetic():
+    """The binding marshals: the shard geometry (rows per rank, real rows of a
+    shard) is read from the library, never recomputed in Python."""
+    src = open(os.path.join(ROOT, "param_collectives_amd", "tide.py")).read()
+    assert "tide_plan_sizes" in src and "tide_plan_layout" in src
+    for pattern in (r"\bmin\(", r"\bmax\(0", r"np\.prod", r"// ?s\[0\]", r"- ?r ?\*"):
+        assert not re.search(pattern, src), pattern
+
+
+@pytest.mark.parametrize("world,shapes", CASES)
 def test_segments_describe_the_oracle_layout(tide, oracle_mod, world, shapes):
     """Each (rank, parameter) pair's real part is one sum segment reading
     n_real elements at the owner's first row, and its padding one zero
