@@ -255,6 +255,38 @@ tide_status tide_reduce_scatter_local(tide_plan* plan, const uint16_t* const* gr
                                       float alpha, int32_t accumulate, void* stream);
 
 /*
+ * Allocation-free reduce-scatter, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, results and errors as
+ * tide_reduce_scatter_local, bit for bit, with these differences:
+ *   - No call allocates anything (no hipMalloc, hipFree, pinned or other
+ *     allocation) and none uses the plan's device tables or binds the plan
+ *     to a device: every call rebuilds its tables in host buffers the plan
+ *     made when it was created, and writes them into a fixed scratch array
+ *     of TIDE_NOALLOC_SCRATCH_BYTES in device memory, which the library holds
+ *     on each device it runs on until the process ends.  The writes are
+ *     kernel launches on `stream` carrying the table words as arguments, so
+ *     the call is asynchronous and may be captured into a graph (a replay
+ *     rewrites the recorded tables before the recorded reduce-scatter).  The
+ *     first call on a device also looks up the array's device address; make
+ *     one call on the device before capturing.
+ *   - The tables of a plan of P parameters and W ranks, with N reduce-
+ *     scatter segments (at most 2*W*P: a sum and a padding segment per rank
+ *     and parameter), take 4*(N+1) bytes rounded up to 16, plus
+ *     16*N + 8*(W+1)*N bytes (at W = 8 without padding, N = W*P segments of
+ *     92 bytes: up to about 1,400 parameters); above
+ *     TIDE_NOALLOC_SCRATCH_BYTES the call returns TIDE_ERR_RANGE and
+ *     enqueues nothing.
+ *   - All calls on one device share its scratch array, which keeps the
+ *     tables of the last call: calls on one stream (or otherwise ordered)
+ *     are safe, while calls that may overlap on the device (other streams,
+ *     other host threads) race for it and give undefined results.
+ */
+#define TIDE_NOALLOC_SCRATCH_BYTES (1u << 20)
+tide_status tide_reduce_scatter_local_noalloc(tide_plan* plan, const uint16_t* const* grads, float* const* out,
+                                              float alpha, int32_t accumulate, void* stream);
+
+/*
  * Reduce-scatter local stage from fp32 gradients (Section 4; the fp32
  * reduce-scatter of Section 4.3): as tide_reduce_scatter_local with
  * grads[u*P + p] fp32 (4-byte aligned) and g_u its value as it is.  With a

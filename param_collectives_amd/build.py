@@ -14,7 +14,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(HERE, "libtide.so")
-SOURCES = [os.path.join(CSRC, n) for n in ("plan.cpp", "capi.cpp", "kernels.hip", "instruments.hip")]
+SOURCES = [os.path.join(CSRC, n) for n in ("plan.cpp", "capi.cpp", "kernels.hip", "instruments.hip", "scratch.hip")]
 ARCH = "gfx950"
 
 

@@ -90,11 +90,26 @@ struct OpState {
 
 }  // namespace
 
+// Host side of the allocation-free reduce-scatter: the buffers its calls
+// build their tables in, sized when the plan is created, so that a call
+// allocates nothing.  The tables go to the device's scratch array as one
+// image: the chunk table (int32, padded to 16 bytes), the segment headers,
+// then the pointers.
+struct NoAllocHost {
+  std::vector<tide::CallHdr> hdr;
+  std::vector<const void*> ptrs;
+  std::vector<uint64_t> image;
+  size_t bytes = 0;     // of the image
+  size_t hdr_off = 0;   // byte offsets of the headers and the pointers in it
+  size_t ptrs_off = 0;
+};
+
 struct tide_plan {
   uint64_t magic = 0;
   tide::Geometry geo;
   tide_options given{};  // as passed (0 = default)
   OpState rs, co, ci, pk, rsf;  // rsf: the reduce-scatter of fp32 gradients
+  NoAllocHost na;                // the allocation-free reduce-scatter (bf16 gradients)
   int device = -1;
   int cu_count = 0;
 };
@@ -457,6 +472,70 @@ tide_status reduce_scatter(tide_plan* plan, const void* const* grads, bool f32, 
       static_cast<hipStream_t>(stream), f32, alpha, accumulate);
 }
 
+// Sizes the allocation-free reduce-scatter's host buffers (when its image
+// fits the device scratch; its calls are refused otherwise).
+void size_noalloc(tide_plan* p) {
+  NoAllocHost& na = p->na;
+  const size_t nseg = p->rs.segs.size(), W = size_t(p->geo.world);
+  na.hdr_off = ((nseg + 1) * sizeof(int32_t) + 15) / 16 * 16;
+  na.ptrs_off = na.hdr_off + nseg * sizeof(tide::CallHdr);
+  na.bytes = na.ptrs_off + nseg * (W + 1) * sizeof(void*);
+  if (na.bytes > tide::kScratchBytes) return;
+  na.hdr.reserve(nseg);
+  na.ptrs.reserve(nseg * (W + 1));
+  na.image.assign((na.bytes + 7) / 8, 0);
+}
+
+// The allocation-free reduce-scatter: the tables of this call are built in the
+// plan's preallocated host buffers, written to the current device's scratch
+// array by put launches (their words travel as kernel arguments) and read
+// there by the same kernels as tide_reduce_scatter_local's.
+tide_status reduce_scatter_noalloc(tide_plan* plan, const uint16_t* const* grads, float* const* out, float alpha,
+                                   int32_t accumulate, void* stream_v) {
+  g_last_error.clear();
+  tide_status st = check_rs(plan, reinterpret_cast<const void* const*>(grads), false, out, accumulate);
+  if (st != TIDE_OK) return st;
+  const OpState& s = plan->rs;
+  NoAllocHost& na = plan->na;
+  if (na.bytes > tide::kScratchBytes)
+    return fail(TIDE_ERR_RANGE, "the reduce-scatter's tables take " + std::to_string(na.bytes) +
+                                    " bytes; the allocation-free entry point holds at most " +
+                                    std::to_string(tide::kScratchBytes));
+  if (s.chunk_begin.back() == 0) return TIDE_OK;  // nothing to write
+  hipStream_t stream = static_cast<hipStream_t>(stream_v);
+  void* base = nullptr;
+  int rc = tide::scratch_address(&base);
+  if (rc != 0) return hip_fail(hipError_t(rc), "hipGetSymbolAddress of the scratch array");
+  int dev = -1, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+
+  const tide::Geometry& g = plan->geo;
+  tide::rs_call_table(g, s.segs, reinterpret_cast<const void* const*>(grads), false, out, &na.hdr, &na.ptrs);
+  unsigned char* img = reinterpret_cast<unsigned char*>(na.image.data());
+  std::memcpy(img, s.chunk_begin.data(), s.chunk_begin.size() * sizeof(int32_t));
+  std::memcpy(img + na.hdr_off, na.hdr.data(), na.hdr.size() * sizeof(tide::CallHdr));
+  std::memcpy(img + na.ptrs_off, na.ptrs.data(), na.ptrs.size() * sizeof(void*));
+  const size_t words = (na.bytes + 7) / 8;
+  for (size_t w0 = 0; w0 < words; w0 += tide::kPutWords) {
+    const uint32_t n = uint32_t(std::min<size_t>(tide::kPutWords, words - w0));
+    rc = tide::launch_scratch_put(static_cast<uint64_t*>(base) + w0, na.image.data() + w0, n, stream);
+    if (rc != 0) return hip_fail(hipError_t(rc), "scratch_put_kernel launch");
+  }
+  tide::KernelArgs a;
+  unsigned char* b = static_cast<unsigned char*>(base);
+  a.chunk_begin = reinterpret_cast<const int32_t*>(b);
+  a.hdr = reinterpret_cast<const tide::CallHdr*>(b + na.hdr_off);
+  a.ptrs = reinterpret_cast<const void* const*>(b + na.ptrs_off);
+  a.nsrc = g.world;
+  a.alpha = alpha;
+  a.accumulate = accumulate;
+  a.realign = needs_shift(na.hdr, na.ptrs, g.world, false);
+  return launch_op(s, tide::kOpRs, tide::effective_options(plan->given, tide::kOpRs, cus, g.world), a, stream, false);
+}
+
 }  // namespace
 
 extern "C" {
@@ -486,6 +565,7 @@ tide_status tide_plan_create(int32_t world, int32_t nparams, const int32_t* ndim
     p->given = given;
     st = rebuild_chunks(p.get(), given);
     if (st != TIDE_OK) return st;
+    size_noalloc(p.get());
     p->magic = kMagic;
     {
       std::lock_guard<std::mutex> lock(g_plans_mu);
@@ -615,6 +695,12 @@ tide_status tide_reduce_scatter_local(tide_plan* plan, const uint16_t* const* gr
   return tide::guarded([&]() -> tide_status {
     return reduce_scatter(plan, reinterpret_cast<const void* const*>(grads), false, out, alpha, accumulate, stream);
   });
+}
+
+tide_status tide_reduce_scatter_local_noalloc(tide_plan* plan, const uint16_t* const* grads, float* const* out,
+                                              float alpha, int32_t accumulate, void* stream) {
+  return tide::guarded(
+      [&]() -> tide_status { return reduce_scatter_noalloc(plan, grads, out, alpha, accumulate, stream); });
 }
 
 tide_status tide_reduce_scatter_local_f32(tide_plan* plan, const float* const* grads, float* const* out,

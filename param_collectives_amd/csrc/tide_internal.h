@@ -1,6 +1,6 @@
-// Private types shared by the host planner (plan.cpp), the C ABI (capi.cpp)
-// and the device code (kernels.hip) of the layout-aware FSDP2 collective local
-// stages.
+// Private types shared by the host planner (plan.cpp), the C ABI (capi.cpp),
+// the device code (kernels.hip) and the allocation-free scratch (scratch.hip)
+// of the layout-aware FSDP2 collective local stages.
 #pragma once
 
 #include <cstdint>
@@ -180,6 +180,22 @@ tide_status guarded(F&& body) noexcept {
     return set_error_nothrow(TIDE_ERR_INVALID, "unexpected host-side exception");
   }
 }
+
+// Device scratch of the allocation-free reduce-scatter: a file-scope device
+// array of kScratchBytes (scratch.hip), one per device, holding the tables of
+// the latest such call on that device.  Its tables are written by put
+// launches, each carrying up to kPutWords 8-byte words as kernel arguments.
+constexpr size_t kScratchBytes = TIDE_NOALLOC_SCRATCH_BYTES;
+static_assert(kScratchBytes % 256 == 0, "scratch size");
+constexpr uint32_t kPutWords = 500;
+constexpr int kMaxDevices = 64;
+
+// Address of the current device's scratch array (looked up once per device
+// with hipGetSymbolAddress and kept); returns the hipError_t as int.
+int scratch_address(void** out);
+// Writes nwords (<= kPutWords) 8-byte words to dst (8-byte aligned) on
+// `stream`; returns the launch status.
+int launch_scratch_put(void* dst, const uint64_t* words, uint32_t nwords, void* stream);
 
 // Launch with `grid` workgroups of kThreads on `stream`; returns the launch
 // status (hipError_t as int).

@@ -37,6 +37,7 @@ FLAG_NO_LDS = 0x4
 DTYPE_BF16 = 0
 DTYPE_F32 = 1
 MAX_WORLD = 256
+NOALLOC_SCRATCH_BYTES = 1 << 20
 
 # Every symbol include/tide.h declares.
 EXPORTS = (
@@ -48,6 +49,7 @@ EXPORTS = (
     "tide_plan_get_options",
     "tide_plan_launches",
     "tide_reduce_scatter_local",
+    "tide_reduce_scatter_local_noalloc",
     "tide_allgather_copyout",
     "tide_allgather_copyin",
     "tide_reduce_scatter_local_f32",
@@ -91,6 +93,7 @@ def _load():
     lib.tide_allgather_copyout.argtypes = [vp, vp, ctypes.POINTER(vp), vp]
     lib.tide_allgather_copyin.argtypes = [vp, ctypes.POINTER(vp), i32, vp, vp]
     lib.tide_reduce_scatter_local_f32.argtypes = lib.tide_reduce_scatter_local.argtypes
+    lib.tide_reduce_scatter_local_noalloc.argtypes = lib.tide_reduce_scatter_local.argtypes
     lib.tide_stock_chunk_cat.argtypes = [vp, ctypes.POINTER(vp), vp, vp]
     i32p = ctypes.POINTER(i32)
     lib.tide_device_info.argtypes = [i32p, i32p, i32p, i32p]
@@ -319,6 +322,20 @@ def reduce_scatter_local(plan, grads, outs, alpha=1.0, accumulate=False, stream=
     added to the old outs[r] when accumulate is true."""
     g, o, f32 = _rs_checked(plan, grads, outs)
     plan.reduce_scatter_local_raw(g, o, alpha, int(bool(accumulate)), _stream_handle(stream), f32=f32)
+
+
+def reduce_scatter_local_noalloc(plan, grads, outs, alpha=1.0, accumulate=False, stream=None):
+    """The allocation-free reduce-scatter (tide_reduce_scatter_local_noalloc):
+    the results of reduce_scatter_local from bf16 gradients, with the call's
+    tables written to the library's fixed device scratch array instead of
+    plan-owned device memory.  Calls that may overlap on one device race for
+    that array."""
+    g, o, f32 = _rs_checked(plan, grads, outs)
+    if f32:
+        raise TypeError("the allocation-free reduce-scatter takes bf16 gradients")
+    _check(lib.tide_reduce_scatter_local_noalloc(plan.handle, _ptr_array(g), _ptr_array(o), ctypes.c_float(alpha),
+                                                 int(bool(accumulate)),
+                                                 ctypes.c_void_p(_stream_handle(stream) or None)))
 
 
 def _pk_checked(plan, grads, packed):
