@@ -52,7 +52,7 @@ DEFAULT_WORKLOAD = "llama3.1-70b-layer"
 # host memory the CPU leg holds at once: one group of parameters' gradients
 GROUP_BYTES = 8_000_000_000
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
-KERNEL_SOURCE = os.path.join(ROOT, "param_collectives_amd", "csrc", "kernels.hip")
+TRAFFIC_SOURCES = [os.path.join(ROOT, "param_collectives_amd", "csrc", n) for n in ("kernels.hip", "plan.cpp")]
 
 
 def parse_args(argv=None):
@@ -75,33 +75,44 @@ def parse_args(argv=None):
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the Equation 5 epilogue, stock-path A/B and flat-copy sections (their launches "
                          "share the kernel names of the timed ones)")
-    ap.add_argument("--only", choices=["rs", "co", "ci", "calib", "stock"],
+    ap.add_argument("--only", choices=["rs", "co", "ci", "calib", "stock", "torch"],
                     help="launch just one kernel (stock: the W packs and the fp32 reduce-scatter of the stock "
-                         "path) --launches times, for profiling, and exit")
+                         "path; torch: PyTorch's own fill and neg kernels over W*S bf16 elements, plain "
+                         "streams of known size for calibrating counters) --launches times, for profiling, and "
+                         "exit")
     ap.add_argument("--launches", type=int, default=5)
     return ap.parse_args(argv)
 
 
 def source_digest():
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """SHA-256 over the sources that decide the kernels' memory traffic: the
+    kernels and the planner that lays out their segments and vector bodies."""
+    h = hashlib.sha256()
+    for path in TRAFFIC_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def traffic_for(kernel_key):
-    """HBM bytes per launch from the committed counter summary, or None when
-    there is none for this kernel and workload or the kernel source changed."""
+    """HBM bytes per operation call from the committed counter summary:
+    (FETCH_SIZE + WRITE_SIZE scaled by a plain stream's calibration factors,
+    DRAM bytes from the 32-byte request counters), or (None, None) when there
+    is none for this kernel and workload or the kernel source changed."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
-        return None
+        return None, None
     if t.get("source_sha256") != source_digest():
-        return None
+        return None, None
     k = t.get("kernels", {}).get(kernel_key)
     cal = t.get("calibration")
     if not k or not cal:
-        return None
-    return k["fetch_kib"] * 1024.0 * cal["fetch_factor"] + k["write_kib"] * 1024.0 * cal["write_factor"]
+        return None, None
+    scaled = k["fetch_kib"] * 1024.0 * cal["fetch_factor"] + k["write_kib"] * 1024.0 * cal["write_factor"]
+    dram = k["dram_read_bytes"] + k["dram_write_bytes"] if "dram_read_bytes" in k else None
+    return scaled, dram
 
 
 def cpu_model():
@@ -237,6 +248,20 @@ def main(argv=None):
     rs_bytes = 2 * W * sum_dk + 4 * W * S
     co_bytes = 4 * sum_dk
     stream = torch.cuda.Stream()
+
+    if args.only == "torch":
+        # PyTorch's own elementwise kernels over W*S bf16 elements: plain
+        # streams of known size, outside this library, for calibrating counters
+        n = W * S
+        a = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+        b = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+        for _ in range(args.launches):
+            a.fill_(1.0)  # writes 2n bytes
+            torch.neg(a, out=b)  # reads 2n bytes, writes 2n bytes
+        torch.cuda.synchronize()
+        print(json.dumps({"only": "torch", "launches": args.launches, "fill_bytes_written": 2 * n,
+                          "neg_bytes_each_way": 2 * n}))
+        return 0
 
     with torch.cuda.stream(stream):
         grads = synth.grads_device(w, "cuda")
@@ -510,6 +535,8 @@ def main(argv=None):
 
     rs_k = kernels["rs_local"]
     achieved = rs_bytes / (rs_k["avg_ms"] * 1e-3) / 1e9
+    # the committed counters are for the workload's own W and default options
+    traffic = traffic_for(f"rs_local/{w.name}") if own_world else (None, None)
     value = (rs_bytes + co_bytes) / (ms_per_step * 1e-3) / 1e9
     line = {
         "metric": METRIC,
@@ -531,7 +558,7 @@ def main(argv=None):
         "roofline": {"bound": "hbm", "kernel": "rs_local_kernel", "unit_of_work": "one reduce-scatter call",
                      "launches_per_call": launches_per_call(plan, 0), "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic_for(f"rs_local/{w.name}") if own_world else None},
+                     "traffic": traffic[0], "traffic_dram": traffic[1]},
         "cpu_baseline": cpu,
         "kernels": kernels,
         "event_ms_per_step": round(step_ms_events, 5),

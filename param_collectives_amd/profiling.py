@@ -7,18 +7,29 @@
 `trace` runs bench.py under `rocprofv3 --kernel-trace --stats` twice: the
 timed step and the copy-in (with the sections whose reduce-scatter launches
 share the timed kernel's name left out), then the stock path alone (W stock
-packs and the fp32 reduce-scatter of the packed buffers); `counters` runs one `rocprofv3 --pmc` pass per counter group (a
-group never exceeds one hardware block's counter slots) on single-kernel
-launches of bench.py, including a calibration copy of known size;
-`summarize` reads those outputs and writes short text summaries and
+packs and the fp32 reduce-scatter of the packed buffers); `counters` runs one
+`rocprofv3 --pmc` pass per counter group (a group never exceeds one hardware
+block's counter slots) on single-kernel launches of bench.py, and on
+PyTorch's own fill and neg kernels over buffers of known size; `summarize`
+reads those outputs and writes short text summaries and
 profiles/hbm_traffic.json.
 
-HBM traffic: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by the
-ratio of known bytes to counted bytes for a plain copy of known size (the
-copy-out kernel on one flat tensor), per direction, and the result is tied to
-the SHA-256 of the kernel source, so that a stale figure is never reported.
-rocprofv3 is always started as a child process with the program to profile
-directly after `--`.
+HBM traffic, two independent ways:
+  * FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each scaled by the ratio of
+    known bytes to counted bytes for a plain stream of known size outside this
+    library (PyTorch's elementwise neg, one bf16 read and one write per
+    element); this is the `traffic` figure the benchmark reports;
+  * the L2-to-memory requests that went to DRAM, counted in 32-byte units
+    (TCC_EA0_RDREQ_DRAM_32B, TCC_EA0_WRREQ_WRITE_DRAM_32B): bytes with no
+    calibration factor.
+On gfx950 the FETCH_SIZE expression takes its 128-byte reads from TCC_BUBBLE,
+which stays 0 while every streaming read goes out as a 128-byte request, so
+FETCH_SIZE reads half the bytes; the calibration factor is that 2.
+A third pass counts the cycles the L2 waited for DRAM credits and the reads
+in flight (for the mean read latency).  Every figure is tied to the SHA-256 of
+the kernel source, so that a stale one is never reported.  rocprofv3 is
+always started as a child process with the program to profile directly after
+`--`.
 """
 import argparse
 import csv
@@ -34,13 +45,23 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-KERNEL_SOURCE = os.path.join(HERE, "csrc", "kernels.hip")
+TRAFFIC_SOURCES = [os.path.join(HERE, "csrc", n) for n in ("kernels.hip", "plan.cpp")]
 KERNEL_REGEX = "rs_local_kernel|ag_copyout_kernel|ag_copyin_kernel|stock_pack_kernel"
+# PyTorch's fill and neg kernels (bench.py --only torch): the calibration streams
+TORCH_REGEX = "FillFunctor|neg_kernel"
 KERNELS = ("rs_local_kernel", "ag_copyout_kernel", "ag_copyin_kernel", "stock_pack_kernel")
 COUNTER_PASSES = {
     "fetch": ["FETCH_SIZE"],
     "write": ["WRITE_SIZE"],
+    "dram": ["TCC_EA0_RDREQ_DRAM_32B", "TCC_EA0_WRREQ_WRITE_DRAM_32B"],
+    "stall": ["TCC_EA0_RDREQ_DRAM_CREDIT_STALL", "TCC_EA0_WRREQ_DRAM_CREDIT_STALL", "TCC_EA0_RDREQ_LEVEL",
+              "TCC_EA0_RDREQ", "GRBM_GUI_ACTIVE"],
 }
+COUNTER_MODES = ("rs", "co", "ci", "stock", "torch")
+# L2 channels per XCD and XCDs: the TCC counters are summed over all 128
+# channels, GRBM_GUI_ACTIVE over the 8 XCDs
+TCC_CHANNELS = 16 * 8
+XCDS = 8
 
 
 def _portable(cmd_text, out_root=None):
@@ -54,8 +75,13 @@ def _portable(cmd_text, out_root=None):
 
 
 def source_digest():
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """SHA-256 over the sources that decide the kernels' memory traffic: the
+    kernels and the planner that lays out their segments and vector bodies."""
+    h = hashlib.sha256()
+    for path in TRAFFIC_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def _run(cmd, log):
@@ -102,10 +128,11 @@ def collect_trace(workload, out, steps=TRACE_STEPS):
 def collect_counters(workload, out, launches=COUNTER_LAUNCHES):
     os.makedirs(out, exist_ok=True)
     cmds = {}
-    for only in ("rs", "co", "ci", "calib", "stock"):
+    for only in COUNTER_MODES:
         for name, counters in COUNTER_PASSES.items():
             d = os.path.join(out, f"pmc_{only}_{name}")
-            cmd = ["rocprofv3", "--pmc", *counters, "--kernel-include-regex", KERNEL_REGEX, "-f", "csv", "-d", d,
+            regex = TORCH_REGEX if only == "torch" else KERNEL_REGEX
+            cmd = ["rocprofv3", "--pmc", *counters, "--kernel-include-regex", regex, "-f", "csv", "-d", d,
                    "-o", "pmc", "--", *bench_cmd(workload, ["--only", only, "--launches", str(launches)])]
             _run(cmd, d + ".log")
             cmds[f"{only}_{name}"] = _portable(" ".join(shlex.quote(c) for c in cmd), out)
@@ -168,7 +195,7 @@ def summarize(workload, out, profiles):
     digest = source_digest()
     # kernel traces: the timed step (+ copy-in), then the stock path alone,
     # whose reduce-scatter is the fp32 instance of rs_local_kernel
-    lines = [f"# rocprofv3 kernel trace: {workload}", "", f"kernel source sha256: {digest}"]
+    lines = [f"# rocprofv3 kernel trace: {workload}", "", f"kernels.hip + plan.cpp sha256: {digest}"]
     any_stats = False
     for run, title in (("trace", "timed step (reduce-scatter from bf16 gradients, copy-out) and copy-in"),
                        ("trace_stock", "stock path: W stock packs, then the reduce-scatter of the W packed fp32 "
@@ -205,31 +232,38 @@ def summarize(workload, out, profiles):
             f.write("\n".join(lines) + "\n")
     # counters
     cdir = out
-    if not os.path.isdir(os.path.join(cdir, "pmc_calib_fetch")):
+    if not os.path.isdir(os.path.join(cdir, "pmc_torch_fetch")):
         return
     cmds = {k: _normalise(v) for k, v in json.load(open(os.path.join(cdir, "counters.cmd.json"))).items()}
 
-    def med(only, name, counter, kernel, calls=COUNTER_LAUNCHES):
-        """KiB of one operation call: the counter summed over every dispatch
-        of the kernel, divided by the operation calls made."""
+    def total(only, name, counter, kernel, calls=COUNTER_LAUNCHES):
+        """One operation call's worth of a counter: summed over every
+        dispatch of the kernel, divided by the operation calls made."""
         vals = [v for n, v in _read_counter(os.path.join(cdir, f"pmc_{only}_{name}"), counter) if kernel in n]
         return sum(vals) / calls if vals else None
 
     import synth
+    from param_collectives_amd import tide
 
     w = synth.workload(workload)
-    sum_dk = sum(w.numel(p) for p in range(w.nparams))
-    R = [-(-s[0] // w.world) for s in w.shapes]
-    K = [w.numel(p) // s[0] if s[0] else 0 for p, s in enumerate(w.shapes)]
-    S = sum(r * k for r, k in zip(R, K))
-    calib_bytes = 2 * w.world * S  # the calibration copy moves W*S bf16 each way
-    cf = med("calib", "fetch", "FETCH_SIZE", "ag_copyout")
-    cw = med("calib", "write", "WRITE_SIZE", "ag_copyout")
-    cal = {"kernel": "ag_copyout_kernel on one flat tensor of W*S bf16", "bytes_read": calib_bytes,
-           "bytes_written": calib_bytes, "fetch_kib": cf, "write_kib": cw,
-           "fetch_factor": calib_bytes / (cf * 1024.0), "write_factor": calib_bytes / (cw * 1024.0)}
-    kernels = {}
     W = w.world
+    plan = tide.Plan(W, w.shapes)
+    sum_dk = sum(plan.numel)
+    S = plan.shard_elems
+    known = 2 * W * S  # bytes each calibration stream reads and/or writes
+    nf, nw = total("torch", "fetch", "FETCH_SIZE", "neg_kernel"), total("torch", "write", "WRITE_SIZE", "neg_kernel")
+    cal = {"kernel": "PyTorch's elementwise neg over W*S bf16 (one read and one write per element)",
+           "bytes_read": known, "bytes_written": known, "fetch_kib": nf, "write_kib": nw,
+           "fetch_factor": known / (nf * 1024.0), "write_factor": known / (nw * 1024.0)}
+    checks = {}
+    for label, kern, alg_r, alg_w in (("torch_neg", "neg_kernel", known, known),
+                                      ("torch_fill", "FillFunctor", 0, known)):
+        rd = total("torch", "dram", "TCC_EA0_RDREQ_DRAM_32B", kern)
+        wd = total("torch", "dram", "TCC_EA0_WRREQ_WRITE_DRAM_32B", kern)
+        if rd is not None and wd is not None:
+            checks[label] = {"dram_read_bytes": 32.0 * rd, "dram_write_bytes": 32.0 * wd,
+                             "algorithmic_read_bytes": alg_r, "algorithmic_write_bytes": alg_w}
+    kernels = {}
     for only, kname, key, alg_r, alg_w in (("rs", "rs_local", "rs_local", 2 * W * sum_dk, 4 * W * S),
                                            ("co", "ag_copyout", "ag_copyout", 2 * sum_dk, 2 * sum_dk),
                                            ("ci", "ag_copyin", "ag_copyin", 4 * sum_dk, 2 * W * S),
@@ -239,16 +273,30 @@ def summarize(workload, out, profiles):
         if not os.path.isdir(os.path.join(cdir, f"pmc_{only}_fetch")):
             continue
         calls = COUNTER_LAUNCHES * (W if kname == "stock_pack_kernel" else 1)
-        f = med(only, "fetch", "FETCH_SIZE", kname, calls)
-        wr = med(only, "write", "WRITE_SIZE", kname, calls)
+        f = total(only, "fetch", "FETCH_SIZE", kname, calls)
+        wr = total(only, "write", "WRITE_SIZE", kname, calls)
         if f is None or wr is None:
             continue
         traffic_r = f * 1024.0 * cal["fetch_factor"]
         traffic_w = wr * 1024.0 * cal["write_factor"]
-        kernels[f"{key}/{workload}"] = {
-            "fetch_kib": f, "write_kib": wr, "hbm_read_bytes": traffic_r, "hbm_write_bytes": traffic_w,
-            "algorithmic_read_bytes": alg_r, "algorithmic_write_bytes": alg_w,
-            "read_ratio": traffic_r / alg_r, "write_ratio": traffic_w / alg_w}
+        k = {"fetch_kib": f, "write_kib": wr, "hbm_read_bytes": traffic_r, "hbm_write_bytes": traffic_w,
+             "algorithmic_read_bytes": alg_r, "algorithmic_write_bytes": alg_w,
+             "read_ratio": traffic_r / alg_r, "write_ratio": traffic_w / alg_w}
+        rd = total(only, "dram", "TCC_EA0_RDREQ_DRAM_32B", kname, calls)
+        wd = total(only, "dram", "TCC_EA0_WRREQ_WRITE_DRAM_32B", kname, calls)
+        if rd is not None and wd is not None:
+            k.update({"dram_read_bytes": 32.0 * rd, "dram_write_bytes": 32.0 * wd,
+                      "dram_read_ratio": 32.0 * rd / alg_r, "dram_write_ratio": 32.0 * wd / alg_w})
+        st = {c: total(only, "stall", c, kname, calls) for c in COUNTER_PASSES["stall"]}
+        if all(v is not None for v in st.values()) and st["GRBM_GUI_ACTIVE"]:
+            cycles = st["GRBM_GUI_ACTIVE"] / XCDS  # per XCD, over the call
+            k.update({
+                "busy_cycles": cycles,
+                "read_credit_stall_frac": st["TCC_EA0_RDREQ_DRAM_CREDIT_STALL"] / (TCC_CHANNELS * cycles),
+                "write_credit_stall_frac": st["TCC_EA0_WRREQ_DRAM_CREDIT_STALL"] / (TCC_CHANNELS * cycles),
+                "read_latency_cycles": st["TCC_EA0_RDREQ_LEVEL"] / st["TCC_EA0_RDREQ"],
+                "reads_in_flight": st["TCC_EA0_RDREQ_LEVEL"] / cycles})
+        kernels[f"{key}/{workload}"] = k
     path = os.path.join(profiles, "hbm_traffic.json")
     try:
         t = json.load(open(path))
@@ -258,19 +306,33 @@ def summarize(workload, out, profiles):
         t = {}
     t["source_sha256"] = digest
     t["calibration"] = cal
+    t.setdefault("calibration_checks", {}).update({f"{k}/{workload}": v for k, v in checks.items()})
     t.setdefault("kernels", {}).update(kernels)
     t.setdefault("commands", {})[workload] = cmds
     with open(path, "w") as fo:
         json.dump(t, fo, indent=1, sort_keys=True)
-    txt = [f"# HBM traffic per dispatch from rocprofv3 counters: {workload}", "",
-           f"kernel source sha256: {digest}", "",
-           "calibration (plain copy of known size, copy-out kernel on one flat tensor):",
-           f"  {calib_bytes} B each way; FETCH_SIZE {cf:.0f} KiB, WRITE_SIZE {cw:.0f} KiB;"
-           f" factors read {cal['fetch_factor']:.4f}, write {cal['write_factor']:.4f}", ""]
+    txt = [f"# HBM traffic per operation call from rocprofv3 counters: {workload}", "",
+           f"kernels.hip + plan.cpp sha256: {digest}", "",
+           "calibration (a plain stream of known size outside this library: PyTorch's elementwise neg):",
+           f"  {known} B each way; FETCH_SIZE {nf:.0f} KiB, WRITE_SIZE {nw:.0f} KiB;"
+           f" factors read {cal['fetch_factor']:.4f}, write {cal['write_factor']:.4f}"]
+    for label, v in checks.items():
+        txt.append(f"  {label}: DRAM read {v['dram_read_bytes'] / 1e9:.4f} GB, DRAM write "
+                   f"{v['dram_write_bytes'] / 1e9:.4f} GB (known: {v['algorithmic_read_bytes'] / 1e9:.4f} GB read, "
+                   f"{v['algorithmic_write_bytes'] / 1e9:.4f} GB written)")
+    txt += ["", "per kernel: FETCH_SIZE/WRITE_SIZE scaled by the factors | DRAM bytes from the 32-byte request "
+                "counters (no factor) | cycles waiting for DRAM credits (read, write; fraction of L2-channel "
+                "cycles) | mean read latency (cycles) and reads in flight"]
     for k, v in kernels.items():
-        txt.append(f"{k}: FETCH_SIZE {v['fetch_kib']:.0f} KiB, WRITE_SIZE {v['write_kib']:.0f} KiB -> "
-                   f"read {v['hbm_read_bytes'] / 1e9:.4f} GB ({v['read_ratio']:.3f} x algorithmic), "
-                   f"write {v['hbm_write_bytes'] / 1e9:.4f} GB ({v['write_ratio']:.3f} x algorithmic)")
+        line = (f"{k}: read {v['hbm_read_bytes'] / 1e9:.4f} GB ({v['read_ratio']:.3f} x algorithmic), "
+                f"write {v['hbm_write_bytes'] / 1e9:.4f} GB ({v['write_ratio']:.3f} x)")
+        if "dram_read_bytes" in v:
+            line += (f" | DRAM read {v['dram_read_bytes'] / 1e9:.4f} GB ({v['dram_read_ratio']:.4f} x), "
+                     f"write {v['dram_write_bytes'] / 1e9:.4f} GB ({v['dram_write_ratio']:.4f} x)")
+        if "read_latency_cycles" in v:
+            line += (f" | credit stalls {v['read_credit_stall_frac']:.3f}, {v['write_credit_stall_frac']:.3f}"
+                     f" | read latency {v['read_latency_cycles']:.0f}, in flight {v['reads_in_flight']:.0f}")
+        txt.append(line)
     txt += ["", "commands (each run in /tmp; <repo> is the repository root, <out> the output folder):"]
     txt += [f"  {k}: {c}" for k, c in sorted(cmds.items())]
     with open(os.path.join(profiles, f"hbm_traffic_{workload}.txt"), "w") as f:

@@ -46,8 +46,9 @@ def test_bench_line(capsys):
     assert r["achieved"] == pytest.approx(k["rs_local"]["gbps"], rel=1e-3)
     assert r["frac"] == pytest.approx(r["achieved"] / r["peak"], abs=1e-4)
     assert 0 < r["frac"] < 1
-    if r["traffic"] is not None:  # counters committed for this kernel source
-        assert r["traffic"] == pytest.approx(rs_bytes, rel=0.05)
+    for key in ("traffic", "traffic_dram"):  # counters committed for this kernel source
+        if r[key] is not None:
+            assert r[key] == pytest.approx(rs_bytes, rel=0.05)
 
     c = d["cpu_baseline"]
     assert c["kind"] == "oracle" and c["unit"] == "GB/s" and c["value"] > 0 and c["cores"] >= 1
