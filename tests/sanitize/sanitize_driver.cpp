@@ -213,7 +213,10 @@ void check_case(const Case& c, Rng& r, int idx) {
   expect(hdr.size() == rs.size() && ptrs.size() == rs.size() * size_t(W + 1), tag + ": call table size");
   for (size_t s = 0; s < rs.size() && s < hdr.size(); ++s) {
     const auto& sg = rs[s];
-    expect(hdr[s].len == sg.len && hdr[s].kind == sg.kind && hdr[s].head <= 8 * 4, tag + ": call header");
+    expect(hdr[s].len == sg.len && hdr[s].kind == sg.kind && hdr[s].head < 4, tag + ": call header");
+    if (hdr[s].head >= 0 && hdr[s].head < sg.len)  // the vector body starts where the destination is 16-byte aligned
+      expect(((reinterpret_cast<uintptr_t>(ptrs[s * (W + 1) + W]) + uintptr_t(hdr[s].head) * 4) & 15) == 0,
+             tag + ": vector body on a 16-byte destination boundary");
     const uintptr_t d = reinterpret_cast<uintptr_t>(ptrs[s * (W + 1) + W]);
     const uintptr_t d0 = reinterpret_cast<uintptr_t>(outp[sg.dst_idx]);
     expect(d >= d0 && d + uintptr_t(sg.len) * 4 <= d0 + uintptr_t(S) * 4, tag + ": destination pointer range");
