@@ -28,6 +28,15 @@ inside the aggressor's run count), the slowdown, the aggressor's own time
 alone and beside the victim, and its CU-ms per call (CUs held x time), the
 analog of the pages' SM-ms per call.
 
+Per call (Table 4's own measure, --per-call): the victim runs back to back on
+its stream, and one aggressor call is released in the middle of that sequence
+(the aggressor's stream waits for an event recorded after a fixed number of
+victim launches).  The penalty of the call is the victims' extra time against
+the same sequence without it; dividing it by the aggressor call's duration
+gives the slowdown of the victim work that overlapped the call.  Configurations
+add a disjoint split (the aggressor masked to 16 CUs, the victim to the other
+240) and report the victim's own cost of that split.
+
 Probe (Table 5's analog): 256 probe workgroups, each claiming a CU's whole LDS
 and holding it 200 us, launched repeatedly during an aggressor's run: a
 workgroup that starts after the first of them leaves was displaced.  Reported:
@@ -196,6 +205,87 @@ class Study:
             counts.append(int((d["entry"] >= d["exit"].min()).sum()))
         return counts
 
+    def per_call(self, agg_fn, agg_stream, vic_fn, vic_stream, t_vic, t_agg, reps=5, before=10):
+        """One aggressor call released after `before` victim launches of a
+        back-to-back victim sequence; returns per repetition (victim ms of the
+        sequence with the call, without it, the call's own ms, victim launches
+        that ran while the call did)."""
+        torch = self.torch
+        n = before + max(20, math.ceil(6.0 * t_agg / max(t_vic, 1e-3))) + 10
+        out = []
+        for _ in range(reps):
+            row = []
+            for with_call in (False, True):
+                torch.cuda.synchronize()
+                marks = [(self.ev(), self.ev()) for _ in range(n)]
+                go = torch.cuda.Event()
+                c0, c1 = self.ev(), self.ev()
+                for i, (a, b) in enumerate(marks):
+                    a.record(vic_stream)
+                    vic_fn(vic_stream)
+                    b.record(vic_stream)
+                    if i == before - 1:
+                        go.record(vic_stream)
+                if with_call:
+                    agg_stream.wait_event(go)
+                    c0.record(agg_stream)
+                    agg_fn(agg_stream)
+                    c1.record(agg_stream)
+                torch.cuda.synchronize()
+                total = sum(a.elapsed_time(b) for a, b in marks)
+                if with_call:
+                    call = c0.elapsed_time(c1)
+                    start, end = marks[0][0].elapsed_time(c0), marks[0][0].elapsed_time(c1)
+                    overlap = sum(1 for a, b in marks
+                                  if marks[0][0].elapsed_time(b) > start and marks[0][0].elapsed_time(a) < end)
+                    row += [total, call, overlap]
+                else:
+                    row.append(total)
+            base, total, call, overlap = row
+            out.append((total, base, call, overlap))
+        return out
+
+    def run_per_call(self, configs, victims):
+        torch, tide = self.torch, self.tide
+        cus = self.info["cu_count"]
+        results = {"device": self.info, "workload": self.w.name, "rs_bytes": self.rs_bytes, "victims": {},
+                   "aggressors": []}
+        vic = {name: self.victim(name) for name in victims}
+        full = self.stream_v.torch
+        rest = tide.Stream(cus=range(16, cus))  # the victim's side of the disjoint split
+        for name, fn in vic.items():
+            t = _median(self.time_alone(fn, full))
+            t_rest = _median(self.time_alone(fn, rest.torch))
+            results["victims"][name] = {"alone_p50_ms": round(t, 5), "alone_on_240_cus_p50_ms": round(t_rest, 5)}
+        for label, kw in configs:
+            disjoint = kw.pop("disjoint", False)
+            fn, stream, held = self.aggressor(**kw)
+            kw["disjoint"] = disjoint
+            t_agg = _median(self.time_alone(fn, stream.torch))
+            row = {"aggressor": label, "cus_held": held, "alone_ms": round(t_agg, 5)}
+            for name, vfn in vic.items():
+                vs = rest.torch if disjoint else full
+                t_vic = results["victims"][name]["alone_on_240_cus_p50_ms" if disjoint else "alone_p50_ms"]
+                reps = self.per_call(fn, stream.torch, vfn, vs, t_vic, t_agg)
+                pen = [t - b for t, b, _, _ in reps]
+                call = [c for _, _, c, _ in reps]
+                p = _median(pen)
+                c = _median(call)
+                row[name] = {"penalty_ms": round(p, 5), "call_ms_beside": round(c, 5),
+                             "overlap_slowdown_pct": round(100.0 * p / c, 2) if c > 0 else None,
+                             "victims_overlapped": int(_median([o for _, _, _, o in reps])),
+                             "penalty_ms_min": round(min(pen), 5), "penalty_ms_max": round(max(pen), 5)}
+                if disjoint:
+                    # what the split itself costs the victim: 240 CUs instead of 256
+                    row[name]["split_cost_pct"] = round(
+                        100.0 * (t_vic / results["victims"][name]["alone_p50_ms"] - 1.0), 2)
+            results["aggressors"].append(row)
+            print(json.dumps(row), flush=True)
+            stream.destroy()
+            torch.cuda.synchronize()
+        rest.destroy()
+        return results
+
     # ---------------------------------------------------------------- study
 
     def run(self, configs, victims):
@@ -251,6 +341,42 @@ DEFAULT_CONFIGS = [
 ]
 
 
+PER_CALL_CONFIGS = [
+    ("tide-rs grid=256", dict(kind="tide")),
+    ("tide-rs grid=64", dict(kind="tide", budget=64)),
+    ("tide-rs grid=16", dict(kind="tide", budget=16)),
+    ("tide-rs mask=16", dict(kind="tide", budget=16, masked=True)),
+    ("tide-rs noLDS grid=16", dict(kind="tide", budget=16, no_lds=True)),
+    ("tide-rs noLDS mask=16", dict(kind="tide", budget=16, masked=True, no_lds=True)),
+    ("tide-rs disjoint 16|240", dict(kind="tide", budget=16, masked=True, no_lds=True, disjoint=True)),
+    ("stock pack+reduce", dict(kind="stock")),
+    ("tide copy-out", dict(kind="copyout")),
+]
+
+
+def per_call_text(res, command):
+    lines = [f"# Interference per call: {res['workload']} on one MI355X", "",
+             f"command: {command}", f"device: {res['device']}", "",
+             "victim p50 latency alone: " + ", ".join(
+                 f"{k} {v['alone_p50_ms']:.4f} ms (on 240 CUs {v['alone_on_240_cus_p50_ms']:.4f} ms)"
+                 for k, v in res["victims"].items()), "",
+             "one aggressor call released in a back-to-back victim sequence: the victims' extra time (penalty, "
+             "median of 5), the call's duration beside them, and penalty / call duration (the slowdown of the "
+             "victim work the call overlapped); the disjoint split runs the victims on 240 CUs, the call on the "
+             "other 16"]
+    vics = list(res["victims"])
+    head = f"{'aggressor':<26} {'CUs':>4} {'alone ms':>9} " + " ".join(
+        f"{v[:18] + ' pen ms':>26} {'call ms':>8} {'overlap %':>9}" for v in vics)
+    lines.append(head)
+    for r in res["aggressors"]:
+        cells = []
+        for v in vics:
+            x = r[v]
+            cells.append(f"{x['penalty_ms']:>26.4f} {x['call_ms_beside']:>8.4f} {x['overlap_slowdown_pct']!s:>9}")
+        lines.append(f"{r['aggressor']:<26} {r['cus_held']:>4} {r['alone_ms']:>9.4f} " + " ".join(cells))
+    return "\n".join(lines) + "\n"
+
+
 def summary_text(res, command):
     lines = [f"# Interference study: {res['workload']} on one MI355X", "",
              f"command: {command}", f"device: {res['device']}", "",
@@ -274,10 +400,25 @@ def main(argv=None):
     ap.add_argument("--out", required=True, help="folder for the JSON result")
     ap.add_argument("--profiles", default=None, help="also write the text summary here")
     ap.add_argument("--victims", default="elementwise," + ",".join(GEMMS))
+    ap.add_argument("--per-call", action="store_true", help="one aggressor call inside a victim sequence")
     args = ap.parse_args(argv)
     if ROOT not in sys.path:
         sys.path.insert(0, ROOT)
     study = Study(args.workload)
+    if args.per_call:
+        victims = [v for v in args.victims.split(",") if v != "gemm_8192x8192x8192"]
+        res = study.run_per_call(PER_CALL_CONFIGS, victims)
+        os.makedirs(args.out, exist_ok=True)
+        with open(os.path.join(args.out, f"interference_per_call_{args.workload}.json"), "w") as f:
+            json.dump(res, f, indent=1)
+        cmd = f"python -m param_collectives_amd.interference --per-call --workload {args.workload} --out <out>"
+        text = per_call_text(res, cmd)
+        print(text, flush=True)
+        if args.profiles:
+            os.makedirs(args.profiles, exist_ok=True)
+            with open(os.path.join(args.profiles, f"interference_per_call_{args.workload}.txt"), "w") as f:
+                f.write(text)
+        return
     res = study.run(DEFAULT_CONFIGS, args.victims.split(","))
     os.makedirs(args.out, exist_ok=True)
     with open(os.path.join(args.out, f"interference_{args.workload}.json"), "w") as f:
