@@ -566,6 +566,8 @@ def main(argv=None):
         "d2d_copy": d2d,
         "flat_copy": flat,
         "parity": parity,
+        # elements per code path in the timed calls (vector, realigned, one by one)
+        "paths": {"rs_local": plan.paths(0), "ag_copyout": plan.paths(1)},
         "stock_ab": stock_ab,
         "host_enqueue_us": host_us,
     }

@@ -213,6 +213,25 @@ tide_status tide_plan_segments(const tide_plan* plan, int32_t op, int64_t* table
 tide_status tide_plan_launches(const tide_plan* plan, int32_t op, int32_t cu_count, int64_t* table,
                                int64_t capacity, int64_t* count);
 
+/*
+ * Which code path the elements of the latest call of `op` take, for spotting a
+ * slow layout at run time (host only).  The latest call's pointers decide it:
+ * a segment's vector body starts where its destination is aligned to the
+ * vector group; the source may sit at another phase there.
+ *   out[0]  elements moved by aligned vector bodies
+ *   out[1]  elements moved by realigned vector bodies (the source at another
+ *           phase than the destination; every operation but the stock pack
+ *           realigns in registers, the reduce-scatter only when out[3] is 1)
+ *   out[2]  elements moved one by one: heads and tails of segments, segments
+ *           whose W sources sit at different phases, and the reduce-scatter's
+ *           off-phase bodies when out[3] is 0
+ *   out[3]  reduce-scatter only: 1 when the call runs the realigning instance
+ *           (off-phase sum segments hold more than 1/50 of its elements)
+ * out[0] + out[1] + out[2] is the elements the operation writes.
+ * Errors: TIDE_ERR_INVALID (bad plan, op or out; no call of `op` made yet).
+ */
+tide_status tide_plan_paths(const tide_plan* plan, int32_t op, int64_t* out);
+
 /* Replace the launch knobs (NULL = defaults).  Results are unaffected.
  * Errors: TIDE_ERR_INVALID, TIDE_ERR_RANGE (too many chunks). */
 tide_status tide_plan_set_options(tide_plan* plan, const tide_options* opt);

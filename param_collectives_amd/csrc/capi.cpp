@@ -664,6 +664,62 @@ tide_status tide_plan_launches(const tide_plan* plan, int32_t op, int32_t cu_cou
   });
 }
 
+tide_status tide_plan_paths(const tide_plan* plan, int32_t op, int64_t* out) {
+  return tide::guarded([&]() -> tide_status {
+    g_last_error.clear();
+    if (!live(plan)) return fail(TIDE_ERR_INVALID, "unknown or destroyed plan");
+    if (op < 0 || op >= tide::kNumOps) return fail(TIDE_ERR_INVALID, std::string("op must be ") + kOpNames);
+    if (out == nullptr) return fail(TIDE_ERR_INVALID, "out must not be NULL");
+    const OpState& s = op_state(plan, tide::Op(op));
+    if (!s.key_valid)
+      return fail(TIDE_ERR_INVALID, "no call of this operation has been made with the plan yet");
+    const bool rs = op == tide::kOpRs || op == tide::kOpRsF32;
+    const int32_t nsrc = nsrc_of(plan, tide::Op(op));
+    int64_t vec = 0, shifted = 0, elem = 0;
+    for (size_t i = 0; i < s.hdr.size(); ++i) {
+      const tide::CallHdr& h = s.hdr[i];
+      const void* src = s.ptrs[i * size_t(nsrc + 1)];
+      // the kernels' vector group (elements) and source element size for this segment
+      int64_t group = 4, esize = 0, salign = 16;
+      switch (op) {
+        case tide::kOpRs: esize = 2; salign = 8; break;
+        case tide::kOpRsF32: esize = 4; break;
+        case tide::kOpCo: group = 8; esize = 2; break;
+        case tide::kOpCi:
+          if (h.kind == tide::kCast) {
+            esize = 4;
+          } else {
+            group = 8;
+            esize = 2;
+          }
+          break;
+        default: break;  // stock pack: the body starts where source and destination are both aligned
+      }
+      if (h.kind == tide::kZero || src == nullptr) esize = 0;
+      if (h.head < 0 || h.len <= h.head) {
+        elem += h.len;
+        continue;
+      }
+      const int64_t body = (h.len - h.head) / group * group;
+      elem += h.len - body;
+      const bool off = esize > 0 && ((reinterpret_cast<uintptr_t>(src) + uintptr_t(h.head * esize)) &
+                                     uintptr_t(salign - 1)) != 0;
+      if (!off) {
+        vec += body;
+      } else if (!rs || s.has_shift) {
+        shifted += body;
+      } else {
+        elem += body;  // the plain reduce-scatter instances take an off-phase body element by element
+      }
+    }
+    out[0] = vec;
+    out[1] = shifted;
+    out[2] = elem;
+    out[3] = rs && s.has_shift ? 1 : 0;
+    return TIDE_OK;
+  });
+}
+
 tide_status tide_plan_set_options(tide_plan* plan, const tide_options* opt) {
   return tide::guarded([&]() -> tide_status {
     g_last_error.clear();

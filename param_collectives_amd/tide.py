@@ -48,6 +48,7 @@ EXPORTS = (
     "tide_plan_set_options",
     "tide_plan_get_options",
     "tide_plan_launches",
+    "tide_plan_paths",
     "tide_reduce_scatter_local",
     "tide_reduce_scatter_local_noalloc",
     "tide_allgather_copyout",
@@ -89,6 +90,7 @@ def _load():
     lib.tide_plan_set_options.argtypes = [vp, ctypes.POINTER(Options)]
     lib.tide_plan_get_options.argtypes = [vp, i32, ctypes.POINTER(Options)]
     lib.tide_plan_launches.argtypes = [vp, i32, i32, i64p, i64, i64p]
+    lib.tide_plan_paths.argtypes = [vp, i32, i64p]
     lib.tide_reduce_scatter_local.argtypes = [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.c_float, i32, vp]
     lib.tide_allgather_copyout.argtypes = [vp, vp, ctypes.POINTER(vp), vp]
     lib.tide_allgather_copyin.argtypes = [vp, ctypes.POINTER(vp), i32, vp, vp]
@@ -180,6 +182,15 @@ class Plan:
                                       table.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), count.value,
                                       ctypes.byref(count)))
         return table[:count.value]
+
+    def paths(self, op=0):
+        """Elements of the latest call of `op` by code path (tide_plan_paths):
+        dict of vector, realigned and element-by-element counts, and whether a
+        reduce-scatter ran its realigning instance."""
+        out = np.zeros(4, dtype=np.int64)
+        _check(lib.tide_plan_paths(self.handle, int(op), out.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))))
+        return {"vector": int(out[0]), "realigned": int(out[1]), "element": int(out[2]),
+                "realigning_instance": bool(out[3])}
 
     def set_options(self, cu_budget=0, wg_per_cu=0, chunk_elems=0, flags=0, wave_chunks=0):
         opt = _options(cu_budget, wg_per_cu, chunk_elems, flags, wave_chunks)

@@ -54,3 +54,7 @@ def test_bench_line(capsys):
     assert c["kind"] == "oracle" and c["unit"] == "GB/s" and c["value"] > 0 and c["cores"] >= 1
     assert c["single_thread_matches"] is True and c["sample"]
     assert d["parity"] == {"rs_local": "bit-exact", "ag_copyout": "bit-exact"}
+    # the layer's tensors are aligned: every element of both timed operations takes a vector body
+    assert d["paths"]["rs_local"] == {"vector": 8 * cfg["shard_elems"], "realigned": 0, "element": 0,
+                                      "realigning_instance": False}
+    assert d["paths"]["ag_copyout"]["vector"] == cfg["elements"]

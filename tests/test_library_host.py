@@ -541,3 +541,17 @@ def test_probe_record_decoding(tide):
     assert (d["block"][0], d["wave"][0], d["simd"][0], d["cu"][0], d["sh"][0], d["se"][0], d["xcc"][0]) == \
         (7, 5, 2, 11, 1, 3, 6)
     assert d["ok"][0] and d["entry"][0] == 2**33 - 1 and d["exit"][0] == 2**33 + 5
+
+
+def test_paths_need_a_call_first(tide):
+    """tide_plan_paths reports the latest call's tables: before any call it is
+    an argument error (host only), as are a bad op and a null output."""
+    import ctypes
+
+    plan = tide.Plan(4, [(8, 3)])
+    out = (ctypes.c_int64 * 4)()
+    assert tide.lib.tide_plan_paths(plan.handle, 0, out) == -1
+    assert "no call" in tide.lib.tide_last_error().decode()
+    assert tide.lib.tide_plan_paths(plan.handle, 5, out) == -1
+    assert tide.lib.tide_plan_paths(plan.handle, 0, None) == -1
+    assert tide.lib.tide_plan_paths(None, 0, out) == -1
