@@ -3,6 +3,9 @@
   Plan                   host shard-layout plan (dimension-0 shards, padding)
   reduce_scatter_local   W ranks' bf16 (or fp32) gradients -> W packed fp32
                          shards (with Equation 5's alpha and accumulate)
+  reduce_scatter_local_noalloc
+                         the same from bf16 gradients, allocating nothing
+                         (tables in a fixed device scratch array)
   allgather_copyout      rank-major bf16 buffer -> per-parameter tensors
   allgather_copyin       every rank's fp32/bf16 shards -> rank-major bf16 buffer
   stock_chunk_cat        stock FSDP2's gradient pack of one rank (the baseline)
@@ -31,6 +34,7 @@ from .tide import (  # noqa: F401
     allgather_copyout_call,
     reduce_scatter_call,
     reduce_scatter_local,
+    reduce_scatter_local_noalloc,
     stock_chunk_cat,
     stock_chunk_cat_call,
     Stream,
