@@ -370,32 +370,6 @@ def main(argv=None):
 
     kernels = {"rs_local": kstats(rs_ms, rs_bytes), "ag_copyout": kstats(co_ms, co_bytes)}
 
-    # CU-budget sweep: each kernel confined to `budget` CUs by a CU-masked
-    # stream (a hard budget), with one workgroup (4 waves, the default) and
-    # four workgroups (16 waves) per CU; results are bit-identical by design
-    sweep = []
-    if not args.no_sweep:
-        for budget in (8, 16, 32, 64, 128, 256):
-            masked = tide.Stream(cus=range(budget))
-            for wg in (1, 4):
-                plan.set_options(**dict(opts, cu_budget=budget, wg_per_cu=wg))
-                row = {"cu_budget": budget, "wg_per_cu": wg, "cu_masked": True}
-                for name, call, nbytes in (("rs_local", rs_call, rs_bytes), ("ag_copyout", co_call, co_bytes)):
-                    ms_ = masked.torch
-                    call(ms_)
-                    e = [(ev(), ev()) for _ in range(10)]
-                    for a, b in e:
-                        a.record(ms_)
-                        call(ms_)
-                        b.record(ms_)
-                    ms_.synchronize()
-                    avg = sum(a.elapsed_time(b) for a, b in e) / len(e)
-                    row[name] = {"avg_ms": round(avg, 5), "gbps": round(nbytes / avg / 1e6, 1),
-                                 "gbps_per_cu": round(nbytes / avg / 1e6 / budget, 2)}
-                sweep.append(row)
-            masked.destroy()
-        plan.set_options(**opts)
-
     # the all-gather copy-in (fp32 master shards of every rank -> rank-major
     # bf16, cast fused), measured beside the step: 4*sum(D*K) read, 2*W*S written
     ci_bytes = 4 * sum_dk + 2 * W * S
@@ -407,7 +381,8 @@ def main(argv=None):
                    for m, s, R in zip(masters, w.shapes, plan.rows_per_rank)] for r in range(W)]
         ci_out = torch.empty(W * S, dtype=torch.bfloat16, device="cuda")
         ci_call = tide.allgather_copyin_call(plan, shards, ci_out)
-        ci_call(stream)
+        for _ in range(3):
+            ci_call(stream)
         e = [(ev(), ev()) for _ in range(10)]
         for a, b_ in e:
             a.record(stream)
@@ -525,6 +500,34 @@ def main(argv=None):
         flat = kstats([a.elapsed_time(b) for a, b in e], co_bytes)
         flat["copyout_over_flat"] = round(flat["avg_ms"] / kernels["ag_copyout"]["avg_ms"], 4)
         del fsrc, fdst, fplan, fcall
+
+    # CU-budget sweep, after every full-GPU measurement (its small budgets
+    # leave the GPU lightly loaded, and the next kernels would start while its
+    # clocks come back up): each kernel confined to `budget` CUs by a CU-masked
+    # stream (a hard budget), with one workgroup (4 waves, the default) and
+    # four workgroups (16 waves) per CU; results are bit-identical by design
+    sweep = []
+    if not args.no_sweep:
+        for budget in (8, 16, 32, 64, 128, 256):
+            masked = tide.Stream(cus=range(budget))
+            for wg in (1, 4):
+                plan.set_options(**dict(opts, cu_budget=budget, wg_per_cu=wg))
+                row = {"cu_budget": budget, "wg_per_cu": wg, "cu_masked": True}
+                for name, call, nbytes in (("rs_local", rs_call, rs_bytes), ("ag_copyout", co_call, co_bytes)):
+                    ms_ = masked.torch
+                    call(ms_)
+                    e = [(ev(), ev()) for _ in range(10)]
+                    for a, b in e:
+                        a.record(ms_)
+                        call(ms_)
+                        b.record(ms_)
+                    ms_.synchronize()
+                    avg = sum(a.elapsed_time(b) for a, b in e) / len(e)
+                    row[name] = {"avg_ms": round(avg, 5), "gbps": round(nbytes / avg / 1e6, 1),
+                                 "gbps_per_cu": round(nbytes / avg / 1e6 / budget, 2)}
+                sweep.append(row)
+            masked.destroy()
+        plan.set_options(**opts)
 
     # CPU oracle on the same workload, streamed in groups of parameters, and a
     # bitwise check of this run's outputs against it

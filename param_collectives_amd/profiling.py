@@ -104,11 +104,11 @@ COUNTER_LAUNCHES = 3
 
 def trace_op_calls(run, kernel, world):
     """Operation calls each trace run makes of a kernel (bench.py: warm-up 2 +
-    timed steps of the reduce-scatter and copy-out, one untimed + 10 timed
+    timed steps of the reduce-scatter and copy-out, three untimed + 10 timed
     copy-ins; the stock run: W packs and one reduce per launch).  An operation
     call may be several dispatches (long operations are split)."""
     calls = {("trace", "rs_local_kernel"): TRACE_STEPS + 2, ("trace", "ag_copyout_kernel"): TRACE_STEPS + 2,
-             ("trace", "ag_copyin_kernel"): 11, ("trace_stock", "stock_pack_kernel"): TRACE_STEPS * world,
+             ("trace", "ag_copyin_kernel"): 13, ("trace_stock", "stock_pack_kernel"): TRACE_STEPS * world,
              ("trace_stock", "rs_local_kernel"): TRACE_STEPS}
     return calls.get((run, kernel))
 
