@@ -117,3 +117,29 @@ def test_noalloc_runs_under_graph_capture():
         torch.cuda.synchronize()
         for r in range(W):
             gpu_util.assert_same_f32(got[r].cpu().numpy(), ref[r].cpu().numpy(), f"replay {replay} rank {r}")
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("name", ["llama3.1-70b-layer", "qwen3-30b-a3b-moe-layer"])
+def test_noalloc_full_size_layers(name):
+    """Full-size layers: the Llama-3.1-70B layer (13 launches per call) and the
+    Qwen3 MoE layer (3,144 segments: about 289 KB of tables, written by 73 put
+    launches) give the allocating entry point's shards, bit for bit."""
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import synth
+    from param_collectives_amd import tide
+
+    w = synth.workload(name)
+    plan = tide.Plan(w.world, w.shapes)
+    grads = synth.grads_device(w, "cuda")
+    ptrs = [grads[u][p].data_ptr() for u in range(w.world) for p in range(w.nparams)]
+    ref = [torch.empty(plan.shard_elems, dtype=torch.float32, device="cuda") for _ in range(w.world)]
+    got = [torch.full((plan.shard_elems,), float("nan"), device="cuda") for _ in range(w.world)]
+    plan.reduce_scatter_local_raw(ptrs, [o.data_ptr() for o in ref], 1.0, 0, 0)
+    assert _call_noalloc(tide, plan, ptrs, [o.data_ptr() for o in got]) == 0, tide.lib.tide_last_error()
+    torch.cuda.synchronize()
+    for r in range(w.world):
+        assert torch.equal(got[r].view(torch.int32), ref[r].view(torch.int32)), f"{name} rank {r}"
