@@ -121,7 +121,10 @@ typedef enum {
  *               operation with more chunks than waves * wave_chunks is run as
  *               several launches of about equal length, back to back on the
  *               stream (waves of one long launch drift apart and spread their
- *               memory traffic).
+ *               memory traffic).  In a reduce-scatter, a rank's shard of
+ *               at least one round that would start mid-round opens a launch
+ *               of its own once the previous group holds wave_chunks/2
+ *               rounds (tide_plan_launches lists the result).
  *               At most 2^30 (one launch for any plan); default 64.
  */
 typedef struct {

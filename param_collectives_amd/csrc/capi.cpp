@@ -24,6 +24,7 @@
 #include <mutex>
 #include <string>
 #include <unordered_set>
+#include <utility>
 #include <vector>
 
 #include "tide_internal.h"
@@ -277,12 +278,23 @@ tide_status bind_device(tide_plan* p) {
 // the launches get equal numbers of whole rounds (a short last launch would be
 // all ramp-up and tail, a partial round leaves waves idle).
 struct Launches {
-  int64_t grid;        // workgroups of a full launch
-  int64_t per_launch;  // chunks of every launch but the last (which may have fewer)
-  int64_t nchunks;     // of the whole operation
+  int64_t grid;                                     // workgroups of a full launch
+  std::vector<std::pair<int64_t, int64_t>> ranges;  // [first, end) chunks of each launch
+  int64_t nchunks;                                  // of the whole operation
 };
 
-Launches split_launches(const OpState& s, const tide_options& eff) {
+// A reduce-scatter's chunks are first cut into groups, each split that way
+// on its own: a group ends where the next rank's shard (a destination stream
+// of at least one round) begins off the phase of the group's rounds (more
+// than waves/64 chunks from a round boundary), once the group holds at least
+// wave_chunks/2 rounds.  That rank's first chunk then opens a launch, and its
+// rounds line up with the start of its shard as rank 0's do.  (Measured on
+// MI355X, same-box A/B in the timed step: the reduce-scatter of the Qwen3 MoE
+// layer, whose ranks own 292 mod 1024 chunks each, +0.75%; of the Wan2.2
+// block, 915 mod 1024, +0.9%.  The Llama layers' ranks own 2 mod 1024 chunks
+// and are not cut.  The same cut at a copy-out's parameters moved the Wan2.2
+// copy-out by -0.7 to +0.4%, so the copies keep one group.)
+Launches split_launches(const OpState& s, const tide_options& eff, bool by_destination) {
   Launches L;
   L.nchunks = s.chunk_begin.back();
   int64_t grid = int64_t(eff.cu_budget) * eff.wg_per_cu;
@@ -292,16 +304,37 @@ Launches split_launches(const OpState& s, const tide_options& eff) {
   if (grid < 1) grid = 1;
   L.grid = grid;
   const int64_t waves = grid * tide::kWavesPerGroup;
-  const int64_t rounds = (L.nchunks + waves - 1) / waves;
-  const int64_t launches = std::max<int64_t>(1, (rounds + eff.wave_chunks - 1) / eff.wave_chunks);
-  L.per_launch = std::max<int64_t>(1, (rounds + launches - 1) / launches * waves);
+  // group boundaries (first chunks), then each group's launches
+  std::vector<int64_t> cuts{0};
+  const int64_t tol = std::max<int64_t>(1, waves / 64);
+  const int64_t min_group = waves * std::max<int64_t>(1, eff.wave_chunks / 2);
+  size_t i = by_destination ? 1 : s.segs.size();
+  while (i < s.segs.size()) {
+    if (s.segs[i].dst_idx == s.segs[i - 1].dst_idx) {
+      ++i;
+      continue;
+    }
+    size_t j = i + 1;  // [i, j): the run of segments with this destination
+    while (j < s.segs.size() && s.segs[j].dst_idx == s.segs[i].dst_idx) ++j;
+    const int64_t c = s.chunk_begin[i], run = s.chunk_begin[j] - c;
+    const int64_t phase = (c - cuts.back()) % waves;
+    if (phase > tol && phase < waves - tol && run >= waves && c - cuts.back() >= min_group) cuts.push_back(c);
+    i = j;
+  }
+  cuts.push_back(L.nchunks);
+  for (size_t k = 0; k + 1 < cuts.size(); ++k) {
+    const int64_t g0 = cuts[k], n = cuts[k + 1] - g0;
+    const int64_t rounds = (n + waves - 1) / waves;
+    const int64_t launches = std::max<int64_t>(1, (rounds + eff.wave_chunks - 1) / eff.wave_chunks);
+    const int64_t per = std::max<int64_t>(1, (rounds + launches - 1) / launches * waves);
+    for (int64_t c0 = g0; c0 < g0 + n; c0 += per) L.ranges.emplace_back(c0, std::min(g0 + n, c0 + per));
+  }
   return L;
 }
 
-// The launch that starts at chunk c0: its span (chunks, and the segments they
+// The launch of chunks [c0, c1): its span (chunks, and the segments they
 // fall in) and its workgroup count.
-void launch_at(const OpState& s, const Launches& L, int64_t c0, tide::ChunkSpan* span, int64_t* grid) {
-  const int64_t c1 = std::min<int64_t>(L.nchunks, c0 + L.per_launch);
+void launch_at(const OpState& s, const Launches& L, int64_t c0, int64_t c1, tide::ChunkSpan* span, int64_t* grid) {
   // the segment of chunk c0, and one past the segment of chunk c1 - 1
   const auto it = std::upper_bound(s.chunk_begin.begin(), s.chunk_begin.end(), int32_t(c0));
   const auto it_end = std::upper_bound(it, s.chunk_begin.end(), int32_t(c1 - 1));
@@ -392,13 +425,13 @@ tide_status run_op(tide_plan* p, tide::Op op, const std::vector<const void*>& ke
 tide_status launch_op(const OpState& s, tide::Op op, const tide_options& eff, tide::KernelArgs a, hipStream_t stream,
                       bool f32) {
   const int32_t nchunks = s.chunk_begin.back();
-  const Launches L = split_launches(s, eff);
+  const Launches L = split_launches(s, eff, op == tide::kOpRs || op == tide::kOpRsF32);
   a.nchunks = nchunks;
   a.chunk = int32_t(eff.chunk_elems);
   a.flags = eff.flags;
-  for (int64_t c0 = 0; c0 < nchunks; c0 += L.per_launch) {
+  for (const auto& rg : L.ranges) {
     int64_t g = 0;
-    launch_at(s, L, c0, &a.span, &g);
+    launch_at(s, L, rg.first, rg.second, &a.span, &g);
     int rc = 0;
     const char* what = "";
     switch (op) {
@@ -645,14 +678,14 @@ tide_status tide_plan_launches(const tide_plan* plan, int32_t op, int32_t cu_cou
     const OpState& s = op_state(plan, tide::Op(op));
     *count = 0;
     if (s.chunk_begin.back() == 0) return TIDE_OK;
-    const Launches L = split_launches(s, eff);
+    const Launches L = split_launches(s, eff, op == tide::kOpRs || op == tide::kOpRsF32);
     int64_t n = 0;
-    for (int64_t c0 = 0; c0 < L.nchunks; c0 += L.per_launch, ++n) {
-      if (n >= capacity) continue;
+    for (const auto& rg : L.ranges) {
+      if (n++ >= capacity) continue;
       tide::ChunkSpan sp;
       int64_t g = 0;
-      launch_at(s, L, c0, &sp, &g);
-      int64_t* row = table + 5 * n;
+      launch_at(s, L, rg.first, rg.second, &sp, &g);
+      int64_t* row = table + 5 * (n - 1);
       row[0] = sp.first;
       row[1] = sp.end;
       row[2] = sp.seg;

@@ -383,45 +383,90 @@ def test_options_round_trip_and_validation(tide):
         assert _status(e) == -1
 
 
+def _launch_groups(op, segs, cb, waves, wave_chunks):
+    """First chunks of the launch groups, re-derived from the segment table:
+    in a reduce-scatter (ops 0 and 4), a run of segments with one destination
+    rank (column 2) of at least one round opens a group when it starts more
+    than waves/64 chunks off the current group's round boundaries and that
+    group holds wave_chunks/2 rounds; other operations are one group."""
+    if op not in (0, 4):
+        return [0]
+    tol = max(1, waves // 64)
+    min_group = waves * max(1, wave_chunks // 2)
+    cuts = [0]
+    i = 1
+    while i < len(segs):
+        if segs[i, 2] == segs[i - 1, 2]:
+            i += 1
+            continue
+        j = i + 1
+        while j < len(segs) and segs[j, 2] == segs[i, 2]:
+            j += 1
+        c, run = int(cb[i]), int(cb[j] - cb[i])
+        phase = (c - cuts[-1]) % waves
+        if tol < phase < waves - tol and run >= waves and c - cuts[-1] >= min_group:
+            cuts.append(c)
+        i = j
+    return cuts
+
+
 def _check_launches(plan, op, L, waves, wave_chunks):
     """The launch table of one operation against its definition: consecutive
-    chunk ranges covering every chunk, equal whole rounds per launch but the
-    last, at most wave_chunks rounds each, and the segment range of each
-    launch found from the chunk table of the plan's segments."""
+    chunk ranges covering every chunk; within each launch group, equal whole
+    rounds per launch but the group's last, at most wave_chunks rounds each;
+    and the segment range of each launch found from the chunk table of the
+    plan's segments.  Returns the group starts."""
     segs = plan.segments(op)
     chunk = plan.options(op)["chunk_elems"]
     cb = np.concatenate([[0], np.cumsum(-(-segs[:, 5] // chunk))])
     nchunks = int(cb[-1])
     assert L[0, 0] == 0 and L[-1, 1] == nchunks
     assert np.array_equal(L[1:, 0], L[:-1, 1])
-    lens = L[:, 1] - L[:, 0]
-    assert np.all(lens[:-1] == lens[0]) and lens[-1] <= lens[0] and lens[-1] > 0
-    assert lens[0] % waves == 0 or len(L) == 1
-    assert np.all(lens <= wave_chunks * waves)
-    rounds = -(-nchunks // waves)
-    assert len(L) == -(-rounds // wave_chunks)
+    cuts = _launch_groups(op, segs, cb, waves, wave_chunks)
+    assert set(cuts) <= set(L[:, 0].tolist())
+    bounds = cuts + [nchunks]
+    for g0, g1 in zip(bounds[:-1], bounds[1:]):
+        G = L[(L[:, 0] >= g0) & (L[:, 0] < g1)]
+        assert G[0, 0] == g0 and G[-1, 1] == g1
+        lens = G[:, 1] - G[:, 0]
+        assert np.all(lens[:-1] == lens[0]) and 0 < lens[-1] <= lens[0]
+        assert lens[0] % waves == 0 or len(G) == 1
+        assert np.all(lens <= wave_chunks * waves)
+        rounds = -(-(g1 - g0) // waves)
+        assert len(G) == -(-rounds // wave_chunks)
     for first, end, seg, seg_end, g in L:
         assert cb[seg] <= first < cb[seg + 1]
         assert cb[seg_end - 1] <= end - 1 < cb[seg_end]
         assert g == min(waves // 4, -(-(end - first) // 4))
+    return cuts
 
 
 def test_launch_split(tide):
     w = synth.workload("llama3.1-8b-layer")
     plan = tide.Plan(w.world, w.shapes)
     L = plan.launches(0, cu_count=256)
-    _check_launches(plan, 0, L, 1024, 64)
+    # every rank owns 2 mod 1024 chunks: one group
+    assert _check_launches(plan, 0, L, 1024, 64) == [0]
     # 213,008 chunks are 209 rounds of 1024 waves: four launches of 53 rounds, the last shorter
     assert len(L) == 4
     assert list(L[:, 1] - L[:, 0]) == [53 * 1024] * 3 + [213008 - 3 * 53 * 1024]
     for op in range(5):
         _check_launches(plan, op, plan.launches(op, cu_count=256), 1024, 64)
-    # the Qwen3 layer's launches each touch a few hundred of its segments
+    # the Qwen3 layer's ranks own 76,068 chunks (292 mod 1024): every rank's
+    # shard opens a group, split into launches of 38 and 36 rounds; each
+    # launch touches a few hundred of its segments
     q = synth.workload("qwen3-30b-a3b-moe-layer")
     qplan = tide.Plan(q.world, q.shapes)
     QL = qplan.launches(0, cu_count=256)
-    _check_launches(qplan, 0, QL, 1024, 64)
+    assert _check_launches(qplan, 0, QL, 1024, 64) == [r * 76068 for r in range(8)]
+    assert len(QL) == 16 and list(QL[:2, 1] - QL[:2, 0]) == [38 * 1024, 76068 - 38 * 1024]
     assert np.all(QL[:, 3] - QL[:, 2] < 400)
+    # the Wan2.2 block: one group per rank shard for the reduce-scatter, one
+    # group for the copy-out
+    v = synth.workload("wan2.2-dit-block")
+    vplan = tide.Plan(v.world, v.shapes)
+    assert len(_check_launches(vplan, 0, vplan.launches(0, cu_count=256), 1024, 64)) == 8
+    assert len(_check_launches(vplan, 1, vplan.launches(1, cu_count=256), 1024, 64)) == 1
     # a small grid, three rounds per launch, a short last launch
     rng = np.random.default_rng(5)
     shapes = [(int(rng.integers(1, 40)), int(rng.integers(1, 70))) for _ in range(30)]
@@ -429,6 +474,10 @@ def test_launch_split(tide):
     for op in range(5):
         _check_launches(small, op, small.launches(op), 8, 3)
     assert len(small.launches(0)) > 3
+    # ranks of a few rounds each at an odd phase are grouped, not cut one by one
+    many = tide.Plan(64, w.shapes)
+    cuts = _check_launches(many, 0, many.launches(0, cu_count=256), 1024, 64)
+    assert len(cuts) < 8
 
 
 def test_launches_need_a_cu_count_until_bound(tide):
