@@ -373,6 +373,10 @@ def test_many_launches_per_call(tide, oracle_mod, world, wave_chunks):
     want = oracle_mod.rs_local_ex(world, shapes, grads, 0.5, True, init)
     for r in range(world):
         gpu_util.assert_same_f32(got[r], want[r], f"bf16 rank {r}")
+    # rank shards that start off the 12-wave round grid open launch groups of
+    # their own, so some launches start off that grid
+    for op in (0, 4):
+        assert np.any(plan.launches(op)[:, 0] % 12 != 0)
     g32 = [[oracle_pins.rand_f32(rng, s) for s in shapes] for _ in range(world)]
     got = run_rs(tide, plan, g32)
     want = oracle_mod.rs_local_ex(world, shapes, g32)
