@@ -25,7 +25,7 @@ Device (torch on the GPU; full-size workloads):
 Both recipes give N(0, sigma^2) bf16 values; the GPU path and the oracle
 always receive the same bytes, whichever recipe made them.
 """
-from .workloads import WORKLOADS, Workload, workload  # noqa: F401
+from .workloads import CONTEXT_WORKLOADS, WORKLOADS, Workload, workload  # noqa: F401
 from .gen import (  # noqa: F401
     BASE_SEED,
     bf16_bits_from_f32,

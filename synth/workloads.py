@@ -104,11 +104,27 @@ def _wan22_block():
     return Workload(4, "wan2.2-dit-block", 8, [s for _, s in named], [n for n, _ in named], sigma=1e-3)
 
 
+def _equal16(index, name, side):
+    """The shape class of the reduce-scatter latency table of "The Endgame of
+    FSDP Communication" (Table 8): 16 bf16 gradients and 32 or 128 MiB of
+    fp32 output per rank at W = 8.  The pages give no tensor shapes; these are
+    16 equal square tensors of that total: side 2048 gives 16 x 256 rows x
+    2048 = 8 Mi fp32 elements (32 MiB) per rank, side 4096 gives 128 MiB."""
+    shapes = [(side, side)] * 16
+    return Workload(index, name, 8, shapes, [f"grad{i}" for i in range(16)], sigma=1e-3)
+
+
 WORKLOADS = {w.name: w for w in (_tiny(), _llama8b(), _llama70b(), _qwen3_moe(), _wan22_block())}
 WORKLOAD_ORDER = ["tiny", "llama3.1-8b-layer", "llama3.1-70b-layer", "qwen3-30b-a3b-moe-layer", "wan2.2-dit-block"]
 
+# Context shapes: not among the graded workloads above, for comparisons with
+# the pages' own latency tables.
+CONTEXT_WORKLOADS = {w.name: w for w in (_equal16(5, "equal16-32mib", 2048), _equal16(6, "equal16-128mib", 4096))}
+
 
 def workload(name: str) -> Workload:
-    if name not in WORKLOADS:
-        raise KeyError(f"unknown workload {name!r}; known: {', '.join(WORKLOAD_ORDER)}")
-    return WORKLOADS[name]
+    if name in WORKLOADS:
+        return WORKLOADS[name]
+    if name in CONTEXT_WORKLOADS:
+        return CONTEXT_WORKLOADS[name]
+    raise KeyError(f"unknown workload {name!r}; known: {', '.join(WORKLOAD_ORDER + list(CONTEXT_WORKLOADS))}")
