@@ -342,7 +342,8 @@ def test_streams_are_honoured(tide, oracle_mod):
 
 # ------------------------------------------------------------ full size
 
-FULL = ["llama3.1-8b-layer", "llama3.1-70b-layer", "qwen3-30b-a3b-moe-layer", "wan2.2-dit-block"]
+# the four layers, and the smaller context shape class (16 equal tensors, 32 MiB of fp32 shard per rank)
+FULL = ["llama3.1-8b-layer", "llama3.1-70b-layer", "qwen3-30b-a3b-moe-layer", "wan2.2-dit-block", "equal16-32mib"]
 
 
 @pytest.mark.timeout(600)
