@@ -190,6 +190,71 @@ def _kernel_stats(out, run="trace"):
     return rows
 
 
+def _kernel_trace_rows(out, run="trace"):
+    """(kernel short name, duration in ns) of every dispatch of a trace run,
+    in dispatch order."""
+    rows = []
+    for fn in glob.glob(os.path.join(out, run, "**", "*kernel_trace.csv"), recursive=True):
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                rows.append((int(r.get("Dispatch_Id", 0) or 0), _short(r.get("Kernel_Name", "")),
+                             int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    rows.sort()
+    return [(name, ns) for _, name, ns in rows]
+
+
+def _launch_bytes(plan, op, W):
+    """Algorithmic bytes of each launch of one call of `op` (0 reduce-scatter,
+    1 copy-out, 2 copy-in), from the segment table and the launch table:
+    a summed element moves 2W bytes in and 4 out, a padding element of a shard
+    4 out; a copied element 2 + 2 (copy-out) or 4 + 2 (copy-in from fp32), a
+    padding slot of the rank-major buffer 2 out."""
+    import numpy as np
+
+    segs = plan.segments(op)
+    chunk = plan.options(op)["chunk_elems"]
+    nch = -(-segs[:, 5] // chunk)
+    first = np.concatenate([[0], np.cumsum(nch)])
+    per_kind = {0: {0: 2 * W + 4, 1: 4}, 1: {2: 4}, 2: {2: 6, 1: 2}}[op]
+    out = []
+    for c0, c1, s0, s1, _ in plan.launches(op, cu_count=256):
+        b = 0
+        for i in range(s0, s1):
+            lo, hi = max(c0, first[i]), min(c1, first[i + 1])
+            if hi > lo:
+                e = min((hi - first[i]) * chunk, segs[i, 5]) - (lo - first[i]) * chunk
+                b += int(e) * per_kind[int(segs[i, 0])]
+        out.append(b)
+    return out
+
+
+def _per_launch_lines(out, workload):
+    """Per launch position within a call of the timed step's kernels: the
+    median duration over the run's calls (the first left out) and the rate."""
+    import numpy as np
+
+    import synth
+    from param_collectives_amd import tide
+
+    w = synth.workload(workload)
+    plan = tide.Plan(w.world, w.shapes)
+    rows = _kernel_trace_rows(out)
+    lines = []
+    for op, kernel in ((0, "rs_local_kernel"), (1, "ag_copyout_kernel"), (2, "ag_copyin_kernel")):
+        ns = [d for name, d in rows if name == kernel]
+        nbytes = _launch_bytes(plan, op, w.world)
+        n = len(nbytes)
+        if not ns or len(ns) % n:
+            continue
+        calls = np.array(ns, dtype=np.float64).reshape(-1, n)[1:]
+        med = np.median(calls, axis=0) / 1e3
+        lines.append(f"{kernel}: {n} launches per call (chunks of each launch: tide_plan_launches), "
+                     f"median of {len(calls)} calls")
+        lines.append("  " + " ".join(f"{i}:{m:.1f}us/{b / m / 1e6:.2f}TB/s" for i, (m, b) in
+                                     enumerate(zip(med, nbytes))))
+    return lines
+
+
 def summarize(workload, out, profiles):
     os.makedirs(profiles, exist_ok=True)
     digest = source_digest()
@@ -228,6 +293,10 @@ def summarize(workload, out, profiles):
             lines.append(f"{name:<22} {r.get('Calls', ''):>10} {avg:>10.2f} {mn:>10.2f} {mx:>10.2f} "
                          f"{float(r.get('Percentage', 0)):>6.1f} {calls!s:>8} {per_call:>12.2f}")
     if any_stats:
+        per_launch = _per_launch_lines(out, workload)
+        if per_launch:
+            lines += ["", "## timed step, per launch within a call (launch index: median duration / rate)"]
+            lines += per_launch
         with open(os.path.join(profiles, f"kernel_trace_{workload}.txt"), "w") as f:
             f.write("\n".join(lines) + "\n")
     # counters
