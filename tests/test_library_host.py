@@ -493,6 +493,22 @@ def test_launches_need_a_cu_count_until_bound(tide):
     assert empty.launches(0, cu_count=4).shape == (0, 5)
 
 
+def test_launch_table_capacity(tide):
+    """A table shorter than the launch count gets the first launches and the
+    full count."""
+    import ctypes
+
+    q = synth.workload("qwen3-30b-a3b-moe-layer")
+    plan = tide.Plan(q.world, q.shapes)
+    full = plan.launches(0, cu_count=256)
+    table = np.full((3, 5), -7, dtype=np.int64)
+    count = ctypes.c_int64(-1)
+    st = tide.lib.tide_plan_launches(plan.handle, 0, 256, table.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), 2,
+                                     ctypes.byref(count))
+    assert st == 0 and count.value == len(full) == 16
+    assert np.array_equal(table[:2], full[:2]) and np.all(table[2] == -7)
+
+
 def test_too_many_chunks_is_a_range_error(tide):
     with pytest.raises(tide.TideError) as e:
         tide.Plan(1, [(2**34,)], chunk_elems=8)
