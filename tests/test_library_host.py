@@ -620,3 +620,16 @@ def test_paths_need_a_call_first(tide):
     assert tide.lib.tide_plan_paths(plan.handle, 5, out) == -1
     assert tide.lib.tide_plan_paths(plan.handle, 0, None) == -1
     assert tide.lib.tide_plan_paths(None, 0, out) == -1
+
+
+def test_readme_example_uses_the_binding_as_it_is(tide):
+    """The README's Python example compiles, and every binding name it calls
+    exists with the keyword arguments it passes."""
+    import inspect
+
+    src = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "README.md")).read()
+    code = re.search(r"```python\n(.*?)```", src, re.S).group(1)
+    compile(code, "README.md", "exec")
+    for name in re.findall(r"tide\.(\w+)\(", code):
+        assert hasattr(tide, name), name
+    assert "alpha" in inspect.signature(tide.reduce_scatter_call).parameters
